@@ -1,0 +1,361 @@
+"""Pins of the oracle's four stages against what the pages and mathematics fix."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import stats
+
+import synth
+from oracle import philox, stages, variates
+
+
+def _chi2_ok(counts, probs, alpha=1e-4):
+    counts = np.asarray(counts, dtype=np.float64)
+    p = np.asarray(probs, dtype=np.float64)
+    p = p / p.sum()
+    n = counts.sum()
+    keep = p * n >= 5
+    obs = np.append(counts[keep], counts[~keep].sum())
+    exp = np.append(p[keep] * n, p[~keep].sum() * n)
+    if exp[-1] == 0:
+        assert obs[-1] == 0
+        obs, exp = obs[:-1], exp[:-1]
+    return stats.chisquare(obs, exp).pvalue > alpha
+
+
+def _small(V=8, Vd=None, r=4, N=3, B=1, std=0.6, seed=0):
+    g = np.random.default_rng(seed)
+    Vd = V if Vd is None else Vd
+    return {
+        "base": g.normal(0, 1.0, size=(B, N, Vd)).astype(np.float32),
+        "w1": synth.bf16_bits(g.normal(0, std, size=(V, r)).astype(np.float32)),
+        "w2": synth.bf16_bits(g.normal(0, std, size=(Vd, r)).astype(np.float32)),
+        "anchor": g.integers(0, V, size=B).astype(np.int32),
+    }
+
+
+# ---------------------------------------------------------------- stage 1
+
+def test_bf16_decode_known_patterns():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x7F7F, 0x3E80, 0x0001], dtype=np.uint16)
+    want = [1.0, -1.0, 3.140625, 0.0, 3.3895313892515355e38, 0.25, 2.0 ** -133]
+    assert list(stages.bf16_decode(bits)) == want
+
+
+def test_draft_logits_one_hot_selects_lm_head_entries():
+    g = np.random.default_rng(1)
+    H, Vd, M = 64, 40, 6
+    W = synth.bf16_bits(g.normal(0, 0.5, size=(Vd, H)).astype(np.float32))
+    pos = g.integers(0, H, size=M)
+    hid = np.zeros((M, H), dtype=np.float32)
+    hid[np.arange(M), pos] = 2.0
+    out = stages.draft_logits(synth.bf16_bits(hid), W, chunk=7)
+    Wf = synth.bf16_to_f32(W)
+    for m in range(M):
+        assert np.array_equal(out[m], (2.0 * Wf[:, pos[m]]).astype(np.float32))
+
+
+def test_draft_logits_linear_in_hidden():
+    g = np.random.default_rng(2)
+    H, Vd = 32, 24
+    W = synth.bf16_bits(g.normal(0, 0.5, size=(Vd, H)).astype(np.float32))
+    a = g.integers(-4, 5, size=(1, H)).astype(np.float32)   # small integers: exact in bf16
+    b = g.integers(-4, 5, size=(1, H)).astype(np.float32)
+    oa = stages.draft_logits(synth.bf16_bits(a), W).astype(np.float64)
+    ob = stages.draft_logits(synth.bf16_bits(b), W).astype(np.float64)
+    oab = stages.draft_logits(synth.bf16_bits(a + b), W).astype(np.float64)
+    assert np.allclose(oab, oa + ob, rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------- stage 2
+
+def test_markov_bias_equals_explicit_bigram_table():
+    # the head is a low-rank factorisation of a V x Vd correction table
+    V, r, N = 16, 4, 5
+    d = _small(V=V, r=r, N=N, std=1.0, seed=3)
+    T = np.float32([0.8])
+    res = stages.markov_sample(d["base"], d["w1"], d["w2"], None, d["anchor"], T,
+                               np.zeros(1, np.uint32), seed=4)
+    table = synth.bf16_to_f32(d["w1"]).astype(np.float64) @ synth.bf16_to_f32(d["w2"]).astype(np.float64).T
+    prev = int(d["anchor"][0])
+    for i in range(N):
+        want = (d["base"][0, i].astype(np.float64) + table[prev]).astype(np.float32)
+        assert np.allclose(res["processed"][0, i], want, rtol=0, atol=2e-7)
+        prev = int(res["tokens"][0, i])
+
+
+def test_markov_zero_w1_is_independent_per_position_sampling():
+    V, N = 12, 4
+    d = _small(V=V, N=N, seed=5)
+    w1 = np.zeros_like(d["w1"])
+    res = stages.markov_sample(d["base"], w1, d["w2"], None, d["anchor"], np.float32([1.0]),
+                               np.array([7], np.uint32), seed=9)
+    for i in range(N):
+        u = philox.uniforms(9, np.arange(V), i, 7, philox.TAG_DRAFT)
+        key = d["base"][0, i].astype(np.float64) - np.log(-np.log(u.astype(np.float64)))
+        assert res["tokens"][0, i] == int(np.argmax(key))
+        assert np.array_equal(res["processed"][0, i], d["base"][0, i])
+
+
+def test_anchor_only_changes_step0_bias():
+    V, N = 10, 4
+    d = _small(V=V, N=N, seed=6)
+    T = np.float32([0.0])          # greedy: step-0 token may or may not move
+    a1 = np.array([1], np.int32)
+    a2 = np.array([2], np.int32)
+    r1 = stages.markov_sample(d["base"], d["w1"], d["w2"], None, a1, T, np.zeros(1, np.uint32), 0)
+    r2 = stages.markov_sample(d["base"], d["w1"], d["w2"], None, a2, T, np.zeros(1, np.uint32), 0)
+    assert not np.array_equal(r1["processed"][0, 0], r2["processed"][0, 0])
+    for i in range(1, N):
+        if r1["tokens"][0, i - 1] == r2["tokens"][0, i - 1]:
+            assert np.array_equal(r1["processed"][0, i], r2["processed"][0, i])
+
+
+def test_markov_greedy_is_argmax():
+    d = _small(V=20, N=3, seed=7)
+    res = stages.markov_sample(d["base"], d["w1"], d["w2"], None, d["anchor"], np.float32([0.0]),
+                               np.zeros(1, np.uint32), 0)
+    for i in range(3):
+        assert res["tokens"][0, i] == int(np.argmax(res["processed"][0, i]))
+        assert res["logZ"][0, i] == res["processed"][0, i].max()
+
+
+def test_markov_chain_distribution_chi_square():
+    # joint law of (x0, x1): softmax((base0 + bias(anchor))/T) * softmax((base1 + bias(x0))/T)
+    V, r, N, B = 5, 3, 2, 30_000
+    g = np.random.default_rng(8)
+    base1 = g.normal(0, 1.0, size=(1, N, V)).astype(np.float32)
+    base = np.repeat(base1, B, axis=0)
+    w1 = synth.bf16_bits(g.normal(0, 1.0, size=(V, r)).astype(np.float32))
+    w2 = synth.bf16_bits(g.normal(0, 1.0, size=(V, r)).astype(np.float32))
+    anchor = np.full(B, 2, np.int32)
+    Tval = 0.7
+    temp = np.full(B, Tval, np.float32)
+    res = stages.markov_sample(base, w1, w2, None, anchor, temp, np.arange(B, dtype=np.uint32), seed=11)
+    table = synth.bf16_to_f32(w1).astype(np.float64) @ synth.bf16_to_f32(w2).astype(np.float64).T
+
+    def sm(x):
+        z = np.exp(x - x.max())
+        return z / z.sum()
+    p0 = sm((base1[0, 0] + table[2]) / np.float32(Tval))
+    joint = np.array([[p0[a] * sm((base1[0, 1] + table[a]) / np.float32(Tval))[b] for b in range(V)]
+                      for a in range(V)])
+    counts = np.zeros((V, V))
+    np.add.at(counts, (res["tokens"][:, 0], res["tokens"][:, 1]), 1)
+    assert _chi2_ok(counts.ravel(), joint.ravel())
+    # logZ is the log-normaliser of the tempered processed row
+    row = res["processed"][0, 0].astype(np.float64) / np.float32(Tval)
+    assert math.isclose(res["logZ"][0, 0], math.log(np.exp(row).sum()), rel_tol=1e-6)
+
+
+def test_markov_reduced_vocab_maps_tokens_through_d2t():
+    V, Vd, N = 30, 8, 3
+    d = _small(V=V, Vd=Vd, N=N, seed=12)
+    g = np.random.default_rng(13)
+    image = g.permutation(V)[:Vd]
+    d2t = image - np.arange(Vd)
+    res = stages.markov_sample(d["base"], d["w1"], d["w2"], d2t, d["anchor"], np.float32([0.0]),
+                               np.zeros(1, np.uint32), 0)
+    for i in range(N):
+        j = int(np.argmax(res["processed"][0, i]))
+        assert res["tokens"][0, i] == j + d2t[j]
+    inv = stages.build_inverse_map(d2t, Vd, V)
+    assert (inv >= 0).sum() == Vd and all(inv[j + d2t[j]] == j for j in range(Vd))
+
+
+def test_markov_head_parameter_count(golden_dir):
+    fig = json.load(open(os.path.join(golden_dir, "pages_figures.json")))["markov_head_params"]
+    w = synth.get("qwen3_8b_single")
+    assert (w.V, w.r) == (fig["V"], fig["r"])
+    n_params = w.V * w.r + w.Vd * w.r          # W1 [V, r] + W2 [Vd, r]
+    assert n_params == 19_447_808
+    assert round(n_params / 1e6, 1) == fig["approx_millions"]
+    lm = json.load(open(os.path.join(golden_dir, "pages_figures.json")))["lm_head_params"]
+    assert round(lm["V"] * lm["H"] / 1e6) == lm["full_approx_millions"]
+    assert round(lm["Vd"] * lm["H"] / 1e6) == lm["reduced_approx_millions"]
+
+
+def test_query_layout_samples_every_position(golden_dir):
+    fig = json.load(open(os.path.join(golden_dir, "pages_figures.json")))["query_layout"]
+    N = fig["N"]
+    d = _small(V=16, N=N, seed=14)
+    res = stages.markov_sample(d["base"], d["w1"], d["w2"], None, d["anchor"], np.float32([1.0]),
+                               np.zeros(1, np.uint32), 0)
+    assert res["tokens"].shape == (1, len(fig["sampled_positions"]))
+
+
+# ---------------------------------------------------------------- stage 3
+
+def _onehot_logits(argmaxes, V, g):
+    rows = g.normal(0, 0.1, size=(len(argmaxes), V)).astype(np.float32)
+    for k, a in enumerate(argmaxes):
+        rows[k, a] = 5.0
+    return rows
+
+
+def test_verify_greedy_golden_cases(golden_dir):
+    cases = json.load(open(os.path.join(golden_dir, "greedy_verify_cases.json")))["cases"]
+    g = np.random.default_rng(15)
+    V = 10
+    for c in cases:
+        N = len(c["draft"])
+        tgt = _onehot_logits(c["target_argmax"], V, g)[None]
+        drf = g.normal(0, 1, size=(1, N, V)).astype(np.float32)
+        res = stages.verify("logits", tgt, drf, np.array([c["draft"]], np.int32), None,
+                            np.array([c["verify_len"]]), np.float32([0.0]), np.zeros(1, np.uint32), 3)
+        assert res["accepted"][0] == c["accepted"]
+        a = c["accepted"]
+        assert list(res["out_tokens"][0, :a + 1]) == c["out"]
+        assert (res["out_tokens"][0, a + 1:] == -1).all()
+
+
+def test_verify_greedy_random_matches_longest_prefix_rule():
+    g = np.random.default_rng(16)
+    V, N = 6, 5
+    for trial in range(200):
+        tgt = g.normal(0, 1, size=(1, N + 1, V)).astype(np.float32)
+        am = tgt[0].argmax(axis=1)
+        draft = np.where(g.random(N) < 0.7, am[:N], g.integers(0, V, N)).astype(np.int32)[None]
+        res = stages.verify("logits", tgt, g.normal(size=(1, N, V)).astype(np.float32), draft, None,
+                            None, np.float32([0.0]), np.zeros(1, np.uint32), trial)
+        acc = 0
+        while acc < N and draft[0, acc] == am[acc]:
+            acc += 1
+        assert res["accepted"][0] == acc
+        assert res["out_tokens"][0, acc] == am[acc]
+
+
+def test_verify_identical_distributions_accept_everything():
+    g = np.random.default_rng(17)
+    B, N, V = 50, 4, 9
+    p = g.dirichlet(np.ones(V), size=(B, N + 1)).astype(np.float32)
+    draft = np.array([[g.choice(V, p=p[b, k].astype(np.float64) / p[b, k].astype(np.float64).sum())
+                       for k in range(N)] for b in range(B)], dtype=np.int32)
+    res = stages.verify("probs", p, p[:, :N], draft, None, None, None,
+                        np.arange(B, dtype=np.uint32), 5)
+    assert (res["accepted"] == N).all()
+
+
+def _verify_stats(V=6, Vd=None, N=3, B=30_000, seed=0, sigma=1.0, T=1.0, d2t=None, L=None):
+    g = np.random.default_rng(seed)
+    Vd = V if Vd is None else Vd
+    base_d = g.normal(0, 1, size=(N, Vd))
+    tgt = g.normal(0, 1, size=(N + 1, V))
+    if d2t is not None:
+        tgt[:N, np.arange(Vd) + d2t] += base_d
+    else:
+        tgt[:N] += base_d
+    tgt = (tgt * sigma).astype(np.float32)
+    proc = base_d.astype(np.float32)
+    p_t = np.stack([stages.probs_from_logits(tgt[k], T) for k in range(N + 1)])
+    p_d = np.stack([stages.probs_from_logits(proc[k], T) for k in range(N)])
+    # drafts: x_k ~ p_d[k] (independent, since these draft rows do not depend on the prefix)
+    pd64 = p_d.astype(np.float64)
+    u = g.random(size=(B, N))
+    cdf = np.cumsum(pd64 / pd64.sum(axis=1, keepdims=True), axis=1)
+    jd = np.minimum((u[:, :, None] > cdf[None]).sum(axis=2), Vd - 1)
+    tgt_ids = jd + (0 if d2t is None else d2t[jd])
+    inv = None if d2t is None else stages.build_inverse_map(d2t, Vd, V)
+    P_t = np.broadcast_to(p_t, (B, N + 1, V))
+    P_d = np.broadcast_to(p_d, (B, N, Vd))
+    Lv = None if L is None else np.full(B, L)
+    res = stages.verify("probs", P_t, P_d, tgt_ids.astype(np.int32), inv, Lv, None,
+                        np.arange(B, dtype=np.uint32), seed + 100)
+    return res, p_t, p_d, inv, tgt_ids
+
+
+def test_verify_is_lossless_chi_square():
+    res, p_t, p_d, _, _ = _verify_stats(seed=21)
+    out, acc = res["out_tokens"], res["accepted"]
+    for k in range(3):
+        sel = acc >= k                     # position k is emitted iff positions < k accepted
+        counts = np.bincount(out[sel, k], minlength=p_t.shape[1])
+        assert _chi2_ok(counts, p_t[k])
+
+
+def test_verify_acceptance_rate_is_one_minus_tv():
+    res, p_t, p_d, _, _ = _verify_stats(seed=22, B=40_000)
+    alpha = stages.accept_prob(p_t[0], p_d[0])
+    tv = 0.5 * np.abs(p_t[0].astype(np.float64) - p_d[0].astype(np.float64)).sum()
+    assert math.isclose(alpha, 1 - tv, rel_tol=1e-6)
+    n = res["accepted"].size
+    rate = (res["accepted"] >= 1).mean()
+    assert abs(rate - alpha) < 4.5 * math.sqrt(alpha * (1 - alpha) / n)
+
+
+def test_verify_reduced_vocab_lossless():
+    g = np.random.default_rng(23)
+    V, Vd = 9, 5
+    d2t = g.permutation(V)[:Vd] - np.arange(Vd)
+    res, p_t, p_d, inv, _ = _verify_stats(V=V, Vd=Vd, seed=23, d2t=d2t)
+    out, acc = res["out_tokens"], res["accepted"]
+    for k in range(2):
+        sel = acc >= k
+        counts = np.bincount(out[sel, k], minlength=V)
+        assert _chi2_ok(counts, p_t[k])
+    off = inv < 0
+    assert out[:, 0][np.isin(out[:, 0], np.nonzero(off)[0])].size > 0   # off-image tokens do appear
+
+
+def test_verify_zero_length_samples_first_target_row():
+    res, p_t, _, _, _ = _verify_stats(seed=24, L=0, B=20_000)
+    assert (res["accepted"] == 0).all()
+    assert _chi2_ok(np.bincount(res["out_tokens"][:, 0], minlength=p_t.shape[1]), p_t[0])
+    assert (res["out_tokens"][:, 1:] == -1).all()
+
+
+def test_verify_all_zero_residual_falls_back_to_target():
+    # unnormalised input p_t = p_d / 2: every rejection has a zero residual
+    g = np.random.default_rng(25)
+    V, B = 5, 20_000
+    p_d = g.dirichlet(np.ones(V)).astype(np.float32)
+    p_t = (p_d * np.float32(0.5)).astype(np.float32)
+    x = g.choice(V, p=p_d.astype(np.float64) / p_d.astype(np.float64).sum(), size=B).astype(np.int32)
+    res = stages.verify("probs", np.broadcast_to(p_t, (B, 2, V)), np.broadcast_to(p_d, (B, 1, V)),
+                        x[:, None], None, None, None, np.arange(B, dtype=np.uint32), 8)
+    rej = res["accepted"] == 0
+    assert abs(rej.mean() - 0.5) < 0.02
+    assert _chi2_ok(np.bincount(res["out_tokens"][rej, 0], minlength=V), p_t)
+
+
+# ---------------------------------------------------------------- stage 4
+
+def test_admit_golden_cases(golden_dir):
+    cases = json.load(open(os.path.join(golden_dir, "admission_cases.json")))["cases"]
+    for c in cases:
+        res = stages.admit(np.array(c["c"], np.float32), c["K"])
+        assert res["survival"].tolist() == c["survival"]
+        assert res["admit_len"].tolist() == c["admit_len"]
+
+
+@pytest.mark.parametrize("K", [0, 1, 17, 100, 255, 256, 1000])
+def test_admit_properties(K):
+    w = synth.get("admission", B=16)
+    c = synth.confidence(w)
+    res = stages.admit(c, K)
+    adm = res["admitted"]
+    L = res["admit_len"]
+    assert L.sum() == min(K, c.size)
+    for b in range(c.shape[0]):
+        assert adm[b, :L[b]].all() and not adm[b, L[b]:].any()        # prefix closure
+    s = res["survival"]
+    assert np.all(np.diff(s.astype(np.float64), axis=1) <= 0)       # monotone along the block
+    if 0 < K < c.size:
+        assert s[adm].min() >= s[~adm].max()
+
+
+def test_admit_non_anticipation():
+    # whether (b, k) is admitted never depends on c[b, j] for j > k
+    g = np.random.default_rng(26)
+    w = synth.get("admission", B=12)
+    c = synth.confidence(w)
+    K = 40
+    base = stages.admit(c, K)["admitted"]
+    for trial in range(60):
+        b = int(g.integers(0, c.shape[0]))
+        k = int(g.integers(0, c.shape[1] - 1))
+        c2 = c.copy()
+        c2[b, k + 1:] = g.uniform(1e-3, 1.0, size=c.shape[1] - k - 1).astype(np.float32)
+        assert stages.admit(c2, K)["admitted"][b, k] == base[b, k]
