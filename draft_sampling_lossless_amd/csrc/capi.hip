@@ -1,0 +1,195 @@
+// C ABI of the DSpark hot path: argument validation on the host, then the
+// kernel launchers.  Nothing here allocates, frees or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "dspark.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+dspark_status fail(dspark_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dspark_status ok() {
+  g_err[0] = '\0';
+  return DSPARK_OK;
+}
+
+dspark_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSPARK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, st, ...)            \
+  do {                                    \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p, name)                                                          \
+  do {                                                                                \
+    if (!(p)) return fail(DSPARK_ERR_INVALID, "%s must not be NULL", name);          \
+  } while (0)
+
+#define REQUIRE_PTR16(p, name)                                                               \
+  do {                                                                                       \
+    if (!(p)) return fail(DSPARK_ERR_INVALID, "%s must not be NULL", name);                 \
+    if (!aligned16(p)) return fail(DSPARK_ERR_INVALID, "%s must be 16-byte aligned", name); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int dspark_abi_version(void) { return DSPARK_ABI_VERSION; }
+
+const char* dspark_last_error(void) { return g_err; }
+
+dspark_status dspark_philox_blocks(const uint32_t* counters, uint64_t seed, uint32_t* out, int64_t n,
+                                   void* stream) {
+  REQUIRE(n >= 0, DSPARK_ERR_INVALID, "n must be >= 0 (got %lld)", (long long)n);
+  if (n == 0) return ok();
+  REQUIRE(n <= ((int64_t)1 << 38), DSPARK_ERR_UNSUPPORTED, "n too large");
+  REQUIRE_PTR16(counters, "counters");
+  REQUIRE_PTR16(out, "out");
+  return hip_status(dspark::launch_philox_blocks(counters, seed, out, n, (hipStream_t)stream), "philox_blocks");
+}
+
+dspark_status dspark_race_exponentials(uint64_t seed, uint32_t position, uint32_t request_id, uint32_t tag,
+                                       float* out, int64_t n, void* stream) {
+  REQUIRE(n >= 0, DSPARK_ERR_INVALID, "n must be >= 0 (got %lld)", (long long)n);
+  if (n == 0) return ok();
+  REQUIRE(n <= ((int64_t)1 << 38), DSPARK_ERR_UNSUPPORTED, "n too large");
+  REQUIRE_PTR(out, "out");
+  return hip_status(dspark::launch_race_exponentials(seed, position, request_id, tag, out, n, (hipStream_t)stream),
+                    "race_exponentials");
+}
+
+dspark_status dspark_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, float* logits, int M, int H,
+                                  int Vd, void* stream) {
+  REQUIRE(M >= 0, DSPARK_ERR_INVALID, "M must be >= 0 (got %d)", M);
+  REQUIRE(H > 0 && H % 8 == 0, DSPARK_ERR_INVALID, "H must be a positive multiple of 8 (got %d)", H);
+  REQUIRE(Vd > 0, DSPARK_ERR_INVALID, "Vd must be > 0 (got %d)", Vd);
+  if (M == 0) return ok();
+  REQUIRE((int64_t)M * Vd < ((int64_t)1 << 40), DSPARK_ERR_UNSUPPORTED, "M * Vd too large");
+  REQUIRE_PTR16(hidden, "hidden");
+  REQUIRE_PTR16(lm_head, "lm_head");
+  REQUIRE_PTR(logits, "logits");
+  return hip_status(dspark::launch_draft_logits(hidden, lm_head, logits, M, H, Vd, (hipStream_t)stream),
+                    "draft_logits");
+}
+
+size_t dspark_markov_workspace_size(int B, int N, int Vd, int r) {
+  if (B <= 0 || N <= 0 || Vd <= 0 || r <= 0) return 0;
+  return dspark::plan_markov(B, N, Vd, r).partial_bytes;
+}
+
+dspark_status dspark_markov_sample(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
+                                   const int32_t* anchor, const float* temperature, const uint32_t* request_id,
+                                   uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,
+                                   int r, void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);
+  REQUIRE(B <= DSPARK_MAX_B, DSPARK_ERR_UNSUPPORTED, "B must be <= %d (got %d)", DSPARK_MAX_B, B);
+  REQUIRE(N >= 1, DSPARK_ERR_INVALID, "N must be >= 1 (got %d)", N);
+  REQUIRE(N <= DSPARK_MAX_N, DSPARK_ERR_UNSUPPORTED, "N must be <= %d (got %d)", DSPARK_MAX_N, N);
+  REQUIRE(V > 0 && V % 4 == 0, DSPARK_ERR_INVALID, "V must be a positive multiple of 4 (got %d)", V);
+  REQUIRE(Vd > 0 && Vd % 4 == 0, DSPARK_ERR_INVALID, "Vd must be a positive multiple of 4 (got %d)", Vd);
+  REQUIRE(Vd <= V, DSPARK_ERR_INVALID, "Vd (%d) must be <= V (%d)", Vd, V);
+  REQUIRE(r >= 8 && r % 8 == 0, DSPARK_ERR_INVALID, "r must be a positive multiple of 8 (got %d)", r);
+  REQUIRE(r <= DSPARK_MAX_RANK, DSPARK_ERR_UNSUPPORTED, "r must be <= %d (got %d)", DSPARK_MAX_RANK, r);
+  REQUIRE((int64_t)B * N * Vd < ((int64_t)1 << 40), DSPARK_ERR_UNSUPPORTED, "B * N * Vd too large");
+  REQUIRE_PTR16(logits, "logits");
+  REQUIRE_PTR16(w1, "w1");
+  REQUIRE_PTR16(w2, "w2");
+  if (Vd != V) REQUIRE_PTR16(d2t, "d2t (required when Vd != V)");
+  else if (d2t) REQUIRE(aligned16(d2t), DSPARK_ERR_INVALID, "d2t must be 16-byte aligned");
+  REQUIRE_PTR(anchor, "anchor");
+  REQUIRE_PTR(temperature, "temperature");
+  REQUIRE_PTR(request_id, "request_id");
+  REQUIRE_PTR(draft_tokens, "draft_tokens");
+  REQUIRE_PTR(log_z, "log_z");
+  const size_t need = dspark_markov_workspace_size(B, N, Vd, r);
+  REQUIRE(workspace != nullptr, DSPARK_ERR_WORKSPACE, "workspace must not be NULL (%zu bytes needed)", need);
+  REQUIRE(aligned16(workspace), DSPARK_ERR_INVALID, "workspace must be 16-byte aligned");
+  REQUIRE(workspace_bytes >= need, DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
+          need);
+  return hip_status(dspark::launch_markov_sample(logits, w1, w2, d2t, anchor, temperature, request_id, seed,
+                                                 draft_tokens, log_z, B, N, V, Vd, r, workspace, (hipStream_t)stream),
+                    "markov_sample");
+}
+
+dspark_status dspark_build_inverse_map(const int64_t* d2t, int Vd, int V, int32_t* inv_map, void* stream) {
+  REQUIRE(Vd > 0 && V > 0 && Vd <= V, DSPARK_ERR_INVALID, "need 0 < Vd <= V (got Vd=%d, V=%d)", Vd, V);
+  REQUIRE_PTR(d2t, "d2t");
+  REQUIRE_PTR(inv_map, "inv_map");
+  return hip_status(dspark::launch_build_inverse_map(d2t, Vd, V, inv_map, (hipStream_t)stream),
+                    "build_inverse_map");
+}
+
+size_t dspark_verify_workspace_size(int B, int N, int V) {
+  if (B <= 0 || N <= 0 || V <= 0) return 0;
+  return dspark::plan_verify(B, N, V).total_bytes;
+}
+
+dspark_status dspark_verify(int input_kind, const float* target, const float* draft, const float* draft_log_z,
+                            const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
+                            const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
+                            int32_t* out_tokens, int B, int N, int V, int Vd, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  REQUIRE(input_kind == DSPARK_INPUT_LOGITS || input_kind == DSPARK_INPUT_PROBS, DSPARK_ERR_INVALID,
+          "input_kind must be DSPARK_INPUT_LOGITS or DSPARK_INPUT_PROBS (got %d)", input_kind);
+  REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);
+  REQUIRE(B <= DSPARK_MAX_B, DSPARK_ERR_UNSUPPORTED, "B must be <= %d (got %d)", DSPARK_MAX_B, B);
+  REQUIRE(N >= 1, DSPARK_ERR_INVALID, "N must be >= 1 (got %d)", N);
+  REQUIRE(N <= DSPARK_MAX_N, DSPARK_ERR_UNSUPPORTED, "N must be <= %d (got %d)", DSPARK_MAX_N, N);
+  REQUIRE(V > 0 && V % 4 == 0, DSPARK_ERR_INVALID, "V must be a positive multiple of 4 (got %d)", V);
+  REQUIRE(Vd > 0 && Vd % 4 == 0, DSPARK_ERR_INVALID, "Vd must be a positive multiple of 4 (got %d)", Vd);
+  REQUIRE(Vd <= V, DSPARK_ERR_INVALID, "Vd (%d) must be <= V (%d)", Vd, V);
+  REQUIRE((int64_t)B * (N + 1) * V < ((int64_t)1 << 40), DSPARK_ERR_UNSUPPORTED, "B * (N+1) * V too large");
+  REQUIRE_PTR16(target, "target");
+  REQUIRE_PTR16(draft, "draft");
+  REQUIRE_PTR(draft_tokens, "draft_tokens");
+  if (Vd != V) REQUIRE_PTR(inv_map, "inv_map (required when Vd != V)");
+  REQUIRE_PTR(request_id, "request_id");
+  REQUIRE_PTR(accepted, "accepted");
+  REQUIRE_PTR(out_tokens, "out_tokens");
+  if (input_kind == DSPARK_INPUT_LOGITS) {
+    REQUIRE_PTR(temperature, "temperature (required for logits input)");
+    REQUIRE_PTR(draft_log_z, "draft_log_z (required for logits input)");
+  }
+  const size_t need = dspark_verify_workspace_size(B, N, V);
+  REQUIRE(workspace != nullptr, DSPARK_ERR_WORKSPACE, "workspace must not be NULL (%zu bytes needed)", need);
+  REQUIRE(aligned16(workspace), DSPARK_ERR_INVALID, "workspace must be 16-byte aligned");
+  REQUIRE(workspace_bytes >= need, DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
+          need);
+  return hip_status(dspark::launch_verify(input_kind, target, draft, draft_log_z, draft_tokens, inv_map, verify_len,
+                                          temperature, request_id, seed, accepted, out_tokens, B, N, V, Vd,
+                                          workspace, (hipStream_t)stream),
+                    "verify");
+}
+
+dspark_status dspark_admit(const float* cond_accept, int B, int N, int K, float* survival, int32_t* admit_len,
+                           void* stream) {
+  REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);
+  REQUIRE(N >= 1, DSPARK_ERR_INVALID, "N must be >= 1 (got %d)", N);
+  REQUIRE(N <= DSPARK_MAX_N, DSPARK_ERR_UNSUPPORTED, "N must be <= %d (got %d)", DSPARK_MAX_N, N);
+  REQUIRE(B <= DSPARK_MAX_B, DSPARK_ERR_UNSUPPORTED, "B must be <= %d (got %d)", DSPARK_MAX_B, B);
+  REQUIRE((int64_t)B * N <= DSPARK_MAX_ADMIT, DSPARK_ERR_UNSUPPORTED, "B * N must be <= %d (got %lld)",
+          DSPARK_MAX_ADMIT, (long long)B * N);
+  REQUIRE(K >= 0, DSPARK_ERR_INVALID, "K must be >= 0 (got %d)", K);
+  REQUIRE_PTR(cond_accept, "cond_accept");
+  REQUIRE_PTR(survival, "survival");
+  REQUIRE_PTR(admit_len, "admit_len");
+  return hip_status(dspark::launch_admit(cond_accept, B, N, K, survival, admit_len, (hipStream_t)stream), "admit");
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Host-side launchers of the DSpark kernels (called by the C ABI layer after it
+// has validated every argument).  Each enqueues on `stream` and returns the
+// launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dspark {
+
+// ---- random numbers
+hipError_t launch_philox_blocks(const uint32_t* counters, uint64_t seed, uint32_t* out, int64_t n,
+                                hipStream_t stream);
+hipError_t launch_race_exponentials(uint64_t seed, uint32_t position, uint32_t request_id, uint32_t tag,
+                                    float* out, int64_t n, hipStream_t stream);
+
+// ---- stage 1
+hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, float* logits, int M, int H,
+                               int Vd, hipStream_t stream);
+
+// ---- stage 2
+struct MarkovPlan {
+  int chunks_per_wg;   // 64-wide vocabulary chunks per workgroup
+  int vslices;         // vocabulary slices (workgroups along the vocabulary)
+  int btiles;          // 64-request tiles
+  size_t partial_bytes;
+};
+MarkovPlan plan_markov(int B, int N, int Vd, int r);
+hipError_t launch_markov_sample(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
+                                const int32_t* anchor, const float* temperature, const uint32_t* request_id,
+                                uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,
+                                int r, void* workspace, hipStream_t stream);
+hipError_t launch_build_inverse_map(const int64_t* d2t, int Vd, int V, int32_t* inv_map, hipStream_t stream);
+
+// ---- stage 3
+struct VerifyPlan {
+  int stat_chunks;     // chunks per target row in the row-statistics pass
+  int stat_chunk;      // elements per chunk (multiple of 4)
+  int sample_chunks;   // chunks per sampling row
+  int sample_chunk;
+  size_t stats_bytes, jobs_bytes, race_bytes, total_bytes;
+};
+VerifyPlan plan_verify(int B, int N, int V);
+hipError_t launch_verify(int input_kind, const float* target, const float* draft, const float* draft_log_z,
+                         const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
+                         const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
+                         int32_t* out_tokens, int B, int N, int V, int Vd, void* workspace, hipStream_t stream);
+
+// ---- stage 4
+hipError_t launch_admit(const float* cond_accept, int B, int N, int K, float* survival, int32_t* admit_len,
+                        hipStream_t stream);
+
+}  // namespace dspark

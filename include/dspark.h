@@ -1,0 +1,215 @@
+/*
+ * dspark.h -- C ABI of the DSpark draft-sample-verify hot path for MI355X (gfx950).
+ *
+ * Pages this follows:
+ *   [P1] "DSpark 的实现和测评"              (vLLM's DSpark speculator, walked through)
+ *   [P2] "推测解码：从零到DSpark"            (summary of the DSpark paper)
+ *   [P3] "xserv/docs/25-speculative-methods-comparison.md"
+ *
+ * One round of the path:
+ *   dspark_draft_logits   stage 1: base logits of all N draft positions  [P1 §2.2, §4]
+ *   dspark_markov_sample  stage 2: N-step low-rank Markov Gumbel-max loop [P1 §2.2, §3, §5; P2 §4]
+ *   dspark_admit          stage 4: survival by chain rule, pooled top-K    [P2 §6, §7]
+ *   dspark_verify         stage 3: lossless rejection-sampling verify      [P2 §2; P3 §2]
+ *
+ * Conventions shared by every call
+ *   Memory     Every pointer argument is device memory (HBM) unless stated otherwise.
+ *              The caller owns all buffers; the library never allocates, frees or
+ *              reads device memory on the host.  Buffers touched with 16-byte
+ *              vector accesses must be 16-byte aligned (stated per argument).
+ *   Streams    `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *              only enqueues kernels on it and returns; buffers must stay alive
+ *              until the stream has passed them.  Nothing synchronises.
+ *   Workspace  Calls that need scratch take (workspace, workspace_bytes); the size
+ *              comes from the matching *_workspace_size query.  Contents need no
+ *              initialisation and are undefined afterwards.  One workspace must
+ *              not be used by two calls in flight at once.
+ *   Errors     Arguments are validated on the host before any launch; a failed
+ *              check returns DSPARK_ERR_INVALID / _UNSUPPORTED / _WORKSPACE and
+ *              enqueues nothing.  A failed launch returns DSPARK_ERR_HIP.  Faults
+ *              inside kernels surface at the caller's next synchronisation.  The
+ *              message of the last failure on the calling host thread is in
+ *              dspark_last_error().  No C++ exception crosses this boundary.
+ *   Threads    Calls are reentrant; the only global state is the thread-local
+ *              error message.
+ *   Sampling   All randomness is Philox4x32-10 (Salmon et al., SC'11) with
+ *                key = (seed & 0xffffffff, seed >> 32),
+ *                counter = (index >> 2, position, request_id, tag), word index & 3,
+ *              and uniform u = ((word >> 8) | 1) * 2^-24 in (0, 1).
+ *              tag 0: Gumbel noise of stage 2 (index = draft-vocabulary index);
+ *              tag 1: acceptance uniform of stage 3 (index 0);
+ *              tag 2: residual resample race; tag 3: bonus race (index = target id).
+ *   Temperature  T > 0 divides logits; T == 0 is greedy (argmax, no noise).
+ *   Ties       Every argmax over a vocabulary goes to the smallest target id.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSPARK_ABI_VERSION 1
+
+typedef enum dspark_status {
+  DSPARK_OK = 0,
+  DSPARK_ERR_INVALID = 1,      /* null/misaligned pointer, bad size or flag          */
+  DSPARK_ERR_UNSUPPORTED = 2,  /* valid request beyond this build's limits           */
+  DSPARK_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the size query   */
+  DSPARK_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed         */
+} dspark_status;
+
+enum { DSPARK_INPUT_LOGITS = 0, DSPARK_INPUT_PROBS = 1 };
+
+/* Limits of this build (DSPARK_ERR_UNSUPPORTED beyond them). */
+#define DSPARK_MAX_N 64          /* draft positions per request                      */
+#define DSPARK_MAX_RANK 256      /* Markov rank r                                    */
+#define DSPARK_MAX_B 65535       /* requests                                          */
+#define DSPARK_MAX_ADMIT 16384   /* B * N of one admission call                       */
+
+/* ABI version of the loaded library (== DSPARK_ABI_VERSION of its header). */
+int dspark_abi_version(void);
+
+/* Message of the last failed call on this host thread ("" if none).  Host memory
+ * owned by the library, valid until the next call on the same thread. */
+const char* dspark_last_error(void);
+
+/* ---------------------------------------------------------------- random numbers
+ * Raw Philox4x32-10 blocks, for checking the generator bit for bit.
+ *   counters  [n, 4] uint32, device, 16-byte aligned: (c0, c1, c2, c3) per block
+ *   seed      64-bit key (low word = key0)
+ *   out       [n, 4] uint32, device, 16-byte aligned: the four output words
+ *   n         number of blocks, >= 0 (0 enqueues nothing)
+ */
+dspark_status dspark_philox_blocks(const uint32_t* counters, uint64_t seed, uint32_t* out,
+                                   int64_t n, void* stream);
+
+/* Exponential variates of the stage-3 race: out[v] = -plog2(u(seed, v, position,
+ * request_id, tag)) for v < n, where plog2 is the portable float32 log2 (IEEE
+ * add/multiply/divide only: u = m * 2^e with m in [sqrt2/2, sqrt2), s = (m-1)/(m+1),
+ * log2 u = e + s * (c1 + z(c3 + z(c5 + z(c7 + z c9)))), z = s*s, c_k = fp32(2/(k ln 2))).
+ *   out  [n] float32, device.  n >= 0. */
+dspark_status dspark_race_exponentials(uint64_t seed, uint32_t position, uint32_t request_id,
+                                       uint32_t tag, float* out, int64_t n, void* stream);
+
+/* ---------------------------------------------------------------- stage 1
+ * Draft base logits for every draft position at once [P1 §2.2 (compute_draft_logits),
+ * §4 step 2]:  logits[m, j] = sum_h hidden[m, h] * lm_head[j, h]   (fp32 accumulation).
+ *   hidden   [M, H] bf16 bits, row m = b*N + i (backbone hidden state of position i
+ *            of request b), device, 16-byte aligned
+ *   lm_head  [Vd, H] bf16 bits, one row per draft token (the Hugging Face lm_head
+ *            layout), device, 16-byte aligned
+ *   logits   [M, Vd] float32, device
+ *   M >= 0 (0 enqueues nothing), H > 0 with H % 8 == 0, Vd > 0.
+ */
+dspark_status dspark_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, float* logits,
+                                  int M, int H, int Vd, void* stream);
+
+/* ---------------------------------------------------------------- stage 2
+ * Sequential low-rank Markov sampling [P1 §2.2 (_sample_sequential), §3
+ * (DSparkMarkovHead), §5 (reduced vocabulary); P2 §4].  For request b, with
+ * prev = anchor[b], for i = 0 .. N-1:
+ *     e      = w1[prev, :]                         (r values)
+ *     bias_j = sum_k w2[j, k] * e_k                (j < Vd)
+ *     l_j    = logits[b, i, j] + bias_j            (written back in place, fp32)
+ *     x      = t(argmax_j key_j),   t(j) = j + d2t[j]  (t(j) = j without d2t)
+ *              key_j = l_j / T_b + Gumbel(u(seed, j, i, request_id[b], 0))   (T_b > 0)
+ *              key_j = l_j                                                    (T_b == 0)
+ *     draft_tokens[b, i] = x;   log_z[b, i] = log sum_j exp(l_j / T_b)  (T_b == 0: max_j l_j)
+ *     prev = x
+ *   logits       [B, N, Vd] float32, device, 16-byte aligned.  In: base logits (stage 1
+ *                output).  Out: processed logits l (untempered), what verify reads.
+ *   w1           [V, r] bf16 bits, device, 16-byte aligned: markov_w1, indexed by target id
+ *   w2           [Vd, r] bf16 bits, device, 16-byte aligned: markov_w2, one row per draft token
+ *   d2t          [Vd] int64 offsets (target id = j + d2t[j]), device, or NULL iff Vd == V.
+ *                Must map [0, Vd) injectively into [0, V) (not checked on the device).
+ *   anchor       [B] int32 target ids in [0, V), device
+ *   temperature  [B] float32 >= 0, device
+ *   request_id   [B] uint32, device (Philox counter word 2)
+ *   draft_tokens [B, N] int32 out, device (target ids)
+ *   log_z        [B, N] float32 out, device
+ *   1 <= B <= DSPARK_MAX_B, 1 <= N <= DSPARK_MAX_N, V % 4 == 0, Vd % 4 == 0, Vd <= V,
+ *   8 <= r <= DSPARK_MAX_RANK with r % 8 == 0.
+ *   workspace    >= dspark_markov_workspace_size(B, N, Vd, r) bytes, device, 16-byte aligned.
+ */
+size_t dspark_markov_workspace_size(int B, int N, int Vd, int r);
+dspark_status dspark_markov_sample(float* logits, const uint16_t* w1, const uint16_t* w2,
+                                   const int64_t* d2t, const int32_t* anchor,
+                                   const float* temperature, const uint32_t* request_id,
+                                   uint64_t seed, int32_t* draft_tokens, float* log_z,
+                                   int B, int N, int V, int Vd, int r,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Inverse of the reduced-vocabulary map [P3 §3.2 (d2t)]: inv_map[v] = j if
+ * v == j + d2t[j], else -1.
+ *   d2t [Vd] int64, device (injective into [0, V), not checked on the device);
+ *   inv_map [V] int32 out, device.  0 < Vd <= V. */
+dspark_status dspark_build_inverse_map(const int64_t* d2t, int Vd, int V, int32_t* inv_map,
+                                       void* stream);
+
+/* ---------------------------------------------------------------- stage 3
+ * Lossless rejection-sampling verification [P2 §2; greedy case P3 §2].  Request b
+ * with L = verify_len[b] (N when verify_len is NULL), x_k = draft_tokens[b, k]:
+ *   for k < L: u_k = u(seed, 0, k, request_id[b], 1); accept x_k iff
+ *              (double)u_k * p_d[k](x_k) < (double)p_t[k](x_k);
+ *   first rejection at k:  y = race sample (tag 2, position k) of
+ *              r_v = max(0, p_t[k](v) - p_d[k](v))  (float32 subtraction);
+ *              if every r_v == 0, of p_t[k] itself (same uniforms);
+ *   all L accepted:        y = race sample (tag 3, position L) of p_t[L].
+ *   Race sample of weights r: argmax_v r_v / E_v with E_v the variates of
+ *   dspark_race_exponentials, compared exactly as r_a*E_b vs r_b*E_a in double,
+ *   ties to the smaller v.
+ *   Outputs: accepted[b] = number of accepted draft tokens a;
+ *            out_tokens[b, :] = x_0 .. x_{a-1}, y, then -1 up to column N.
+ * input_kind DSPARK_INPUT_PROBS: target = p_t [B, N+1, V] float32 probabilities,
+ *            draft = p_d [B, N, Vd] float32 probabilities; draft_log_z and
+ *            temperature are ignored (may be NULL).  Given the same float32 arrays
+ *            the result is bit-identical to the rule above.
+ * input_kind DSPARK_INPUT_LOGITS: target = target logits [B, N+1, V] float32,
+ *            draft = processed draft logits [B, N, Vd] (stage 2 output), draft_log_z
+ *            = stage 2's log_z [B, N] (required); p_t = softmax(target / T),
+ *            p_d(j) = exp(draft_j / T - log_z), both evaluated in float32 on the GPU.
+ *            T == 0: p_t is the point mass on the target row's argmax and p_d the
+ *            point mass on x_k (no randomness is used).
+ *   target, draft  device, 16-byte aligned.  Only rows k <= L of the target and the
+ *            entries needed of draft rows k < L are read.
+ *   draft_tokens [B, N] int32 target ids, device.
+ *   inv_map  [V] int32 (dspark_build_inverse_map), device; NULL iff Vd == V.
+ *   verify_len [B] int32 in [0, N], device, or NULL (= N); dspark_admit's admit_len fits.
+ *   temperature [B] float32 >= 0 (logits mode), request_id [B] uint32, device.
+ *   accepted [B] int32 out; out_tokens [B, N+1] int32 out; device.
+ *   1 <= B <= DSPARK_MAX_B, 1 <= N <= DSPARK_MAX_N, V % 4 == 0, Vd % 4 == 0, Vd <= V.
+ *   workspace >= dspark_verify_workspace_size(B, N, V) bytes, device, 16-byte aligned.
+ */
+size_t dspark_verify_workspace_size(int B, int N, int V);
+dspark_status dspark_verify(int input_kind, const float* target, const float* draft,
+                            const float* draft_log_z, const int32_t* draft_tokens,
+                            const int32_t* inv_map, const int32_t* verify_len,
+                            const float* temperature, const uint32_t* request_id, uint64_t seed,
+                            int32_t* accepted, int32_t* out_tokens,
+                            int B, int N, int V, int Vd,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- stage 4
+ * Confidence-scheduled admission [P2 §6 (chain rule, pooled greedy sort), §7 (K fixed
+ * ahead, sort at the last moment, non-anticipation)]:
+ *   survival[b, 0] = c[b, 0];  survival[b, k] = survival[b, k-1] * c[b, k]  (float32);
+ *   all B*N (b, k) ordered by survival descending, then k ascending, then b ascending;
+ *   the first min(K, B*N) admitted; admit_len[b] = admitted positions of request b.
+ *   With c in [0, 1] every request's admitted set is a prefix, and whether (b, k) is
+ *   admitted never depends on c[b, j > k].
+ *   cond_accept [B, N] float32 in [0, 1], device; survival [B, N] float32 out, device;
+ *   admit_len [B] int32 out, device.  1 <= B, 1 <= N <= DSPARK_MAX_N,
+ *   B * N <= DSPARK_MAX_ADMIT, K >= 0.  Runs as one workgroup; no workspace.
+ */
+dspark_status dspark_admit(const float* cond_accept, int B, int N, int K, float* survival,
+                           int32_t* admit_len, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,253 @@
+"""GPU parity of each stage against the oracle, through the C ABI.
+
+Small cases compare every output; the full Qwen3-8B-shaped workloads compare
+sampled requests / entries (the stages never mix requests, except admission,
+which is always compared in full).
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_sampling_lossless_amd as dsl
+import synth
+from oracle import philox, stages, variates
+
+from gpu_util import compare_markov, compare_verify, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(dspark_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- random numbers
+
+def test_philox_blocks_bit_exact():
+    g = np.random.default_rng(0)
+    ctr = g.integers(0, 2**32, size=(10_000, 4), dtype=np.uint64)
+    ctr[0] = [0, 0, 0, 0]
+    ctr[1] = [0xFFFFFFFF] * 4
+    for seed in (0, 0xFFFFFFFFFFFFFFFF, 0x299F31D0A4093822, 12345):
+        say(f"philox seed={seed:#x}")
+        out = host(dsl.philox_blocks(dev(ctr.astype(np.uint32)), seed)).view(np.uint32)
+        ref = philox.philox4x32_10(ctr[:, 0], ctr[:, 1], ctr[:, 2], ctr[:, 3], seed & 0xFFFFFFFF, seed >> 32)
+        assert np.array_equal(out, np.stack(ref, axis=1).astype(np.uint32))
+
+
+@pytest.mark.parametrize("n,pos,req,tag", [(1 << 16, 0, 0, 2), (151936, 7, 12345, 3), (37, 1, 2**32 - 1, 2)])
+def test_race_exponentials_bit_exact(n, pos, req, tag):
+    say(f"race_exponentials n={n}")
+    out = host(dsl.race_exponentials(0xDEADBEEF12345678, pos, req, tag, n))
+    ref = variates.race_exponentials(0xDEADBEEF12345678, n, pos, req, tag)
+    assert out.dtype == np.float32 and np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------- stage 1
+
+@pytest.mark.parametrize("M,H,Vd", [(8, 256, 1024), (20, 264, 1000), (40, 256, 996), (1, 4096, 4096),
+                                    (300, 200, 1004), (129, 4096, 640), (64, 64, 68)])
+def test_draft_logits_small(M, H, Vd):
+    say(f"draft_logits M={M} H={H} Vd={Vd}")
+    g = np.random.default_rng(M * 7 + H)
+    hid = synth.bf16_bits(g.normal(0, 1, size=(M, H)).astype(np.float32))
+    W = synth.bf16_bits(g.normal(0, 0.02, size=(Vd, H)).astype(np.float32))
+    out = host(dsl.draft_logits(dev(hid), dev(W)))
+    ref = stages.draft_logits(hid, W)
+    err = np.abs(out.astype(np.float64) - ref.astype(np.float64)).max()
+    say(f"  max |err| = {err:.3g}")
+    assert err <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b_single", "batched", "reduced_vocab"])
+def test_draft_logits_full_size_sampled(name):
+    w = synth.get(name)
+    say(f"draft_logits full size {name}: M={w.M} H={w.H} Vd={w.Vd}")
+    hid = synth.hidden_bf16(w)
+    W = synth.lm_head_bf16(w)
+    out = dsl.draft_logits(dev(hid), dev(W))
+    g = np.random.default_rng(1)
+    cols = np.unique(np.concatenate([g.integers(0, w.Vd, 300), [0, w.Vd - 1]]))
+    rows = np.unique(np.concatenate([g.integers(0, w.M, 16), [0, w.M - 1]]))
+    got = host(out[torch.as_tensor(rows).cuda()][:, torch.as_tensor(cols).cuda()])
+    ref = stages.draft_logits(hid[rows], synth.lm_head_bf16(w, rows=cols))
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64)).max()
+    say(f"  max |err| = {err:.3g}")
+    assert err <= 2e-2
+
+
+# ---------------------------------------------------------------- stage 2
+
+def _markov_case(B, N, V, Vd, r, temps, seed=0, base=None, d2t=None):
+    g = np.random.default_rng(B * 1000 + N * 10 + r)
+    if base is None:
+        base = (g.normal(0, 1.28, size=(B, N, Vd))).astype(np.float32)
+    w1 = synth.bf16_bits(g.normal(0, 0.02 * 8, size=(V, r)).astype(np.float32))
+    w2 = synth.bf16_bits(g.normal(0, 0.02 * 8, size=(Vd, r)).astype(np.float32))
+    anchor = g.integers(0, V, size=B).astype(np.int32)
+    temp = np.asarray(temps, np.float32)[g.integers(0, len(temps), size=B)]
+    rid = (np.arange(B) * 7 + 3).astype(np.uint32)
+    return dict(base=base, w1=w1, w2=w2, d2t=d2t, anchor=anchor, temp=temp, rid=rid, seed=seed, V=V)
+
+
+def _run_markov_gpu(c):
+    logits = dev(c["base"])
+    tok, logz = dsl.markov_sample(logits, dev(c["w1"]), dev(c["w2"]),
+                                  None if c["d2t"] is None else dev(c["d2t"]),
+                                  dev(c["anchor"]), dev(c["temp"]), dev(c["rid"]), c["seed"])
+    return host(tok), host(logits), host(logz)
+
+
+@pytest.mark.parametrize("B,N,V,Vd,r,temps,reduced", [
+    (1, 8, 1024, 1024, 16, (1.0,), False),
+    (1, 8, 1024, 1024, 16, (0.0,), False),
+    (70, 5, 2048, 2048, 64, (0.0, 0.7, 1.0), False),
+    (33, 4, 4096, 1000, 32, (0.0, 0.7, 1.0), True),
+    (20, 3, 3000, 3000, 256, (0.7,), False),
+    (130, 2, 1024, 1024, 8, (1.0,), False),
+])
+def test_markov_small(B, N, V, Vd, r, temps, reduced):
+    say(f"markov B={B} N={N} V={V} Vd={Vd} r={r} T={temps} reduced={reduced}")
+    d2t = None
+    if reduced:
+        g = np.random.default_rng(5)
+        d2t = (g.permutation(V)[:Vd] - np.arange(Vd)).astype(np.int64)
+    c = _markov_case(B, N, V, Vd, r, temps, seed=0x1234, d2t=d2t)
+    tok, proc, logz = _run_markov_gpu(c)
+    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], d2t, c["anchor"], c["temp"], c["rid"], c["seed"])
+    checked, near = compare_markov(tok, proc, logz, ref)
+    say(f"  compared {checked} positions, {near} near-tie mismatches")
+    if d2t is not None:
+        image = set((np.arange(Vd) + d2t).tolist())
+        assert all(int(t) in image for t in tok.ravel())
+
+
+@pytest.mark.parametrize("name,nsample", [("qwen3_8b_single", 1), ("batched", 4), ("admission", 3),
+                                          ("reduced_vocab", 6)])
+def test_markov_full_size_sampled(name, nsample):
+    w = synth.get(name)
+    say(f"markov full size {name}: B={w.B} N={w.N} Vd={w.Vd} r={w.r}")
+    rp = synth.request_params(w)
+    d2t = synth.d2t_offsets(w)
+    g = np.random.default_rng(2)
+    reqs = np.array(sorted({0, w.B - 1, *g.integers(0, w.B, nsample).tolist()}))
+    # every request gets stand-in base logits on the device; the sampled ones the seeded values
+    base = torch.randn((w.B, w.N, w.Vd), device="cuda", dtype=torch.float32) * (w.weight_std * w.H ** 0.5)
+    sb = synth.synthetic_base_logits(w, reqs)
+    base[torch.as_tensor(reqs).cuda()] = dev(sb)
+    w1, w2 = synth.markov_w1_bf16(w), synth.markov_w2_bf16(w)
+    tok, logz = dsl.markov_sample(base, dev(w1), dev(w2), None if d2t is None else dev(d2t), dev(rp["anchor"]),
+                                  dev(rp["temperature"]), dev(rp["request_id"]), w.philox_seed)
+    tok, logz = host(tok)[reqs], host(logz)[reqs]
+    proc = host(base[torch.as_tensor(reqs).cuda()])
+    ref = stages.markov_sample(sb, w1, w2, d2t, rp["anchor"], rp["temperature"], rp["request_id"],
+                               w.philox_seed, requests=reqs)
+    checked, near = compare_markov(tok, proc, logz, ref)
+    say(f"  requests {reqs.tolist()}: compared {checked} positions, {near} near-tie mismatches")
+
+
+# ---------------------------------------------------------------- stage 3
+
+def _verify_inputs(B, N, V, Vd, temps, seed, reduced=False, sigma=1.0):
+    g = np.random.default_rng(seed)
+    d2t = inv = None
+    if reduced:
+        d2t = (g.permutation(V)[:Vd] - np.arange(Vd)).astype(np.int64)
+        inv = stages.build_inverse_map(d2t, Vd, V)
+    proc = g.normal(0, 1.28, size=(B, N, Vd)).astype(np.float32)
+    tgt = g.normal(0, sigma, size=(B, N + 1, V))
+    t_of_j = np.arange(Vd) + (0 if d2t is None else d2t)
+    tgt[:, :N, t_of_j] += proc
+    tgt[:, N, t_of_j] += proc[:, N - 1]
+    tgt = tgt.astype(np.float32)
+    temp = np.asarray(temps, np.float32)[g.integers(0, len(temps), size=B)]
+    # drafts: the target id of a draw from the tempered draft row (argmax at T = 0)
+    tok = np.empty((B, N), np.int32)
+    for b in range(B):
+        for k in range(N):
+            if temp[b] > 0:
+                p = stages.probs_from_logits(proc[b, k], float(temp[b])).astype(np.float64)
+                j = g.choice(Vd, p=p / p.sum())
+            else:
+                j = int(np.argmax(proc[b, k]))
+            tok[b, k] = t_of_j[j]
+    L = g.integers(0, N + 1, size=B).astype(np.int32)
+    rid = (np.arange(B) * 3 + 11).astype(np.uint32)
+    return dict(proc=proc, tgt=tgt, temp=temp, tok=tok, L=L, rid=rid, d2t=d2t, inv=inv)
+
+
+@pytest.mark.parametrize("B,N,V,Vd,reduced", [(200, 6, 1024, 1024, False), (64, 8, 2048, 1000, True),
+                                              (3, 1, 64, 64, False)])
+def test_verify_probs_bit_exact(B, N, V, Vd, reduced):
+    say(f"verify probs B={B} N={N} V={V} Vd={Vd}")
+    c = _verify_inputs(B, N, V, Vd, (0.7, 1.0), seed=B + N, reduced=reduced)
+    p_t = np.stack([[stages.probs_from_logits(c["tgt"][b, k], float(c["temp"][b])) for k in range(N + 1)]
+                    for b in range(B)])
+    p_d = np.stack([[stages.probs_from_logits(c["proc"][b, k], float(c["temp"][b])) for k in range(N)]
+                    for b in range(B)])
+    seed = 0xABCDEF0123
+    acc, out = dsl.verify(dsl.INPUT_PROBS, dev(p_t), dev(p_d), None, dev(c["tok"]),
+                          None if c["inv"] is None else dev(c["inv"]), dev(c["L"]), None, dev(c["rid"]), seed)
+    ref = stages.verify("probs", p_t, p_d, c["tok"], c["inv"], c["L"], None, c["rid"], seed)
+    compare_verify(host(acc), host(out), ref, exact=True)
+    say(f"  accepted mean {host(acc).mean():.2f}")
+
+
+@pytest.mark.parametrize("B,N,V,Vd,temps,reduced", [(200, 6, 1024, 1024, (0.0, 0.7, 1.0), False),
+                                                    (64, 8, 2048, 1000, (0.0, 1.0), True),
+                                                    (16, 4, 4096, 4096, (0.0,), False)])
+def test_verify_logits_parity(B, N, V, Vd, temps, reduced):
+    say(f"verify logits B={B} N={N} V={V} Vd={Vd} T={temps}")
+    c = _verify_inputs(B, N, V, Vd, temps, seed=B * N + 1, reduced=reduced)
+    # draft log Z of the processed rows (the oracle's values; stage 2 emits the same quantity)
+    logz = np.empty((B, N), np.float32)
+    for b in range(B):
+        for k in range(N):
+            T = float(c["temp"][b])
+            y = c["proc"][b, k].astype(np.float64)
+            logz[b, k] = (np.log(np.exp(y / T - (y / T).max()).sum()) + (y / T).max()) if T > 0 else y.max()
+    seed = 77
+    acc, out = dsl.verify(dsl.INPUT_LOGITS, dev(c["tgt"]), dev(c["proc"]), dev(logz), dev(c["tok"]),
+                          None if c["inv"] is None else dev(c["inv"]), dev(c["L"]), dev(c["temp"]), dev(c["rid"]),
+                          seed)
+    ref = stages.verify("logits", c["tgt"], c["proc"], c["tok"], c["inv"], c["L"], c["temp"], c["rid"], seed)
+    near = compare_verify(host(acc), host(out), ref, exact=False)
+    say(f"  {near} near-tie requests of {B}")
+    assert near <= max(1, B // 50)
+
+
+def test_verify_greedy_is_longest_argmax_prefix():
+    B, N, V = 100, 6, 1024
+    c = _verify_inputs(B, N, V, V, (0.0,), seed=9, sigma=0.3)
+    L = np.full(B, N, np.int32)
+    logz = c["proc"].max(axis=2).astype(np.float32)
+    acc, out = dsl.verify(dsl.INPUT_LOGITS, dev(c["tgt"]), dev(c["proc"]), dev(logz), dev(c["tok"]), None,
+                          dev(L), dev(c["temp"]), dev(c["rid"]), 5)
+    acc, out = host(acc), host(out)
+    am = c["tgt"].argmax(axis=2)
+    for b in range(B):
+        a = 0
+        while a < N and c["tok"][b, a] == am[b, a]:
+            a += 1
+        assert acc[b] == a and out[b, a] == am[b, a]
+        assert np.array_equal(out[b, :a], c["tok"][b, :a]) and (out[b, a + 1:] == -1).all()
+
+
+# ---------------------------------------------------------------- stage 4
+
+@pytest.mark.parametrize("B,N,K", [(256, 16, 1024), (1, 8, 3), (100, 7, 0), (100, 7, 700), (100, 7, 5000),
+                                   (1024, 16, 9000), (7, 64, 100), (64, 8, 1)])
+def test_admit_bit_exact(B, N, K):
+    say(f"admit B={B} N={N} K={K}")
+    w = synth.get("admission", B=B, N=N)
+    c = synth.confidence(w)
+    if B >= 64:
+        c[:8] = c[8:16]          # exact survival ties across requests
+    surv, L = dsl.admit(dev(c), K)
+    ref = stages.admit(c, K)
+    assert np.array_equal(host(surv).view(np.uint32), ref["survival"].view(np.uint32))
+    assert np.array_equal(host(L), ref["admit_len"])
