@@ -1,0 +1,318 @@
+"""Benchmark of the DSpark draft-sample-verify path on one MI355X.
+
+One step = one round of the whole hot path over one batch of synthetic input:
+  stage 1 draft_logits -> stage 2 markov_sample -> stage 4 admit -> stage 3 verify
+(verify on the admitted prefixes, logits input).  All inputs are resident in
+HBM before the timed region; the target logits are the step's own base logits
+plus seeded noise, made once before timing.
+
+Metric: draft+verify positions per second (B * N per step), plus the roofline
+of the dominant kernel (the draft-logit GEMM: HBM-bound when the batch is a few
+positions, MFMA-bound for large batches) measured with HIP events on the stream
+the kernels run on, and the CPU oracle timed on a bounded sample of the same
+workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--graph]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="qwen3_8b_single",
+                   help="tiny | qwen3_8b_single | batched | admission | reduced_vocab")
+    p.add_argument("--graph", action="store_true", help="replay each step as one captured HIP graph")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB five times (reference for the "
+                        "HBM byte counters) and exit")
+    return p.parse_args()
+
+
+def src_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+class Path:
+    """Device buffers and the four C-ABI calls of one round."""
+
+    def __init__(self, w, torch, dsl, synth):
+        self.w, self.torch, self.dsl = w, torch, dsl
+        dev = torch.device("cuda:0")
+        rp = synth.request_params(w)
+
+        def up(x):
+            x = np.ascontiguousarray(x)
+            if x.dtype == np.uint16:
+                x = x.view(np.int16)
+            if x.dtype == np.uint32:
+                x = x.view(np.int32)
+            return torch.from_numpy(x).to(dev)
+
+        t0 = time.time()
+        self.hidden = up(synth.hidden_bf16(w))
+        self.lm_head = up(synth.lm_head_bf16(w))
+        self.w1 = up(synth.markov_w1_bf16(w))
+        self.w2 = up(synth.markov_w2_bf16(w))
+        d2t = synth.d2t_offsets(w)
+        self.d2t = None if d2t is None else up(d2t)
+        self.inv = None if d2t is None else dsl.build_inverse_map(self.d2t, w.V)
+        self.anchor = up(rp["anchor"])
+        self.temp = up(rp["temperature"])
+        self.rid = up(rp["request_id"])
+        self.sigma = up(rp["sigma"])
+        self.conf = up(synth.confidence(w))
+        self.K = w.budget
+        self.seed = w.philox_seed
+        self.logits = torch.empty((w.B, w.N, w.Vd), dtype=torch.float32, device=dev)
+        self.tokens = torch.empty((w.B, w.N), dtype=torch.int32, device=dev)
+        self.logz = torch.empty((w.B, w.N), dtype=torch.float32, device=dev)
+        self.survival = torch.empty((w.B, w.N), dtype=torch.float32, device=dev)
+        self.admit_len = torch.empty(w.B, dtype=torch.int32, device=dev)
+        self.accepted = torch.empty(w.B, dtype=torch.int32, device=dev)
+        self.out_tokens = torch.empty((w.B, w.N + 1), dtype=torch.int32, device=dev)
+        self.ws_markov = torch.empty(max(16, dsl.markov_workspace_size(w.B, w.N, w.Vd, w.r)),
+                                     dtype=torch.uint8, device=dev)
+        self.ws_verify = torch.empty(max(16, dsl.verify_workspace_size(w.B, w.N, w.V)),
+                                     dtype=torch.uint8, device=dev)
+        # target logits [B, N+1, V]: this batch's base logits (row N repeats row N-1),
+        # scattered to target ids, plus N(0, sigma_b) noise -- made once, untimed
+        dsl.draft_logits(self.hidden, self.lm_head, out=self.logits.view(w.M, w.Vd))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed)
+        self.target = torch.randn((w.B, w.N + 1, w.V), generator=gen, device=dev, dtype=torch.float32)
+        self.target.mul_(self.sigma.view(-1, 1, 1))
+        rows = list(range(w.N)) + [w.N - 1]
+        if self.d2t is None:
+            self.target.add_(self.logits[:, rows])
+        else:
+            tids = torch.arange(w.Vd, device=dev, dtype=torch.int64) + self.d2t
+            self.target[:, :, tids] += self.logits[:, rows]
+        torch.cuda.synchronize()
+        self.setup_s = time.time() - t0
+        self.ev = None
+
+    def step(self, events=None):
+        """One round.  events: optional list of 5 torch.cuda.Event bracketing the stages."""
+        w, dsl = self.w, self.dsl
+        rec = (lambda i: events[i].record()) if events else (lambda i: None)
+        rec(0)
+        dsl.draft_logits(self.hidden, self.lm_head, out=self.logits.view(w.M, w.Vd))
+        rec(1)
+        dsl.markov_sample(self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, self.seed,
+                          draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov)
+        rec(2)
+        dsl.admit(self.conf, self.K, survival=self.survival, admit_len=self.admit_len)
+        rec(3)
+        dsl.verify(dsl.INPUT_LOGITS, self.target, self.logits, self.logz, self.tokens, self.inv, self.admit_len,
+                   self.temp, self.rid, self.seed, accepted=self.accepted, out_tokens=self.out_tokens,
+                   workspace=self.ws_verify)
+        rec(4)
+
+
+def k1_work(w):
+    """Algorithmic work of one draft-logit GEMM launch: bytes and flops."""
+    bytes_ = 2 * w.Vd * w.H + 2 * w.M * w.H + 4 * w.M * w.Vd
+    flops = 2 * w.M * w.H * w.Vd
+    return bytes_, flops
+
+
+def k1_roofline(w, k1_ms):
+    bytes_, flops = k1_work(w)
+    # arithmetic intensity vs the ridge of the chip decides the bound
+    ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops / bytes_ < ridge:
+        ach = bytes_ / (k1_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = flops / (k1_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFS, 4)}
+    roof["kernel"] = "draft_logits (k1_skinny)" if w.M <= 64 else "draft_logits (k1_tiled)"
+    roof["traffic"] = measured_traffic(w)
+    return roof
+
+
+def measured_traffic(w):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else null."""
+    path = os.path.join(PROFILES, f"draft_logits_{w.name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        if d.get("source_sha256_16") != src_hash(os.path.join(ROOT, "draft_sampling_lossless_amd", "csrc",
+                                                              "gemm.hip")):
+            return None
+        return d.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle, as it stands, on a bounded sample of the workload: whole rounds
+    of the first request (all N positions, full vocabulary), repeated while the
+    budget lasts (at least once)."""
+    import synth
+    from oracle import stages
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    reqs = [0]
+    ws = synth.get(w.name, B=1, K=None if w.K is None else max(1, w.K // w.B))
+    rp = synth.request_params(w)
+    hid = synth.hidden_bf16(w, rows=list(range(w.N)))
+    lm = synth.lm_head_bf16(w)
+    w1, w2 = synth.markov_w1_bf16(w), synth.markov_w2_bf16(w)
+    d2t = synth.d2t_offsets(w)
+    inv = None if d2t is None else stages.build_inverse_map(d2t, w.Vd, w.V)
+    conf = synth.confidence(w)[:1]
+    noise = synth.target_noise(w, reqs)
+    t_of_j = np.arange(w.Vd) + (0 if d2t is None else d2t)
+    runs, t_total = 0, 0.0
+    while runs == 0 or t_total < budget_s:
+        t0 = time.perf_counter()
+        base = stages.draft_logits(hid, lm).reshape(1, w.N, w.Vd)
+        mk = stages.markov_sample(base, w1, w2, d2t, rp["anchor"], rp["temperature"], rp["request_id"],
+                                  w.philox_seed, requests=reqs)
+        ad = stages.admit(conf, ws.budget)
+        tgt = noise * rp["sigma"][0]
+        tgt[:, :, t_of_j] += base[:, list(range(w.N)) + [w.N - 1]]
+        stages.verify("logits", tgt.astype(np.float32), mk["processed"], mk["tokens"], inv, ad["admit_len"],
+                      rp["temperature"], rp["request_id"], w.philox_seed, requests=reqs)
+        t_total += time.perf_counter() - t0
+        runs += 1
+        if t_total > budget_s:
+            break
+    pos = runs * w.N
+    return {"value": round(pos / t_total, 3), "unit": "positions/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{runs} round(s) of request 0 of {w.name} (N={w.N} positions, V={w.V}, full stage 1-4 "
+                      f"oracle incl. the {w.Vd}x{w.H} fp64 draft-logit product), {t_total:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "requested_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import draft_sampling_lossless_amd as dsl
+    import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+        return
+    if not os.path.exists(dsl.LIB_PATH):
+        from draft_sampling_lossless_amd import build
+        build.build()
+    w = synth.get(args.workload)
+    path = Path(w, torch, dsl, synth)
+
+    graph = None
+    if args.graph:
+        for _ in range(2):
+            path.step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            path.step()
+        torch.cuda.synchronize()
+
+    def run_step(events=None):
+        if graph is not None:
+            if events:
+                events[0].record()
+            graph.replay()
+            if events:
+                for e in events[1:]:
+                    e.record()
+        else:
+            path.step(events)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, no per-stage events (they would add work)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-stage durations with HIP events on the launch stream (eager steps)
+    stage_ms = np.zeros(4)
+    nrep = max(5, min(args.steps, 50))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nrep)]
+    for e in evs:
+        path.step(e)
+    torch.cuda.synchronize()
+    for e in evs:
+        stage_ms += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
+    stage_ms /= nrep
+
+    positions = w.B * w.N
+    value = positions / (ms_per_step * 1e-3)
+    roof = k1_roofline(w, stage_ms[0])
+    result = {
+        "metric": "draft+verify positions/sec (B*N) and achieved HBM GB/s at V=151936",
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "V": w.V, "Vd": w.Vd, "r": w.r,
+                   "K": w.budget, "graph": bool(args.graph)},
+        "stage_ms": {"draft_logits": round(stage_ms[0], 4), "markov_sample": round(stage_ms[1], 4),
+                     "admit": round(stage_ms[2], 4), "verify": round(stage_ms[3], 4)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
