@@ -149,7 +149,10 @@ def k1_roofline(w, k1_ms):
         ach = flops / (k1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_BF16_PEAK_TFS, 4)}
-    roof["kernel"] = "draft_logits (k1_skinny)" if w.M <= 64 else "draft_logits (k1_tiled)"
+    if w.M <= 16 and w.H % 512 == 0 and w.H <= 4096:
+        roof["kernel"] = "draft_logits (k1_stream)"
+    else:
+        roof["kernel"] = "draft_logits (k1_skinny)" if w.M <= 64 else "draft_logits (k1_tiled)"
     roof["traffic"] = measured_traffic(w)
     return roof
 

@@ -90,7 +90,7 @@ dspark_status dspark_draft_logits(const uint16_t* hidden, const uint16_t* lm_hea
 
 size_t dspark_markov_workspace_size(int B, int N, int Vd, int r) {
   if (B <= 0 || N <= 0 || Vd <= 0 || r <= 0) return 0;
-  return dspark::plan_markov(B, N, Vd, r).partial_bytes;
+  return dspark::plan_markov(B, N, Vd, r, 0).partial_bytes;
 }
 
 dspark_status dspark_markov_sample(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,

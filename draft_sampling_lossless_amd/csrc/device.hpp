@@ -112,6 +112,12 @@ __device__ __forceinline__ void lse2_merge(float& m, float& s, float m2, float s
   m = mn;
 }
 
+// Workgroup barrier without the memory fence of __syncthreads() (which makes every
+// wave wait for all of its outstanding global loads): only this wave's LDS
+// operations are completed first.  Used where asynchronous global->LDS loads must
+// stay in flight across the barrier; their completion is awaited explicitly.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 }  // namespace dspark

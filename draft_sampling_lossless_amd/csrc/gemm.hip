@@ -1,11 +1,18 @@
 // Stage 1: draft base logits, logits[m, j] = sum_h hidden[m, h] * lm_head[j, h]
 // (bf16 in, fp32 accumulate and out) on gfx950 MFMA (v_mfma_f32_16x16x32_bf16).
 //
-// Two tilings, picked by M (= B * N, the number of draft positions):
-//  * skinny (M <= 64): the product is bound by streaming the LM head from HBM
-//    (2 * Vd * H bytes, read once).  Each wave owns 16*FR vocabulary rows and
-//    streams them straight from global memory into MFMA B fragments; the few
-//    hidden rows (A fragments) come from L1/L2.  No LDS.
+// Three tilings, picked by the shape (M = B * N, the number of draft positions):
+//  * stream (M <= 16, H % 512 == 0, H <= 4096): bound by streaming the LM head
+//    from HBM (2 * Vd * H bytes, read once).  One persistent workgroup per CU
+//    walks 16-row blocks of the LM head; each block's rows arrive 512 k at a time
+//    (1 KB per row) through a 3-stage LDS ring filled by direct global->LDS loads,
+//    so every load instruction reads 1 KB contiguous and two stages stay in
+//    flight across the barriers.  The hidden rows sit in registers for the whole
+//    kernel (each wave always takes the same 4 k steps of a stage); the 4 waves'
+//    partial sums of a block are added in LDS.
+//  * skinny (other M <= 64): each wave owns 16*FR vocabulary rows and streams them
+//    straight from global memory into MFMA B fragments; the hidden rows (A
+//    fragments) come from L1/L2.  No LDS.
 //  * tiled (M > 64): MFMA-bound.  128 x 128 output tiles, BK = 64, both operands
 //    staged through double-buffered LDS; 4 waves, each a 64 x 64 block of 16x16
 //    MFMA fragments.
@@ -97,6 +104,101 @@ __global__ __launch_bounds__(256) void k1_skinny(const uint16_t* __restrict__ A,
         if (m < M) C[(size_t)m * Vd + j] = acc[t][f][i];
       }
     }
+}
+
+// ------------------------------------------------------------------ stream
+
+constexpr int SNS = 3;                        // ring stages
+constexpr int SROW = 1024 + 16;               // LDS bytes per row of a stage (512 k + pad)
+constexpr int SSTAGE = 16 * SROW;             // one stage: 16 rows x 512 k
+constexpr int SLDS = SNS * SSTAGE + 4 * 64 * 4 * 4;  // ring + cross-wave reduction
+
+__global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                                                 float* __restrict__ C, int M, int H, int Vd) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* ring = smem;
+  float* red = reinterpret_cast<float*>(smem + SNS * SSTAGE);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int spb = H / 512;  // stages per 16-row block (<= 8)
+
+  // hidden rows: fragment of stage st, k step 4*wave+u (rows >= M are zero)
+  bf16x8 af[8][4];
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = st * 512 + (wave * 4 + u) * 32 + 8 * g;
+      af[st][u] = (st < spb && n < M) ? load_bf16x8(A + (size_t)n * H + k) : zero_bf16x8();
+    }
+
+  const int nblocks = (Vd + 15) / 16;
+  const int myblocks = (nblocks - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int T = myblocks * spb;  // stages this workgroup consumes
+  // stage t: block blockIdx.x + (t / spb) * gridDim.x, k range (t % spb) * 512 .. +512;
+  // wave w loads rows w, w+4, w+8, w+12 of it (one 1 KB instruction each)
+  auto issue = [&](int t) {
+    const int blk = blockIdx.x + (t / spb) * gridDim.x, kst = t % spb;
+    char* base = ring + (t % SNS) * SSTAGE;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = wave + 4 * q;
+      const int j = min(blk * 16 + row, Vd - 1);  // rows past Vd load a valid row, never stored
+      __builtin_amdgcn_global_load_lds(W + (size_t)j * H + kst * 512 + lane * 8, base + row * SROW, 16, 0, 0);
+    }
+  };
+  for (int t = 0; t < SNS - 1 && t < T; ++t) issue(t);
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < T; ++t) {
+    // this wave's loads of stage t are done once at most (SNS-2) later stages are pending
+    if (t + SNS - 2 < T) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((SNS - 2) * 4) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // every wave's share of stage t is in LDS; stage t-1's buffer is free
+    if (t + SNS - 1 < T) issue(t + SNS - 1);
+    const char* buf = ring + (t % SNS) * SSTAGE;
+    const int kst = t % spb;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st != kst) continue;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = wave * 4 + u;
+        const bf16x8 b =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(buf + n * SROW + (s * 32 + 8 * g) * 2));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st][u], b, acc, 0, 0, 0);
+      }
+    }
+    if (kst == spb - 1) {  // block done: add the 4 waves' partial sums
+      *reinterpret_cast<floatx4*>(red + (wave * 64 + lane) * 4) = acc;
+      lds_barrier();
+      if (wave == 0) {
+        floatx4 sum = acc;
+#pragma unroll
+        for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const floatx4*>(red + (w * 64 + lane) * 4);
+        const int j = (blockIdx.x + (t / spb) * gridDim.x) * 16 + n;
+        if (j < Vd) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 4 * g + i;
+            if (m < M) C[(size_t)m * Vd + j] = sum[i];
+          }
+        }
+      }
+      acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 // ------------------------------------------------------------------ tiled
@@ -208,7 +310,11 @@ __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, 
 hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, float* logits, int M, int H,
                                int Vd, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  if (M <= 64) {
+  if (M <= 16 && H % 512 == 0 && H <= 4096) {
+    const int nblocks = (Vd + 15) / 16;
+    const int grid = min(cu_count(), nblocks);
+    hipLaunchKernelGGL(k1_stream, dim3(grid), dim3(256), SLDS, stream, hidden, lm_head, logits, M, H, Vd);
+  } else if (M <= 64) {
     constexpr int FR = 2;
     const int waves = (Vd + 16 * FR - 1) / (16 * FR);
     const dim3 grid((waves + 3) / 4), block(256);

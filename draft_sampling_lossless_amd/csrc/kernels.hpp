@@ -20,13 +20,30 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
                                int Vd, hipStream_t stream);
 
 // ---- stage 2
+// Few requests: one cooperative launch (markov_few.hip).
+struct FewPlan {
+  bool use;            // B <= 16 and the per-workgroup W2 slice fits in LDS
+  int grid, ch;        // workgroups (at most one per CU), 64-wide vocabulary chunks per workgroup
+  int cap;             // survivors per step whose weight rows phase C can hold in LDS
+  size_t lds;          // dynamic LDS bytes
+  int gmax;            // workgroup count the workspace layout is sized for
+  size_t off_norms, off_n1, off_rec, off_fstep, off_partF, off_partD, off_rows, off_ctr, bytes;
+};
+FewPlan plan_markov_few(int B, int N, int Vd, int r, int cus);
+hipError_t launch_markov_few(const FewPlan& p, float* logits, const uint16_t* w1, const uint16_t* w2,
+                             const int64_t* d2t, const int32_t* anchor, const float* temperature,
+                             const uint32_t* request_id, uint64_t seed, int32_t* draft_tokens, float* log_z, int B,
+                             int N, int V, int Vd, int r, void* workspace, hipStream_t stream);
+
 struct MarkovPlan {
-  int chunks_per_wg;   // 64-wide vocabulary chunks per workgroup
+  int chunks_per_wg;   // 64-wide vocabulary chunks per workgroup (per-step path)
   int vslices;         // vocabulary slices (workgroups along the vocabulary)
   int btiles;          // 64-request tiles
-  size_t partial_bytes;
+  size_t partial_bytes;  // workspace bytes (the larger need of the two paths)
+  FewPlan few;
 };
-MarkovPlan plan_markov(int B, int N, int Vd, int r);
+// cus: compute units of the device (0: upper bound for workspace sizing, no HIP calls)
+MarkovPlan plan_markov(int B, int N, int Vd, int r, int cus);
 hipError_t launch_markov_sample(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
                                 const int32_t* anchor, const float* temperature, const uint32_t* request_id,
                                 uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,

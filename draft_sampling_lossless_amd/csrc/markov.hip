@@ -21,36 +21,30 @@
 //   markov_merge  one wave per request reduces the slice partials, writes the
 //                 token and log Z.  The next step's kernel reads that token.
 //
+//   markov_small  few requests (B <= 16): the per-step work is small and the two
+//                 launches per step are latency.  One cooperative workgroup per CU
+//                 owns a fixed vocabulary slice for all N steps and keeps that
+//                 slice of W2 in LDS; a grid barrier separates the steps, and every
+//                 workgroup reduces the previous step's partials itself to learn the
+//                 sampled tokens (workgroup 0 also writes them out).  The next step's
+//                 base logits are loaded before the barrier.
+//
 // Workgroup order is XCD-aware: the workgroups of one vocabulary slice (one per
 // request tile) go to the same XCD one after another, so the slice of W2 they
 // all read is fetched from HBM once and then served by that XCD's L2.
 #include <math.h>
 
+#include <algorithm>
+
 #include "device.hpp"
 #include "kernels.hpp"
+#include "markov_common.hpp"
 
 namespace dspark {
 
 namespace {
 
-constexpr int kReqPerWave = 16;
-constexpr int kReqPerWG = 64;
-constexpr int kChunk = 64;       // vocabulary entries per MFMA chunk
-constexpr int kMaxKSteps = 8;    // r <= 256 in steps of 32
-
-struct MarkovPartial {
-  float key;   // best Gumbel key (base-2 units; T == 0: the logit)
-  int tok;     // its target id
-  float m, s;  // log-sum-exp state: log2 sum 2^y = m + log2 s, y = l * log2(e) / T (T == 0: y = l)
-};
-
-__device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
-
-__device__ __forceinline__ void wg_coords(int CH, int nvs, int nbt, int& vs, int& bt) {
-  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-  vs = (local / nbt) * 8 + xcd;
-  bt = local % nbt;
-}
+using namespace mk;
 
 __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, const uint16_t* __restrict__ w1,
                                                    const uint16_t* __restrict__ w2, const int64_t* __restrict__ d2t,
@@ -265,10 +259,9 @@ __global__ void inverse_scatter(const int64_t* __restrict__ d2t, int Vd, int V, 
 
 }  // namespace
 
-MarkovPlan plan_markov(int B, int N, int Vd, int r) {
-  (void)N;
-  (void)r;
+MarkovPlan plan_markov(int B, int N, int Vd, int r, int cus) {
   MarkovPlan p{};
+  p.few = plan_markov_few(B, N, Vd, r, cus);
   p.btiles = (B + kReqPerWG - 1) / kReqPerWG;
   const int chunks = (Vd + kChunk - 1) / kChunk;
   int ch = 16;
@@ -276,6 +269,8 @@ MarkovPlan plan_markov(int B, int N, int Vd, int r) {
   p.chunks_per_wg = ch;
   p.vslices = (chunks + ch - 1) / ch;
   p.partial_bytes = (size_t)B * p.vslices * sizeof(MarkovPartial);
+  // the query (cus == 0) must cover whichever path a launch picks
+  if (p.few.bytes > p.partial_bytes) p.partial_bytes = p.few.bytes;
   return p;
 }
 
@@ -283,7 +278,10 @@ hipError_t launch_markov_sample(float* logits, const uint16_t* w1, const uint16_
                                 const int32_t* anchor, const float* temperature, const uint32_t* request_id,
                                 uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,
                                 int r, void* workspace, hipStream_t stream) {
-  const MarkovPlan p = plan_markov(B, N, Vd, r);
+  const MarkovPlan p = plan_markov(B, N, Vd, r, cu_count_markov());
+  if (p.few.use)
+    return launch_markov_few(p.few, logits, w1, w2, d2t, anchor, temperature, request_id, seed, draft_tokens, log_z,
+                             B, N, V, Vd, r, workspace, stream);
   MarkovPartial* partial = static_cast<MarkovPartial*>(workspace);
   const int nvs8 = (p.vslices + 7) / 8 * 8;
   const dim3 grid(nvs8 * p.btiles), block(256);

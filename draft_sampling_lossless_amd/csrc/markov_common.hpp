@@ -1,0 +1,267 @@
+// Pieces shared by the two implementations of the Markov loop (markov.hip: one
+// launch per step for many requests; markov_few.hip: one cooperative launch for
+// few requests).
+#pragma once
+
+#include <math.h>
+
+#include "device.hpp"
+
+namespace dspark {
+namespace mk {
+
+constexpr int kReqPerWave = 16;
+constexpr int kReqPerWG = 64;
+constexpr int kChunk = 64;       // vocabulary entries per MFMA chunk
+constexpr int kMaxKSteps = 8;    // r <= 256 in steps of 32
+
+struct MarkovPartial {
+  float key;   // best Gumbel key (base-2 units; T == 0: the logit)
+  int tok;     // its target id
+  float m, s;  // log-sum-exp state: log2 sum 2^y = m + log2 s, y = l * log2(e) / T (T == 0: y = l)
+};
+
+inline int cu_count_markov() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+__device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+
+__device__ __forceinline__ void wg_coords(int CH, int nvs, int nbt, int& vs, int& bt) {
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  vs = (local / nbt) * 8 + xcd;
+  bt = local % nbt;
+}
+
+// ---- cross-lane moves without the LDS crossbar
+// A butterfly over a 64-lane wave: four DPP moves inside each 16-lane row (swap
+// neighbours, swap pairs, mirror within 8, mirror within 16), then the gfx950
+// permlane swaps, which hand every lane the value of the same lane in the other
+// row of its row pair (16) and in the other half of the wave (32).  After a stage
+// both partners hold the merge of their two inputs (up to the rounding order of
+// a floating-point merge), so every lane of the group ends with the group's result.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0u, v, kCtrl, 0xF, 0xF, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(v)));
+}
+constexpr int kDppSwap1 = 0xB1, kDppSwap2 = 0x4E, kDppMirror8 = 0x141, kDppMirror16 = 0x140;
+
+// {value in the even row, value in the odd row} of this lane's row pair
+__device__ __forceinline__ void rows_pair(uint32_t v, uint32_t& even, uint32_t& odd) {
+  const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  even = s[0];
+  odd = s[1];
+}
+// {value in the lower half, value in the upper half} of the wave
+__device__ __forceinline__ void halves_pair(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  lo = s[0];
+  hi = s[1];
+}
+
+// sum over aligned groups of `width` lanes (1, 2, 4, ..., 64; uniform)
+__device__ __forceinline__ float group_sum(float v, int width) {
+  if (width >= 2) v += dpp_f32<kDppSwap1>(v);
+  if (width >= 4) v += dpp_f32<kDppSwap2>(v);
+  if (width >= 8) v += dpp_f32<kDppMirror8>(v);
+  if (width >= 16) v += dpp_f32<kDppMirror16>(v);
+  if (width >= 32) {
+    uint32_t a, b;
+    rows_pair(__float_as_uint(v), a, b);
+    v = __uint_as_float(a) + __uint_as_float(b);
+  }
+  if (width >= 64) {
+    uint32_t a, b;
+    halves_pair(__float_as_uint(v), a, b);
+    v = __uint_as_float(a) + __uint_as_float(b);
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<kDppSwap1>(v));
+  v = fmaxf(v, dpp_f32<kDppSwap2>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror8>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror16>(v));
+  uint32_t a, b;
+  rows_pair(__float_as_uint(v), a, b);
+  v = fmaxf(__uint_as_float(a), __uint_as_float(b));
+  halves_pair(__float_as_uint(v), a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppSwap1>(v));
+  v = max(v, dpp_u32<kDppSwap2>(v));
+  v = max(v, dpp_u32<kDppMirror8>(v));
+  v = max(v, dpp_u32<kDppMirror16>(v));
+  uint32_t a, b;
+  rows_pair(v, a, b);
+  v = max(a, b);
+  halves_pair(v, a, b);
+  return max(a, b);
+}
+
+// argmax (key desc, id asc) and log-sum-exp merges of a (key, tok, m, s) state
+__device__ __forceinline__ void state_merge(float& key, int& tok, float& m, float& s, float k2, int t2, float m2,
+                                            float s2) {
+  if (key_beats(k2, t2, key, tok)) {
+    key = k2;
+    tok = t2;
+  }
+  lse2_merge(m, s, m2, s2);
+}
+template <int kCtrl>
+__device__ __forceinline__ void state_stage(float& key, int& tok, float& m, float& s) {
+  state_merge(key, tok, m, s, dpp_f32<kCtrl>(key), (int)dpp_u32<kCtrl>((uint32_t)tok), dpp_f32<kCtrl>(m),
+              dpp_f32<kCtrl>(s));
+}
+// merge over each 16-lane row
+__device__ __forceinline__ void row_state_merge(float& key, int& tok, float& m, float& s) {
+  state_stage<kDppSwap1>(key, tok, m, s);
+  state_stage<kDppSwap2>(key, tok, m, s);
+  state_stage<kDppMirror8>(key, tok, m, s);
+  state_stage<kDppMirror16>(key, tok, m, s);
+}
+// merge over the wave (every lane ends with the same state)
+__device__ __forceinline__ void wave_state_merge(float& key, int& tok, float& m, float& s) {
+  row_state_merge(key, tok, m, s);
+  uint32_t k0, k1, t0, t1, m0, m1, s0, s1;
+  rows_pair(__float_as_uint(key), k0, k1);
+  rows_pair((uint32_t)tok, t0, t1);
+  rows_pair(__float_as_uint(m), m0, m1);
+  rows_pair(__float_as_uint(s), s0, s1);
+  key = __uint_as_float(k0);
+  tok = (int)t0;
+  m = __uint_as_float(m0);
+  s = __uint_as_float(s0);
+  state_merge(key, tok, m, s, __uint_as_float(k1), (int)t1, __uint_as_float(m1), __uint_as_float(s1));
+  halves_pair(__float_as_uint(key), k0, k1);
+  halves_pair((uint32_t)tok, t0, t1);
+  halves_pair(__float_as_uint(m), m0, m1);
+  halves_pair(__float_as_uint(s), s0, s1);
+  key = __uint_as_float(k0);
+  tok = (int)t0;
+  m = __uint_as_float(m0);
+  s = __uint_as_float(s0);
+  state_merge(key, tok, m, s, __uint_as_float(k1), (int)t1, __uint_as_float(m1), __uint_as_float(s1));
+}
+
+template <int kCtrl>
+__device__ __forceinline__ void argmax_stage(float& key, int& tok) {
+  const float k2 = dpp_f32<kCtrl>(key);
+  const int t2 = (int)dpp_u32<kCtrl>((uint32_t)tok);
+  if (key_beats(k2, t2, key, tok)) {
+    key = k2;
+    tok = t2;
+  }
+}
+// argmax (key desc, id asc) over each 16-lane row
+__device__ __forceinline__ void row_argmax(float& key, int& tok) {
+  argmax_stage<kDppSwap1>(key, tok);
+  argmax_stage<kDppSwap2>(key, tok);
+  argmax_stage<kDppMirror8>(key, tok);
+  argmax_stage<kDppMirror16>(key, tok);
+}
+// argmax (key desc, id asc) over the wave
+__device__ __forceinline__ void wave_argmax(float& key, int& tok) {
+  row_argmax(key, tok);
+  uint32_t k0, k1, t0, t1;
+  rows_pair(__float_as_uint(key), k0, k1);
+  rows_pair((uint32_t)tok, t0, t1);
+  key = __uint_as_float(k0);
+  tok = (int)t0;
+  if (key_beats(__uint_as_float(k1), (int)t1, key, tok)) {
+    key = __uint_as_float(k1);
+    tok = (int)t1;
+  }
+  halves_pair(__float_as_uint(key), k0, k1);
+  halves_pair((uint32_t)tok, t0, t1);
+  key = __uint_as_float(k0);
+  tok = (int)t0;
+  if (key_beats(__uint_as_float(k1), (int)t1, key, tok)) {
+    key = __uint_as_float(k1);
+    tok = (int)t1;
+  }
+}
+template <int kCtrl>
+__device__ __forceinline__ void lse_stage(float& m, float& s) {
+  lse2_merge(m, s, dpp_f32<kCtrl>(m), dpp_f32<kCtrl>(s));
+}
+// log-sum-exp merge over each 16-lane row
+__device__ __forceinline__ void row_lse_merge(float& m, float& s) {
+  lse_stage<kDppSwap1>(m, s);
+  lse_stage<kDppSwap2>(m, s);
+  lse_stage<kDppMirror8>(m, s);
+  lse_stage<kDppMirror16>(m, s);
+}
+
+// Cross-workgroup traffic of the persistent kernel goes through device-scope
+// atomic stores and loads: on this chip they bypass the per-XCD L2 caches, so the
+// barrier needs no L2 write-back / invalidate (which would cost far more than the
+// few partials exchanged per step).
+__device__ __forceinline__ void store_partial(MarkovPartial* p, const MarkovPartial& v) {
+  __hip_atomic_store(&p->key, v.key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&p->tok, v.tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&p->m, v.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&p->s, v.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ MarkovPartial load_partial(const MarkovPartial* p) {
+  MarkovPartial v;
+  v.key = __hip_atomic_load(&p->key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.tok = __hip_atomic_load(&p->tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.m = __hip_atomic_load(&p->m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  v.s = __hip_atomic_load(&p->s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+
+// Grid barrier of the cooperative launch (every workgroup is resident).  The
+// __syncthreads() before it completes this workgroup's partial stores; one thread
+// arrives on a monotonic counter and waits until all G workgroups of this round
+// have.  The wait is bounded (about 0.1 s) so that a broken launch can never hang
+// the device; the co-residency of a cooperative launch makes it unreachable.
+__device__ __forceinline__ void grid_barrier(unsigned* ctr, unsigned target) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+
+// Merge every workgroup's partial of request b (one wave; all lanes get the result).
+__device__ __forceinline__ MarkovPartial wave_merge(const MarkovPartial* __restrict__ part, int count, int lane) {
+  float key = -INFINITY, m = -INFINITY, s = 0.0f;
+  int tok = 0x7FFFFFFF;
+  for (int p = lane; p < count; p += 64) {
+    const MarkovPartial q = load_partial(part + p);
+    state_merge(key, tok, m, s, q.key, q.tok, q.m, q.s);
+  }
+  wave_state_merge(key, tok, m, s);
+  return MarkovPartial{key, tok, m, s};
+}
+
+__device__ __forceinline__ float log_z_of(const MarkovPartial& q, float T) {
+  return (T > 0.0f) ? (q.m + log2f(q.s)) * 0.69314718055994531f : q.m;
+}
+
+
+}  // namespace mk
+}  // namespace dspark

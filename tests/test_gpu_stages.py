@@ -50,7 +50,9 @@ def test_race_exponentials_bit_exact(n, pos, req, tag):
 # ---------------------------------------------------------------- stage 1
 
 @pytest.mark.parametrize("M,H,Vd", [(8, 256, 1024), (20, 264, 1000), (40, 256, 996), (1, 4096, 4096),
-                                    (300, 200, 1004), (129, 4096, 640), (64, 64, 68)])
+                                    (300, 200, 1004), (129, 4096, 640), (64, 64, 68),
+                                    (8, 4096, 4100), (16, 512, 1000), (13, 1024, 72), (1, 2048, 65540),
+                                    (8, 4096, 8)])
 def test_draft_logits_small(M, H, Vd):
     say(f"draft_logits M={M} H={H} Vd={Vd}")
     g = np.random.default_rng(M * 7 + H)
@@ -82,12 +84,12 @@ def test_draft_logits_full_size_sampled(name):
 
 # ---------------------------------------------------------------- stage 2
 
-def _markov_case(B, N, V, Vd, r, temps, seed=0, base=None, d2t=None):
+def _markov_case(B, N, V, Vd, r, temps, seed=0, base=None, d2t=None, wstd=0.16):
     g = np.random.default_rng(B * 1000 + N * 10 + r)
     if base is None:
         base = (g.normal(0, 1.28, size=(B, N, Vd))).astype(np.float32)
-    w1 = synth.bf16_bits(g.normal(0, 0.02 * 8, size=(V, r)).astype(np.float32))
-    w2 = synth.bf16_bits(g.normal(0, 0.02 * 8, size=(Vd, r)).astype(np.float32))
+    w1 = synth.bf16_bits(g.normal(0, wstd, size=(V, r)).astype(np.float32))
+    w2 = synth.bf16_bits(g.normal(0, wstd, size=(Vd, r)).astype(np.float32))
     anchor = g.integers(0, V, size=B).astype(np.int32)
     temp = np.asarray(temps, np.float32)[g.integers(0, len(temps), size=B)]
     rid = (np.arange(B) * 7 + 3).astype(np.uint32)
@@ -109,6 +111,10 @@ def _run_markov_gpu(c):
     (33, 4, 4096, 1000, 32, (0.0, 0.7, 1.0), True),
     (20, 3, 3000, 3000, 256, (0.7,), False),
     (130, 2, 1024, 1024, 8, (1.0,), False),
+    (16, 6, 2048, 2048, 64, (0.0, 0.7, 1.0), False),
+    (5, 4, 4096, 1000, 64, (0.0, 1.0), True),
+    (3, 3, 3000, 3000, 256, (0.7,), False),
+    (2, 64, 1024, 1024, 16, (1.0,), False),
 ])
 def test_markov_small(B, N, V, Vd, r, temps, reduced):
     say(f"markov B={B} N={N} V={V} Vd={Vd} r={r} T={temps} reduced={reduced}")
@@ -124,6 +130,72 @@ def test_markov_small(B, N, V, Vd, r, temps, reduced):
     if d2t is not None:
         image = set((np.arange(Vd) + d2t).tolist())
         assert all(int(t) in image for t in tok.ravel())
+
+
+@pytest.mark.parametrize("B,N,V,Vd,r,temps,wstd", [
+    (1, 8, 8192, 8192, 64, (1.0,), 0.02),       # few survivors: chain on rows staged in LDS
+    (4, 5, 2048, 2048, 64, (0.7, 1.0), 0.15),    # wider margin, mixed temperatures
+    (3, 4, 4096, 4096, 64, (0.0, 1.0), 1.0),     # margin too wide for the recorded entries: per-step pass
+    (2, 6, 4096, 1000, 32, (1.0,), 1.0),         # the same with a reduced vocabulary
+    (1, 20, 151936, 151936, 64, (1.0,), 0.02),   # recorded entries in several rounds; two 16-step tiles
+])
+def test_markov_candidate_paths(B, N, V, Vd, r, temps, wstd):
+    say(f"markov candidate paths B={B} N={N} V={V} Vd={Vd} r={r} std={wstd}")
+    d2t = None
+    if Vd != V:
+        g = np.random.default_rng(7)
+        d2t = (g.permutation(V)[:Vd] - np.arange(Vd)).astype(np.int64)
+    c = _markov_case(B, N, V, Vd, r, temps, seed=0x777, d2t=d2t, wstd=wstd)
+    tok, proc, logz = _run_markov_gpu(c)
+    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], d2t, c["anchor"], c["temp"], c["rid"], c["seed"])
+    checked, near = compare_markov(tok, proc, logz, ref)
+    say(f"  compared {checked} positions, {near} near-tie mismatches")
+
+
+def test_markov_unstaged_chain():
+    # one large base logit per 256-entry workgroup slice, the rest far below: every
+    # slice's best entry survives the margin while its second one stays outside, so
+    # the survivors (about 256 per step) exceed what fits in LDS and the chain reads
+    # weight rows from global memory
+    B, N, V, Vd, r = 1, 4, 65536, 65536, 64
+    g = np.random.default_rng(11)
+    base = np.full((B, N, Vd), -60.0, np.float32)
+    pick = np.arange(0, Vd, 256) + g.integers(0, 256, size=Vd // 256)
+    base[:, :, pick] = g.normal(0, 0.3, size=(B, N, pick.size)).astype(np.float32)
+    say(f"markov unstaged chain B={B} N={N} V={V} r={r}")
+    c = _markov_case(B, N, V, Vd, r, (1.0,), seed=0x99, base=base, wstd=0.33)
+    tok, proc, logz = _run_markov_gpu(c)
+    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], None, c["anchor"], c["temp"], c["rid"], c["seed"])
+    checked, near = compare_markov(tok, proc, logz, ref)
+    say(f"  compared {checked} positions, {near} near-tie mismatches")
+    assert set(tok.ravel().tolist()) <= set(pick.tolist())
+
+
+@pytest.mark.parametrize("B,N,V,Vd,r,temps,wstd", [
+    (2, 5, 8192, 8192, 64, (1.0,), 0.02),   # survivors: the staged chain
+    (3, 4, 4096, 4096, 64, (0.0, 1.0), 1.0),  # the per-step pass
+])
+def test_markov_few_solo(B, N, V, Vd, r, temps, wstd, monkeypatch):
+    # the few-request kernel with every slice run by one workgroup (what it does when
+    # not all of its workgroups become resident): same results as the oracle
+    monkeypatch.setenv("DSPARK_MARKOV_SOLO", "1")
+    say(f"markov few solo B={B} N={N} V={V} r={r} std={wstd}")
+    c = _markov_case(B, N, V, Vd, r, temps, seed=0x51, wstd=wstd)
+    tok, proc, logz = _run_markov_gpu(c)
+    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], None, c["anchor"], c["temp"], c["rid"], c["seed"])
+    checked, near = compare_markov(tok, proc, logz, ref)
+    say(f"  compared {checked} positions, {near} near-tie mismatches")
+
+
+def test_markov_deterministic():
+    # same inputs twice (few requests: the cooperative kernel; many: the per-step kernels)
+    for B in (1, 40):
+        c = _markov_case(B, 6, 2048, 2048, 64, (0.0, 1.0), seed=3)
+        a = _run_markov_gpu(c)
+        b = _run_markov_gpu(c)
+        for x, y in zip(a, b):
+            assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                                  y.view(np.uint32) if y.dtype == np.float32 else y)
 
 
 @pytest.mark.parametrize("name,nsample", [("qwen3_8b_single", 1), ("batched", 4), ("admission", 3),
