@@ -47,7 +47,7 @@ _SIGS = {
                              + [_c_void_p, _c_size, _c_void_p]),
     "dspark_build_inverse_map": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_void_p]),
     "dspark_verify_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
-    "dspark_verify": (_c_int, [_c_int] + [_c_void_p] * 8 + [_c_u64, _c_void_p, _c_void_p] + [_c_int] * 4
+    "dspark_verify": (_c_int, [_c_int] + [_c_void_p] * 8 + [_c_u64, _c_void_p, _c_void_p, _c_void_p] + [_c_int] * 4
                       + [_c_void_p, _c_size, _c_void_p]),
     "dspark_admit": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
 }
@@ -207,8 +207,10 @@ def verify(input_kind: int, target: torch.Tensor, draft: torch.Tensor, draft_log
            draft_tokens: torch.Tensor, inv_map: Optional[torch.Tensor], verify_len: Optional[torch.Tensor],
            temperature: Optional[torch.Tensor], request_id: torch.Tensor, seed: int,
            accepted: Optional[torch.Tensor] = None, out_tokens: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Stage 3.  target [B, N+1, V], draft [B, N, Vd].  Returns (accepted [B], out_tokens [B, N+1])."""
+           workspace: Optional[torch.Tensor] = None, accept_prob: Optional[torch.Tensor] = None,
+           with_accept_prob: bool = False):
+    """Stage 3.  target [B, N+1, V], draft [B, N, Vd].  Returns (accepted [B], out_tokens [B, N+1]),
+    plus accept_prob [B, N] (NaN past verify_len) when it is passed or with_accept_prob is set."""
     B, N, Vd = draft.shape
     V = target.shape[2]
     dev = target.device
@@ -216,6 +218,8 @@ def verify(input_kind: int, target: torch.Tensor, draft: torch.Tensor, draft_log
         accepted = torch.empty(B, dtype=torch.int32, device=dev)
     if out_tokens is None:
         out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+    if accept_prob is None and with_accept_prob:
+        accept_prob = torch.empty((B, N), dtype=torch.float32, device=dev)
     ws = _workspace(workspace, verify_workspace_size(B, N, V), dev)
     _check("dspark_verify", load().dspark_verify(
         input_kind, _ptr(target, "target", _F32, dev, (B, N + 1, V)), _ptr(draft, "draft", _F32, dev),
@@ -224,7 +228,10 @@ def verify(input_kind: int, target: torch.Tensor, draft: torch.Tensor, draft_log
         _ptr(verify_len, "verify_len", _I32, dev, (B,)), _ptr(temperature, "temperature", _F32, dev, (B,)),
         _ptr(request_id, "request_id", _U32, dev, (B,)), seed,
         _ptr(accepted, "accepted", _I32, dev, (B,)), _ptr(out_tokens, "out_tokens", _I32, dev, (B, N + 1)),
+        _ptr(accept_prob, "accept_prob", _F32, dev, (B, N)),
         B, N, V, Vd, ws.data_ptr(), ws.numel(), _stream(target)))
+    if accept_prob is not None:
+        return accepted, out_tokens, accept_prob
     return accepted, out_tokens
 
 

@@ -143,7 +143,7 @@ size_t dspark_verify_workspace_size(int B, int N, int V) {
 dspark_status dspark_verify(int input_kind, const float* target, const float* draft, const float* draft_log_z,
                             const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
                             const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
-                            int32_t* out_tokens, int B, int N, int V, int Vd, void* workspace,
+                            int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
                             size_t workspace_bytes, void* stream) {
   REQUIRE(input_kind == DSPARK_INPUT_LOGITS || input_kind == DSPARK_INPUT_PROBS, DSPARK_ERR_INVALID,
           "input_kind must be DSPARK_INPUT_LOGITS or DSPARK_INPUT_PROBS (got %d)", input_kind);
@@ -172,8 +172,8 @@ dspark_status dspark_verify(int input_kind, const float* target, const float* dr
   REQUIRE(workspace_bytes >= need, DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
           need);
   return hip_status(dspark::launch_verify(input_kind, target, draft, draft_log_z, draft_tokens, inv_map, verify_len,
-                                          temperature, request_id, seed, accepted, out_tokens, B, N, V, Vd,
-                                          workspace, (hipStream_t)stream),
+                                          temperature, request_id, seed, accepted, out_tokens, accept_prob, B, N,
+                                          V, Vd, workspace, (hipStream_t)stream),
                     "verify");
 }
 

@@ -41,79 +41,6 @@ __device__ __forceinline__ void wg_coords(int CH, int nvs, int nbt, int& vs, int
   bt = local % nbt;
 }
 
-// ---- cross-lane moves without the LDS crossbar
-// A butterfly over a 64-lane wave: four DPP moves inside each 16-lane row (swap
-// neighbours, swap pairs, mirror within 8, mirror within 16), then the gfx950
-// permlane swaps, which hand every lane the value of the same lane in the other
-// row of its row pair (16) and in the other half of the wave (32).  After a stage
-// both partners hold the merge of their two inputs (up to the rounding order of
-// a floating-point merge), so every lane of the group ends with the group's result.
-template <int kCtrl>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0u, v, kCtrl, 0xF, 0xF, false);
-}
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(v)));
-}
-constexpr int kDppSwap1 = 0xB1, kDppSwap2 = 0x4E, kDppMirror8 = 0x141, kDppMirror16 = 0x140;
-
-// {value in the even row, value in the odd row} of this lane's row pair
-__device__ __forceinline__ void rows_pair(uint32_t v, uint32_t& even, uint32_t& odd) {
-  const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  even = s[0];
-  odd = s[1];
-}
-// {value in the lower half, value in the upper half} of the wave
-__device__ __forceinline__ void halves_pair(uint32_t v, uint32_t& lo, uint32_t& hi) {
-  const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  lo = s[0];
-  hi = s[1];
-}
-
-// sum over aligned groups of `width` lanes (1, 2, 4, ..., 64; uniform)
-__device__ __forceinline__ float group_sum(float v, int width) {
-  if (width >= 2) v += dpp_f32<kDppSwap1>(v);
-  if (width >= 4) v += dpp_f32<kDppSwap2>(v);
-  if (width >= 8) v += dpp_f32<kDppMirror8>(v);
-  if (width >= 16) v += dpp_f32<kDppMirror16>(v);
-  if (width >= 32) {
-    uint32_t a, b;
-    rows_pair(__float_as_uint(v), a, b);
-    v = __uint_as_float(a) + __uint_as_float(b);
-  }
-  if (width >= 64) {
-    uint32_t a, b;
-    halves_pair(__float_as_uint(v), a, b);
-    v = __uint_as_float(a) + __uint_as_float(b);
-  }
-  return v;
-}
-
-__device__ __forceinline__ float wave_max_f32(float v) {
-  v = fmaxf(v, dpp_f32<kDppSwap1>(v));
-  v = fmaxf(v, dpp_f32<kDppSwap2>(v));
-  v = fmaxf(v, dpp_f32<kDppMirror8>(v));
-  v = fmaxf(v, dpp_f32<kDppMirror16>(v));
-  uint32_t a, b;
-  rows_pair(__float_as_uint(v), a, b);
-  v = fmaxf(__uint_as_float(a), __uint_as_float(b));
-  halves_pair(__float_as_uint(v), a, b);
-  return fmaxf(__uint_as_float(a), __uint_as_float(b));
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<kDppSwap1>(v));
-  v = max(v, dpp_u32<kDppSwap2>(v));
-  v = max(v, dpp_u32<kDppMirror8>(v));
-  v = max(v, dpp_u32<kDppMirror16>(v));
-  uint32_t a, b;
-  rows_pair(v, a, b);
-  v = max(a, b);
-  halves_pair(v, a, b);
-  return max(a, b);
-}
-
 // argmax (key desc, id asc) and log-sum-exp merges of a (key, tok, m, s) state
 __device__ __forceinline__ void state_merge(float& key, int& tok, float& m, float& s, float k2, int t2, float m2,
                                             float s2) {

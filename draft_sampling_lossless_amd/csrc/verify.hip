@@ -4,20 +4,25 @@
 // u_k * p_d(x_k) < p_t(x_k) (double products of float32 values: exact), stop at
 // the first rejection k and resample from max(0, p_t - p_d) there, or, with all
 // L accepted, draw a bonus token from target row L.  Both draws are exponential
-// races: argmax_v r_v / E_v with E_v = -plog2(u_v), compared exactly.
+// races: argmax_v r_v / E_v with E_v = -plog2(u_v), compared exactly.  On request
+// the per-position acceptance probability alpha_k = sum_v min(p_t, p_d) is also
+// produced for k < L.
 //
-// Kernels (one pass each, grid-wide where a row is long):
+// Kernels:
 //   rowstats   logits mode only.  Row statistics of target rows k <= L: base-2
 //              log-sum-exp of l / T (T > 0) or the argmax (T == 0), per
 //              (row, chunk) partial.
-//   accept     one wave per request: merges the row partials, runs the sequential
-//              acceptance test (one element per row of each side), writes the
-//              accepted prefix and a sampling job (row, residual or bonus).
-//   sample     (request, chunk) workgroups stream the job row(s): target row, and
-//              for a residual the draft row (gathered through the inverse map);
-//              per-chunk race winner for the residual and for its fallback
-//              (p_t itself, used only if the residual is zero everywhere).
-//   finalize   one wave per request reduces the race partials and writes y.
+//   accept     one workgroup per request: merges every row's partials at once,
+//              tests all L positions in parallel (one lane each) and takes the
+//              first rejection; writes the accepted prefix, the merged row
+//              statistics and a sampling job.
+//   sample     (request, row, chunk) workgroups stream the job row: the target
+//              row and, for a residual, the draft row gathered through the inverse
+//              map; per-chunk race winners for the residual and for its fallback
+//              (p_t itself, used only if the residual is zero everywhere).  With
+//              alpha requested, rows k < L are streamed too for their partial sums.
+//              The last workgroup of a request (a ticket counter the accept kernel
+//              cleared) merges the partials and writes y and alpha.
 #include <math.h>
 
 #include "dspark.h"
@@ -40,8 +45,11 @@ enum { kJobDone = 0, kJobResid = 1, kJobBonus = 2 };
 
 struct Job {
   int mode;       // kJobDone / kJobResid / kJobBonus
-  int row;        // position k of the sampling row
-  float m, invs;  // target row statistics (logits mode): p_t = 2^(y - m) * invs
+  int row;        // position a of the sampling row
+  int L;          // verify length
+  int parts;      // sampling workgroups of the request (ticket target)
+  int hot;        // probabilities are not point masses (T > 0 or probability input)
+  int pad[3];
 };
 
 struct RacePartial {
@@ -54,6 +62,83 @@ struct RacePartial {
 
 __device__ __forceinline__ bool amax_beats(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ void stat_merge(float& m, float& s, float& av, int& ai, float m2, float s2, float av2,
+                                           int ai2) {
+  lse2_merge(m, s, m2, s2);
+  if (amax_beats(av2, ai2, av, ai)) {
+    av = av2;
+    ai = ai2;
+  }
+}
+
+template <int kCtrl>
+__device__ __forceinline__ void stat_stage(float& m, float& s, float& av, int& ai) {
+  stat_merge(m, s, av, ai, dpp_f32<kCtrl>(m), dpp_f32<kCtrl>(s), dpp_f32<kCtrl>(av), (int)dpp_u32<kCtrl>((uint32_t)ai));
+}
+
+// merge of (log-sum-exp, argmax) states over the wave (lane 0 holds the result)
+__device__ __forceinline__ void wave_stat_merge(float& m, float& s, float& av, int& ai) {
+  stat_stage<kDppSwap1>(m, s, av, ai);
+  stat_stage<kDppSwap2>(m, s, av, ai);
+  stat_stage<kDppMirror8>(m, s, av, ai);
+  stat_stage<kDppMirror16>(m, s, av, ai);
+  uint32_t a0, a1, b0, b1, c0, c1, d0, d1;
+  rows_pair(__float_as_uint(m), a0, a1);
+  rows_pair(__float_as_uint(s), b0, b1);
+  rows_pair(__float_as_uint(av), c0, c1);
+  rows_pair((uint32_t)ai, d0, d1);
+  m = __uint_as_float(a0);
+  s = __uint_as_float(b0);
+  av = __uint_as_float(c0);
+  ai = (int)d0;
+  stat_merge(m, s, av, ai, __uint_as_float(a1), __uint_as_float(b1), __uint_as_float(c1), (int)d1);
+  halves_pair(__float_as_uint(m), a0, a1);
+  halves_pair(__float_as_uint(s), b0, b1);
+  halves_pair(__float_as_uint(av), c0, c1);
+  halves_pair((uint32_t)ai, d0, d1);
+  m = __uint_as_float(a0);
+  s = __uint_as_float(b0);
+  av = __uint_as_float(c0);
+  ai = (int)d0;
+  stat_merge(m, s, av, ai, __uint_as_float(a1), __uint_as_float(b1), __uint_as_float(c1), (int)d1);
+}
+
+// The value as the compiler must materialise it: keeps a clamped, unconditional
+// load from being sunk under the branch that decides whether it is used (which
+// would serialise a batch of loads).
+__device__ __forceinline__ float opaque(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ void st_f(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ float ld_f(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_i(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ int ld_i(const int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+__device__ __forceinline__ void store_race(RacePartial* p, const RacePartial& v) {
+  st_f(&p->r, v.r);
+  st_f(&p->E, v.E);
+  st_i(&p->v, v.v);
+  st_f(&p->fr, v.fr);
+  st_f(&p->fE, v.fE);
+  st_i(&p->fv, v.fv);
+}
+__device__ __forceinline__ RacePartial load_race(const RacePartial* p) {
+  RacePartial v;
+  v.r = ld_f(&p->r);
+  v.E = ld_f(&p->E);
+  v.v = ld_i(&p->v);
+  v.fr = ld_f(&p->fr);
+  v.fE = ld_f(&p->fE);
+  v.fv = ld_i(&p->fv);
+  return v;
 }
 
 // ------------------------------------------------------------------ row statistics
@@ -96,50 +181,35 @@ __global__ __launch_bounds__(256) void verify_rowstats(const float* __restrict__
       m = mn;
     }
   }
-  // block reduction: waves, then LDS
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float om = __shfl_xor(m, off), os = __shfl_xor(s, off), ov = __shfl_xor(av, off);
-    const int oi = __shfl_xor(ai, off);
-    lse2_merge(m, s, om, os);
-    if (amax_beats(ov, oi, av, ai)) {
-      av = ov;
-      ai = oi;
-    }
-  }
+  wave_stat_merge(m, s, av, ai);
   __shared__ RowStat red[4];
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = RowStat{m, s, av, ai};
   __syncthreads();
   if (threadIdx.x == 0) {
     RowStat a = red[0];
-    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) {
-      lse2_merge(a.m, a.s, red[w].m, red[w].s);
-      if (amax_beats(red[w].amax, red[w].aidx, a.amax, a.aidx)) {
-        a.amax = red[w].amax;
-        a.aidx = red[w].aidx;
-      }
-    }
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) stat_merge(a.m, a.s, a.amax, a.aidx, red[w].m, red[w].s, red[w].amax, red[w].aidx);
     stats[(size_t)row * nchunks + c] = a;
   }
 }
 
 // ------------------------------------------------------------------ acceptance
 
-__global__ __launch_bounds__(64) void verify_accept(int input_kind, const float* __restrict__ target,
-                                                    const float* __restrict__ draft,
-                                                    const float* __restrict__ draft_log_z,
-                                                    const int32_t* __restrict__ draft_tokens,
-                                                    const int32_t* __restrict__ inv_map,
-                                                    const int32_t* __restrict__ verify_len,
-                                                    const float* __restrict__ temperature,
-                                                    const uint32_t* __restrict__ request_id, uint32_t key0,
-                                                    uint32_t key1, const RowStat* __restrict__ stats,
-                                                    Job* __restrict__ jobs, int32_t* __restrict__ accepted,
-                                                    int32_t* __restrict__ out_tokens, int B, int N, int V,
-                                                    int Vd, int nchunks) {
+__global__ __launch_bounds__(256) void verify_accept(int input_kind, const float* __restrict__ target,
+                                                     const float* __restrict__ draft,
+                                                     const float* __restrict__ draft_log_z,
+                                                     const int32_t* __restrict__ draft_tokens,
+                                                     const int32_t* __restrict__ inv_map,
+                                                     const int32_t* __restrict__ verify_len,
+                                                     const float* __restrict__ temperature,
+                                                     const uint32_t* __restrict__ request_id, uint32_t key0,
+                                                     uint32_t key1, const RowStat* __restrict__ stats,
+                                                     float2* __restrict__ rstat, Job* __restrict__ jobs,
+                                                     unsigned* __restrict__ tickets, int32_t* __restrict__ accepted,
+                                                     int32_t* __restrict__ out_tokens, float* __restrict__ accept_prob,
+                                                     int B, int N, int V, int Vd, int nchunks, int sample_chunks) {
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = verify_len ? min(max(verify_len[b], 0), N) : N;
   const uint32_t req = request_id[b];
   const bool probs = input_kind == DSPARK_INPUT_PROBS;
@@ -147,60 +217,64 @@ __global__ __launch_bounds__(64) void verify_accept(int input_kind, const float*
   const bool hot = probs || T > 0.0f;
   const float c2 = (!probs && hot) ? (1.0f / T) * kLog2e : 1.0f;
 
-  // Merged statistics of target rows k <= L (logits mode), kept in LDS.
+  // Merged statistics of target rows k <= L (logits mode): tpr threads per row
+  // each merge a strided share of the row's partials, then one thread per row.
   __shared__ float row_m[DSPARK_MAX_N + 1], row_s[DSPARK_MAX_N + 1];
   __shared__ int row_amax[DSPARK_MAX_N + 1];
+  __shared__ float pm[256], ps[256], pav[256];
+  __shared__ int pai[256];
+  __shared__ int s_a;
   if (!probs) {
-    for (int k = 0; k <= L; ++k) {
-      float m = -INFINITY, s = 0.0f, av = -INFINITY;
-      int ai = 0x7FFFFFFF;
+    const int rows = L + 1, tpr = 256 / rows;
+    const int k = tid / tpr, sub = tid - k * tpr;
+    float m = -INFINITY, s = 0.0f, av = -INFINITY;
+    int ai = 0x7FFFFFFF;
+    if (k < rows) {
       const RowStat* rp = stats + ((size_t)b * (N + 1) + k) * nchunks;
-      for (int c = lane; c < nchunks; c += 64) {
-        const RowStat q = rp[c];
-        lse2_merge(m, s, q.m, q.s);
-        if (amax_beats(q.amax, q.aidx, av, ai)) {
-          av = q.amax;
-          ai = q.aidx;
-        }
-      }
+      for (int c0 = sub; c0 < nchunks; c0 += 8 * tpr) {
+        RowStat q[8];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float om = __shfl_xor(m, off), os = __shfl_xor(s, off), ov = __shfl_xor(av, off);
-        const int oi = __shfl_xor(ai, off);
-        lse2_merge(m, s, om, os);
-        if (amax_beats(ov, oi, av, ai)) {
-          av = ov;
-          ai = oi;
-        }
-      }
-      if (lane == 0) {
-        row_m[k] = m;
-        row_s[k] = s;
-        row_amax[k] = ai;
+        for (int u = 0; u < 8; ++u) q[u] = rp[min(c0 + u * tpr, nchunks - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (c0 + u * tpr < nchunks)
+            stat_merge(m, s, av, ai, opaque(q[u].m), opaque(q[u].s), opaque(q[u].amax), opaque(q[u].aidx));
       }
     }
+    pm[tid] = m;
+    ps[tid] = s;
+    pav[tid] = av;
+    pai[tid] = ai;
+    __syncthreads();
+    if (tid < rows) {
+      float m2 = -INFINITY, s2 = 0.0f, av2 = -INFINITY;
+      int ai2 = 0x7FFFFFFF;
+      for (int t = tid * tpr; t < (tid + 1) * tpr; ++t) stat_merge(m2, s2, av2, ai2, pm[t], ps[t], pav[t], pai[t]);
+      row_m[tid] = m2;
+      row_s[tid] = s2;
+      row_amax[tid] = ai2;
+      rstat[(size_t)b * (N + 1) + tid] = make_float2(m2, 1.0f / s2);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
-  // Sequential acceptance test (every lane computes it; lane k supplies row k's stats).
-  int a = L;
-  for (int k = 0; k < L; ++k) {
-    const int x = draft_tokens[(size_t)b * N + k];
-    if (x < 0 || x >= V) {  // not a target id: reject without reading anything
-      a = k;
-      break;
-    }
-    const int j = inv_map ? inv_map[x] : x;
-    float pt, pd;
-    if (probs) {
-      pt = target[((size_t)b * (N + 1) + k) * V + x];
-      pd = (j >= 0) ? draft[((size_t)b * N + k) * Vd + j] : 0.0f;
-    } else {
-      const float m = row_m[k], s = row_s[k];
-      const int ai = row_amax[k];
-      if (hot) {
-        const float lt = target[((size_t)b * (N + 1) + k) * V + x];
-        pt = __builtin_amdgcn_exp2f(lt * c2 - m) / s;
+  // All L positions at once, one lane each; the first rejection decides.
+  if (wave == 0) {
+    bool rej = false;
+    float greedy_alpha = 0.0f;
+    if (lane < L) {
+      const int k = lane;
+      const int x = draft_tokens[(size_t)b * N + k];
+      const bool valid = x >= 0 && x < V;  // not a target id: rejected without reading anything
+      const int xs = valid ? x : 0;
+      const int j = inv_map ? inv_map[xs] : xs;
+      float pt, pd;
+      if (probs) {
+        pt = target[((size_t)b * (N + 1) + k) * V + xs];
+        pd = (j >= 0) ? draft[((size_t)b * N + k) * Vd + j] : 0.0f;
+      } else if (hot) {
+        const float lt = target[((size_t)b * (N + 1) + k) * V + xs];
+        pt = __builtin_amdgcn_exp2f(lt * c2 - row_m[k]) / row_s[k];
         if (j >= 0) {
           const float ld = draft[((size_t)b * N + k) * Vd + j];
           pd = __builtin_amdgcn_exp2f(ld * c2 - draft_log_z[(size_t)b * N + k] * kLog2e);
@@ -208,44 +282,53 @@ __global__ __launch_bounds__(64) void verify_accept(int input_kind, const float*
           pd = 0.0f;
         }
       } else {
-        pt = (x == ai) ? 1.0f : 0.0f;
+        pt = (x == row_amax[k]) ? 1.0f : 0.0f;
         pd = 1.0f;
+        greedy_alpha = pt;
       }
+      const u32x4 w = philox4x32_10(u32x4{0u, (uint32_t)k, req, kTagAccept}, key0, key1);
+      const float u = uniform01(w.x);
+      rej = !valid || !((double)u * (double)pd < (double)pt);
     }
-    const u32x4 w = philox4x32_10(u32x4{0u, (uint32_t)k, req, kTagAccept}, key0, key1);
-    const float u = uniform01(w.x);
-    if (!((double)u * (double)pd < (double)pt)) {
-      a = k;
-      break;
-    }
+    const uint64_t mask = __ballot(rej);
+    const int a = mask ? __builtin_ctzll(mask) : L;
+    if (lane == 0) s_a = a;
+    // greedy: alpha is 1 where the draft token is the target argmax (computed here)
+    if (accept_prob && !hot && lane < N)
+      accept_prob[(size_t)b * N + lane] = (lane < L) ? greedy_alpha : __builtin_nanf("");
   }
+  __syncthreads();
+  const int a = s_a;
 
   // Outputs: accepted prefix, -1 padding, the sampling job.
-  for (int k = lane; k <= N; k += 64) {
+  for (int k = tid; k <= N; k += 256) {
     int32_t o = -1;
     if (k < a) o = draft_tokens[(size_t)b * N + k];
     out_tokens[(size_t)b * (N + 1) + k] = o;
   }
-  if (lane == 0) accepted[b] = a;
-  const int row = a;  // residual row (a < L) or bonus row (a == L)
-  if (lane == 0) {
-    const float m = probs ? 0.0f : row_m[row], s = probs ? 1.0f : row_s[row];
-    const int ai = probs ? 0 : row_amax[row];
+  if (tid == 0) {
+    accepted[b] = a;
     Job jb;
-    jb.row = row;
+    jb.row = a;
+    jb.L = L;
+    jb.hot = hot ? 1 : 0;
     jb.mode = (a < L) ? kJobResid : kJobBonus;
-    jb.m = m;
-    jb.invs = probs ? 1.0f : 1.0f / s;
-    if (!probs && !hot) {
+    if (!hot) {
       // greedy: the residual and the bonus are both the point mass on the argmax
-      out_tokens[(size_t)b * (N + 1) + a] = ai;
+      out_tokens[(size_t)b * (N + 1) + a] = row_amax[a];
       jb.mode = kJobDone;
     }
+    // sampling rows: the job row, and with alpha every row k < L of a non-greedy request
+    int rows = (jb.mode == kJobDone) ? 0 : 1;
+    if (accept_prob && hot) rows = L + ((a == L) ? 1 : 0);
+    jb.parts = rows * sample_chunks;
     jobs[b] = jb;
+    tickets[b] = 0u;
+    if (probs) rstat[(size_t)b * (N + 1)] = make_float2(0.0f, 1.0f);
   }
 }
 
-// ------------------------------------------------------------------ sampling row
+// ------------------------------------------------------------------ sampling rows
 
 __device__ __forceinline__ void race_update(float r, float E, int v, float& br, float& bE, int& bv) {
   if (race_beats(r, E, v, br, bE, bv)) {
@@ -262,103 +345,138 @@ __global__ __launch_bounds__(256) void verify_sample(int input_kind, const float
                                                      const float* __restrict__ temperature,
                                                      const uint32_t* __restrict__ request_id, uint32_t key0,
                                                      uint32_t key1, const Job* __restrict__ jobs,
-                                                     RacePartial* __restrict__ race, int B, int N, int V, int Vd,
-                                                     int nchunks, int chunk) {
-  const int b = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+                                                     const float2* __restrict__ rstat, RacePartial* __restrict__ race,
+                                                     float* __restrict__ apart, unsigned* __restrict__ tickets,
+                                                     const int32_t* __restrict__ accepted,
+                                                     int32_t* __restrict__ out_tokens, float* __restrict__ accept_prob,
+                                                     int B, int N, int V, int Vd, int R, int nchunks, int chunk) {
+  const int b = blockIdx.x / (R * nchunks), rr = (blockIdx.x / nchunks) % R, c = blockIdx.x % nchunks;
   const Job jb = jobs[b];
-  if (jb.mode == kJobDone) return;
+  const bool alpha = accept_prob != nullptr && jb.hot;
+  const int k = (R > 1) ? rr : jb.row;
+  const bool do_race = jb.mode != kJobDone && k == jb.row;
+  const bool do_alpha = alpha && k < jb.L;
+  if (!do_race && !do_alpha) return;  // (exactly jb.parts workgroups of the request pass here)
+  const int tid = threadIdx.x, wave = tid >> 6;
   const bool probs = input_kind == DSPARK_INPUT_PROBS;
-  const bool resid = jb.mode == kJobResid;
-  const int k = jb.row;
+  const bool need_draft = do_alpha || jb.mode == kJobResid;
   const uint32_t req = request_id[b];
-  const uint32_t tag = resid ? kTagResid : kTagBonus;
+  const uint32_t tag = (jb.mode == kJobResid) ? kTagResid : kTagBonus;
   const float c2 = probs ? 1.0f : (1.0f / temperature[b]) * kLog2e;
-  const float dlz2 = (!probs && resid) ? draft_log_z[(size_t)b * N + k] * kLog2e : 0.0f;
+  const float dlz2 = (!probs && need_draft && k < N) ? draft_log_z[(size_t)b * N + k] * kLog2e : 0.0f;
+  const float2 st = rstat[(size_t)b * (N + 1) + (probs ? 0 : k)];
   const float* trow = target + ((size_t)b * (N + 1) + k) * V;
-  const float* drow = resid ? draft + ((size_t)b * N + k) * Vd : nullptr;
+  const float* drow = draft + ((size_t)b * N + min(k, N - 1)) * Vd;
   const int lo = c * chunk, hi = min(V, lo + chunk);
 
   // Race candidates start as "nobody": r = 0 with E = 1 at index INT_MAX loses
   // to everything with r > 0, and index order decides among r = 0.
-  float br = 0.0f, bE = 1.0f, fr = 0.0f, fE = 1.0f;
+  float br = 0.0f, bE = 1.0f, fr = 0.0f, fE = 1.0f, asum = 0.0f;
   int bv = 0x7FFFFFFF, fv = 0x7FFFFFFF;
-  for (int v = lo + 4 * threadIdx.x; v < hi; v += 4 * blockDim.x) {
+  for (int v = lo + 4 * tid; v < hi; v += 4 * blockDim.x) {
     const float4 q = *reinterpret_cast<const float4*>(trow + v);
     float pt[4] = {q.x, q.y, q.z, q.w};
     if (!probs) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) pt[f] = __builtin_amdgcn_exp2f(pt[f] * c2 - jb.m) * jb.invs;
+      for (int f = 0; f < 4; ++f) pt[f] = __builtin_amdgcn_exp2f(pt[f] * c2 - st.x) * st.y;
     }
-    const u32x4 w = philox4x32_10(u32x4{(uint32_t)v >> 2, (uint32_t)k, req, tag}, key0, key1);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float pd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (need_draft) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const float E = -plog2(uniform01(ws[f]));
-      if (resid) {
+      for (int f = 0; f < 4; ++f) {
         const int j = inv_map ? inv_map[v + f] : v + f;
-        float pd = 0.0f;
         if (j >= 0) {
           const float d = drow[j];
-          pd = probs ? d : __builtin_amdgcn_exp2f(d * c2 - dlz2);
+          pd[f] = probs ? d : __builtin_amdgcn_exp2f(d * c2 - dlz2);
         }
-        const float r = fmaxf(0.0f, __fsub_rn(pt[f], pd));
-        race_update(r, E, v + f, br, bE, bv);
-        race_update(pt[f], E, v + f, fr, fE, fv);
-      } else {
-        race_update(pt[f], E, v + f, br, bE, bv);
+      }
+    }
+    if (do_alpha) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) asum += fminf(pt[f], pd[f]);
+    }
+    if (do_race) {
+      const u32x4 w = philox4x32_10(u32x4{(uint32_t)v >> 2, (uint32_t)k, req, tag}, key0, key1);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const float E = -plog2(uniform01(ws[f]));
+        if (jb.mode == kJobResid) {
+          race_update(fmaxf(0.0f, __fsub_rn(pt[f], pd[f])), E, v + f, br, bE, bv);
+          race_update(pt[f], E, v + f, fr, fE, fv);
+        } else {
+          race_update(pt[f], E, v + f, br, bE, bv);
+        }
       }
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float o_r = __shfl_xor(br, off), o_E = __shfl_xor(bE, off);
-    const int o_v = __shfl_xor(bv, off);
-    const float o_fr = __shfl_xor(fr, off), o_fE = __shfl_xor(fE, off);
-    const int o_fv = __shfl_xor(fv, off);
-    race_update(o_r, o_E, o_v, br, bE, bv);
-    race_update(o_fr, o_fE, o_fv, fr, fE, fv);
-  }
   __shared__ RacePartial red[4];
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = RacePartial{br, bE, bv, fr, fE, fv, {0, 0}};
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    RacePartial a = red[0];
-    for (int w2 = 1; w2 < (int)(blockDim.x >> 6); ++w2) {
-      race_update(red[w2].r, red[w2].E, red[w2].v, a.r, a.E, a.v);
-      race_update(red[w2].fr, red[w2].fE, red[w2].fv, a.fr, a.fE, a.fv);
-    }
-    race[(size_t)b * nchunks + c] = a;
-  }
-}
-
-__global__ __launch_bounds__(64) void verify_finalize(const Job* __restrict__ jobs,
-                                                      const RacePartial* __restrict__ race,
-                                                      const int32_t* __restrict__ accepted,
-                                                      int32_t* __restrict__ out_tokens, int N, int nchunks) {
-  const int b = blockIdx.x, lane = threadIdx.x;
-  const Job jb = jobs[b];
-  if (jb.mode == kJobDone) return;
-  float br = 0.0f, bE = 1.0f, fr = 0.0f, fE = 1.0f;
-  int bv = 0x7FFFFFFF, fv = 0x7FFFFFFF;
-  for (int c = lane; c < nchunks; c += 64) {
-    const RacePartial q = race[(size_t)b * nchunks + c];
-    race_update(q.r, q.E, q.v, br, bE, bv);
-    race_update(q.fr, q.fE, q.fv, fr, fE, fv);
-  }
+  __shared__ float ared[4];
+  __shared__ unsigned s_ticket;
+  if (do_race) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float o_r = __shfl_xor(br, off), o_E = __shfl_xor(bE, off);
-    const int o_v = __shfl_xor(bv, off);
-    const float o_fr = __shfl_xor(fr, off), o_fE = __shfl_xor(fE, off);
-    const int o_fv = __shfl_xor(fv, off);
-    race_update(o_r, o_E, o_v, br, bE, bv);
-    race_update(o_fr, o_fE, o_fv, fr, fE, fv);
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float o_r = __shfl_xor(br, off), o_E = __shfl_xor(bE, off);
+      const int o_v = __shfl_xor(bv, off);
+      const float o_fr = __shfl_xor(fr, off), o_fE = __shfl_xor(fE, off);
+      const int o_fv = __shfl_xor(fv, off);
+      race_update(o_r, o_E, o_v, br, bE, bv);
+      race_update(o_fr, o_fE, o_fv, fr, fE, fv);
+    }
+    if ((tid & 63) == 0) red[wave] = RacePartial{br, bE, bv, fr, fE, fv, {0, 0}};
   }
-  if (lane == 0) {
+  if (do_alpha) {
+    asum = group_sum(asum, 64);
+    if ((tid & 63) == 0) ared[wave] = asum;
+  }
+  __syncthreads();
+  const int slot = (b * R + (R > 1 ? k : 0)) * nchunks + c;
+  if (tid == 0) {
+    if (do_race) {
+      RacePartial a = red[0];
+      for (int w2 = 1; w2 < 4; ++w2) {
+        race_update(red[w2].r, red[w2].E, red[w2].v, a.r, a.E, a.v);
+        race_update(red[w2].fr, red[w2].fE, red[w2].fv, a.fr, a.fE, a.fv);
+      }
+      store_race(race + slot, a);
+    }
+    if (do_alpha) st_f(apart + slot, (ared[0] + ared[1]) + (ared[2] + ared[3]));
+  }
+  // the request's last workgroup merges (its partial stores completed at the barrier)
+  __syncthreads();
+  if (tid == 0) s_ticket = __hip_atomic_fetch_add(tickets + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_ticket != (unsigned)jb.parts - 1) return;
+  const int lane = tid & 63;
+  if (jb.mode != kJobDone && wave == 0) {
+    float r0 = 0.0f, E0 = 1.0f, r1 = 0.0f, E1 = 1.0f;
+    int v0 = 0x7FFFFFFF, v1 = 0x7FFFFFFF;
+    const RacePartial* rp = race + (size_t)(b * R + (R > 1 ? jb.row : 0)) * nchunks;
+    for (int cc = lane; cc < nchunks; cc += 64) {
+      const RacePartial q = load_race(rp + cc);
+      race_update(q.r, q.E, q.v, r0, E0, v0);
+      race_update(q.fr, q.fE, q.fv, r1, E1, v1);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float o_r = __shfl_xor(r0, off), o_E = __shfl_xor(E0, off);
+      const int o_v = __shfl_xor(v0, off);
+      const float o_fr = __shfl_xor(r1, off), o_fE = __shfl_xor(E1, off);
+      const int o_fv = __shfl_xor(v1, off);
+      race_update(o_r, o_E, o_v, r0, E0, v0);
+      race_update(o_fr, o_fE, o_fv, r1, E1, v1);
+    }
     // an all-zero residual leaves r == 0 at the winner: fall back to p_t
-    const int y = (jb.mode == kJobResid && br == 0.0f) ? fv : bv;
-    out_tokens[(size_t)b * (N + 1) + accepted[b]] = y;
+    if (lane == 0) out_tokens[(size_t)b * (N + 1) + jb.row] = (jb.mode == kJobResid && r0 == 0.0f) ? v1 : v0;
+  }
+  if (alpha) {
+    for (int kk = wave; kk < N; kk += 4) {
+      float sum = 0.0f;
+      if (kk < jb.L)
+        for (int cc = lane; cc < nchunks; cc += 64) sum += ld_f(apart + (size_t)(b * R + kk) * nchunks + cc);
+      sum = group_sum(sum, 64);
+      if (lane == 0) accept_prob[(size_t)b * N + kk] = (kk < jb.L) ? sum : __builtin_nanf("");
+    }
   }
 }
 
@@ -380,9 +498,12 @@ VerifyPlan plan_verify(int B, int N, int V) {
   p.sample_chunks = pick_chunks(B, V);
   p.sample_chunk = ((V + p.sample_chunks - 1) / p.sample_chunks + 3) / 4 * 4;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  p.stats_bytes = al((size_t)B * (N + 1) * p.stat_chunks * sizeof(RowStat));
-  p.jobs_bytes = al((size_t)B * sizeof(Job));
-  p.race_bytes = al((size_t)B * p.sample_chunks * sizeof(RacePartial));
+  const size_t rows = (size_t)B * (N + 1);
+  p.stats_bytes = al(rows * p.stat_chunks * sizeof(RowStat));
+  p.jobs_bytes = al((size_t)B * sizeof(Job)) + al(rows * sizeof(float2)) + al((size_t)B * sizeof(unsigned));
+  // race and alpha partials for every (request, row, chunk): the rows dimension is
+  // used only when alpha is requested, but the size must not depend on the call
+  p.race_bytes = al(rows * p.sample_chunks * sizeof(RacePartial)) + al(rows * p.sample_chunks * sizeof(float));
   p.total_bytes = p.stats_bytes + p.jobs_bytes + p.race_bytes;
   return p;
 }
@@ -390,26 +511,37 @@ VerifyPlan plan_verify(int B, int N, int V) {
 hipError_t launch_verify(int input_kind, const float* target, const float* draft, const float* draft_log_z,
                          const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
                          const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
-                         int32_t* out_tokens, int B, int N, int V, int Vd, void* workspace, hipStream_t stream) {
+                         int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
+                         hipStream_t stream) {
   const VerifyPlan p = plan_verify(B, N, V);
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t rows = (size_t)B * (N + 1);
   char* ws = static_cast<char*>(workspace);
   RowStat* stats = reinterpret_cast<RowStat*>(ws);
-  Job* jobs = reinterpret_cast<Job*>(ws + p.stats_bytes);
-  RacePartial* race = reinterpret_cast<RacePartial*>(ws + p.stats_bytes + p.jobs_bytes);
+  char* w = ws + p.stats_bytes;
+  Job* jobs = reinterpret_cast<Job*>(w);
+  w += al((size_t)B * sizeof(Job));
+  float2* rstat = reinterpret_cast<float2*>(w);
+  w += al(rows * sizeof(float2));
+  unsigned* tickets = reinterpret_cast<unsigned*>(w);
+  w += al((size_t)B * sizeof(unsigned));
+  RacePartial* race = reinterpret_cast<RacePartial*>(w);
+  w += al(rows * p.sample_chunks * sizeof(RacePartial));
+  float* apart = reinterpret_cast<float*>(w);
   const uint32_t k0 = (uint32_t)(seed & 0xFFFFFFFFu), k1 = (uint32_t)(seed >> 32);
   const bool probs = input_kind == DSPARK_INPUT_PROBS;
   if (!probs) {
     hipLaunchKernelGGL(verify_rowstats, dim3((unsigned)((long)B * (N + 1) * p.stat_chunks)), dim3(256), 0, stream,
                        target, verify_len, temperature, stats, B, N, V, p.stat_chunks, p.stat_chunk);
   }
-  hipLaunchKernelGGL(verify_accept, dim3(B), dim3(64), 0, stream, input_kind, target, draft, draft_log_z,
-                     draft_tokens, inv_map, verify_len, temperature, request_id, k0, k1, stats, jobs, accepted,
-                     out_tokens, B, N, V, Vd, p.stat_chunks);
-  hipLaunchKernelGGL(verify_sample, dim3((unsigned)((long)B * p.sample_chunks)), dim3(256), 0, stream, input_kind,
-                     target, draft, draft_log_z, inv_map, temperature, request_id, k0, k1, jobs, race, B, N, V, Vd,
-                     p.sample_chunks, p.sample_chunk);
-  hipLaunchKernelGGL(verify_finalize, dim3(B), dim3(64), 0, stream, jobs, race, accepted, out_tokens, N,
-                     p.sample_chunks);
+  hipLaunchKernelGGL(verify_accept, dim3(B), dim3(256), 0, stream, input_kind, target, draft, draft_log_z,
+                     draft_tokens, inv_map, verify_len, temperature, request_id, k0, k1, stats, rstat, jobs, tickets,
+                     accepted, out_tokens, accept_prob, B, N, V, Vd, p.stat_chunks, p.sample_chunks);
+  const int R = accept_prob ? N + 1 : 1;
+  hipLaunchKernelGGL(verify_sample, dim3((unsigned)((long)B * R * p.sample_chunks)), dim3(256), 0, stream,
+                     input_kind, target, draft, draft_log_z, inv_map, temperature, request_id, k0, k1, jobs, rstat,
+                     race, apart, tickets, accepted, out_tokens, accept_prob, B, N, V, Vd, R, p.sample_chunks,
+                     p.sample_chunk);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 1
+#define DSPARK_ABI_VERSION 2
 
 typedef enum dspark_status {
   DSPARK_OK = 0,
@@ -163,7 +163,12 @@ dspark_status dspark_build_inverse_map(const int64_t* d2t, int Vd, int V, int32_
  *   dspark_race_exponentials, compared exactly as r_a*E_b vs r_b*E_a in double,
  *   ties to the smaller v.
  *   Outputs: accepted[b] = number of accepted draft tokens a;
- *            out_tokens[b, :] = x_0 .. x_{a-1}, y, then -1 up to column N.
+ *            out_tokens[b, :] = x_0 .. x_{a-1}, y, then -1 up to column N;
+ *            accept_prob[b, k] (optional) = sum_v min(p_t[k](v), p_d[k](v)), the
+ *            probability that position k is accepted, i.e. one minus the total
+ *            variation distance [P2 §2], for k < L; NaN for k >= L (those target
+ *            rows are not read).  It costs one extra pass over rows k < L of both
+ *            sides; NULL skips it.
  * input_kind DSPARK_INPUT_PROBS: target = p_t [B, N+1, V] float32 probabilities,
  *            draft = p_d [B, N, Vd] float32 probabilities; draft_log_z and
  *            temperature are ignored (may be NULL).  Given the same float32 arrays
@@ -180,7 +185,8 @@ dspark_status dspark_build_inverse_map(const int64_t* d2t, int Vd, int V, int32_
  *   inv_map  [V] int32 (dspark_build_inverse_map), device; NULL iff Vd == V.
  *   verify_len [B] int32 in [0, N], device, or NULL (= N); dspark_admit's admit_len fits.
  *   temperature [B] float32 >= 0 (logits mode), request_id [B] uint32, device.
- *   accepted [B] int32 out; out_tokens [B, N+1] int32 out; device.
+ *   accepted [B] int32 out; out_tokens [B, N+1] int32 out; accept_prob [B, N] float32
+ *            out or NULL; device.
  *   1 <= B <= DSPARK_MAX_B, 1 <= N <= DSPARK_MAX_N, V % 4 == 0, Vd % 4 == 0, Vd <= V.
  *   workspace >= dspark_verify_workspace_size(B, N, V) bytes, device, 16-byte aligned.
  */
@@ -189,7 +195,7 @@ dspark_status dspark_verify(int input_kind, const float* target, const float* dr
                             const float* draft_log_z, const int32_t* draft_tokens,
                             const int32_t* inv_map, const int32_t* verify_len,
                             const float* temperature, const uint32_t* request_id, uint64_t seed,
-                            int32_t* accepted, int32_t* out_tokens,
+                            int32_t* accepted, int32_t* out_tokens, float* accept_prob,
                             int B, int N, int V, int Vd,
                             void* workspace, size_t workspace_bytes, void* stream);
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(dspark_lib):
 
 
 def test_abi_version(dspark_lib):
-    assert dsl.abi_version() == 1
+    assert dsl.abi_version() == 2
 
 
 def _err():
@@ -77,7 +77,7 @@ def test_markov_validation(dspark_lib):
 
 def _verify(**kw):
     a = dict(kind=0, target=FAKE, draft=FAKE, draft_log_z=FAKE, draft_tokens=FAKE, inv_map=None, verify_len=None,
-             temperature=FAKE, request_id=FAKE, seed=0, accepted=FAKE, out_tokens=FAKE, B=2, N=8, V=1024,
+             temperature=FAKE, request_id=FAKE, seed=0, accepted=FAKE, out_tokens=FAKE, accept_prob=None, B=2, N=8, V=1024,
              Vd=1024, workspace=FAKE, workspace_bytes=1 << 30, stream=None)
     a.update(kw)
     return dsl.load().dspark_verify(*a.values())

@@ -292,6 +292,63 @@ def test_verify_logits_parity(B, N, V, Vd, temps, reduced):
     assert near <= max(1, B // 50)
 
 
+def _alpha_ref(p_t, p_d, inv, L):
+    """Oracle alpha_k = sum_v min(p_t, p_d) for k < L (p_d mapped to target ids), NaN after."""
+    B, N = p_d.shape[:2]
+    out = np.full((B, N), np.nan)
+    for b in range(B):
+        for k in range(int(L[b])):
+            pd_t = p_d[b, k] if inv is None else np.where(inv >= 0, p_d[b, k][np.maximum(inv, 0)], 0.0)
+            out[b, k] = stages.accept_prob(p_t[b, k], pd_t)
+    return out
+
+
+def _check_alpha(gpu, ref, tol):
+    assert np.array_equal(np.isnan(gpu), np.isnan(ref)), "alpha: NaN pattern (positions past verify_len)"
+    m = ~np.isnan(ref)
+    err = np.abs(gpu[m].astype(np.float64) - ref[m])
+    assert err.max(initial=0.0) <= tol, f"alpha: max abs err {err.max():.3g}"
+    return err.max(initial=0.0)
+
+
+@pytest.mark.parametrize("mode,B,N,V,Vd,temps,reduced", [
+    ("probs", 40, 6, 1024, 1024, (0.7, 1.0), False),
+    ("probs", 9, 8, 2048, 1000, (1.0,), True),
+    ("logits", 33, 5, 4096, 4096, (0.0, 0.7, 1.0), False),
+    ("logits", 12, 8, 2048, 1000, (0.0, 1.0), True),
+    ("logits", 1, 8, 151936, 151936, (1.0,), False),
+])
+def test_verify_accept_prob(mode, B, N, V, Vd, temps, reduced):
+    say(f"verify accept_prob {mode} B={B} N={N} V={V} Vd={Vd} T={temps}")
+    c = _verify_inputs(B, N, V, Vd, temps, seed=B * 7 + N, reduced=reduced)
+    temp = c["temp"]
+    p_t = np.stack([[stages.probs_from_logits(c["tgt"][b, k], float(temp[b])) for k in range(N + 1)]
+                    for b in range(B)])
+    p_d = np.stack([[stages.draft_probs(c["proc"][b, k], float(temp[b]),
+                                        int(c["inv"][c["tok"][b, k]]) if c["inv"] is not None else int(c["tok"][b, k]))
+                     for k in range(N)] for b in range(B)])
+    seed = 991
+    inv = None if c["inv"] is None else dev(c["inv"])
+    if mode == "probs":
+        args = (dsl.INPUT_PROBS, dev(p_t), dev(p_d), None, dev(c["tok"]), inv, dev(c["L"]), None, dev(c["rid"]), seed)
+    else:
+        logz = np.empty((B, N), np.float32)
+        for b in range(B):
+            for k in range(N):
+                T = float(temp[b])
+                y = c["proc"][b, k].astype(np.float64)
+                logz[b, k] = (np.log(np.exp(y / T - (y / T).max()).sum()) + (y / T).max()) if T > 0 else y.max()
+        args = (dsl.INPUT_LOGITS, dev(c["tgt"]), dev(c["proc"]), dev(logz), dev(c["tok"]), inv, dev(c["L"]),
+                dev(temp), dev(c["rid"]), seed)
+    acc0, out0 = dsl.verify(*args)
+    acc1, out1, alpha = dsl.verify(*args, with_accept_prob=True)
+    # the optional output does not change the sampled result
+    assert np.array_equal(host(acc0), host(acc1)) and np.array_equal(host(out0), host(out1))
+    ref = _alpha_ref(p_t, p_d, c["inv"], c["L"])
+    err = _check_alpha(host(alpha), ref, 2e-5)
+    say(f"  alpha max abs err {err:.2e}")
+
+
 def test_verify_greedy_is_longest_argmax_prefix():
     B, N, V = 100, 6, 1024
     c = _verify_inputs(B, N, V, V, (0.0,), seed=9, sigma=0.3)
