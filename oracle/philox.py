@@ -20,6 +20,8 @@ caller's 32-bit request id, ``tag`` the purpose of the draw:
     TAG_ACCEPT  1  acceptance uniform of the rejection test
     TAG_RESID   2  exponential race of the residual resample
     TAG_BONUS   3  exponential race of the bonus token
+    TAG_TARGET  4  Gumbel noise of a target id outside the draft vocabulary
+                   (Gumbel-coupled verification)
 
 Uniform map: ``u = ((w >> 8) | 1) * 2**-24`` -- exact in float32, odd
 multiples of 2**-24, so never 0 and never 1.
@@ -31,7 +33,7 @@ from __future__ import annotations
 
 import numpy as np
 
-TAG_DRAFT, TAG_ACCEPT, TAG_RESID, TAG_BONUS = 0, 1, 2, 3
+TAG_DRAFT, TAG_ACCEPT, TAG_RESID, TAG_BONUS, TAG_TARGET = 0, 1, 2, 3, 4
 
 _MASK = np.uint64(0xFFFFFFFF)
 _MUL0 = np.uint64(0xD2511F53)   # multiplier of counter word 0

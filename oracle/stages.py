@@ -21,6 +21,11 @@ Stage 3  verify          [P2 §2; greedy case P3 §2]: accept x_k with
 Stage 4  admit           [P2 §6, §7]: survival = running product of the
                          conditional acceptances; all B*N candidates pooled,
                          ordered by survival, the first K admitted.
+Next rows:
+  verify_coupled         [P1 §5]: the target verifies with the same Gumbel seed
+                         the draft sampled with: y_k = Gumbel-max sample of the
+                         target row under the draft's noise; accept while y_k ==
+                         x_k; the first mismatch (or the bonus row) emits y.
 
 Readings where the pages are silent (the same readings hold on the GPU side):
   * temperature T > 0 divides the logits; T = 0 means greedy (argmax, no
@@ -296,6 +301,74 @@ def accept_prob(p_t_row, p_d_row_target_space) -> float:
     a = np.asarray(p_t_row, dtype=np.float64)
     b = np.asarray(p_d_row_target_space, dtype=np.float64)
     return float(np.minimum(a, b).sum())
+
+
+def coupled_noise(seed: int, position: int, req: int, V: int, inv) -> np.ndarray:
+    """Gumbel noise G(v) of target row ``position`` for Gumbel-coupled verification.
+
+    A target id v that is draft entry j (inv[v] = j, or j = v without a reduced
+    vocabulary) gets the very noise stage 2 drew for j at that position (tag 0,
+    keyed on j); an id outside the draft vocabulary gets its own draw (tag 4,
+    keyed on v).  So the G(v) are independent standard Gumbels over v.
+    """
+    v_all = np.arange(V, dtype=np.int64)
+    if inv is None:
+        j = v_all
+        own = np.zeros(V, dtype=bool)
+    else:
+        inv = np.asarray(inv, dtype=np.int64)
+        own = inv < 0
+        j = np.where(own, v_all, inv)
+    u_draft = philox.uniforms(seed, j.astype(np.uint64), position, req, philox.TAG_DRAFT)
+    u_own = philox.uniforms(seed, v_all.astype(np.uint64), position, req, philox.TAG_TARGET)
+    return gumbel(np.where(own, u_own, u_draft))
+
+
+def verify_coupled(target_logits, draft_tokens, inv_map, verify_len, temperature, request_id,
+                   seed: int, requests: Optional[Sequence[int]] = None) -> Dict[str, object]:
+    """Gumbel-coupled verification [P1 §5: the target verifies with the same
+    Gumbel seed as the draft, and the output distribution is unchanged].
+
+    target_logits [B, N+1, V] fp32; draft_tokens [B, N] target ids drawn by
+    stage 2 with the same seed and request ids; inv_map [V] or None.
+    Row k of request b: y_k = argmax_v l_t[k](v) / T + G_k(v) (coupled_noise;
+    T = 0: argmax l_t[k]), ties to the smaller v, keys in fp64.  With L the
+    verify length, a = the first k < L with y_k != x_k (else L); the output is
+    x_0 .. x_{a-1}, y_a, then -1.  Every emitted token is a y, a Gumbel-max draw
+    from p_t, so the output follows the target; a draft token is accepted exactly
+    when the target's own draw under the same noise picks it.
+
+    Returns accepted [B], out_tokens [B, N+1], and gap [B, N+1]: the top-2 key
+    margin of each row k <= L (NaN beyond), for near-tie tolerance.
+    Pins: T = 0 equals greedy verification; a target equal to the draft's
+    processed logits accepts every stage-2 draft; the emitted first token follows
+    softmax(l_t/T) (chi-square); acceptance at position 0 is at most 1 - TV.
+    """
+    x_all = np.asarray(draft_tokens, dtype=np.int64)
+    nb, N = x_all.shape
+    reqs = np.arange(nb) if requests is None else np.asarray(requests, dtype=np.int64)
+    inv = None if inv_map is None else np.asarray(inv_map, dtype=np.int64)
+    accepted = np.empty(nb, dtype=np.int32)
+    out = np.full((nb, N + 1), -1, dtype=np.int32)
+    gap = np.full((nb, N + 1), np.nan)
+    for n, b in enumerate(reqs):
+        L = N if verify_len is None else int(verify_len[b])
+        T = float(np.float32(temperature[b]))
+        req = int(request_id[b])
+        a, y_a = L, None
+        for k in range(L + 1):
+            l = np.asarray(target_logits[n, k], dtype=np.float64)
+            key = (l / T + coupled_noise(seed, k, req, l.size, inv)) if T > 0.0 else l
+            y = int(np.argmax(key))                 # the first maximum: the smaller v
+            top2 = np.partition(key, -2)[-2:] if key.size > 1 else np.array([-np.inf, key[0]])
+            gap[n, k] = float(top2[1] - top2[0])
+            if k == L or y != x_all[n, k]:
+                a, y_a = k, y
+                break
+        accepted[n] = a
+        out[n, :a] = x_all[n, :a]
+        out[n, a] = y_a
+    return {"accepted": accepted, "out_tokens": out, "gap": gap}
 
 
 # ---------------------------------------------------------------- stage 4

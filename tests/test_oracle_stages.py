@@ -359,3 +359,80 @@ def test_admit_non_anticipation():
         c2 = c.copy()
         c2[b, k + 1:] = g.uniform(1e-3, 1.0, size=c.shape[1] - k - 1).astype(np.float32)
         assert stages.admit(c2, K)["admitted"][b, k] == base[b, k]
+
+
+# ---------------------------------------------------------------- next rows: coupled verify
+
+def test_coupled_verify_greedy_equals_greedy_verify():
+    # T = 0 uses no noise: the longest prefix matching the target argmaxes, then the argmax
+    g = np.random.default_rng(21)
+    B, N, V = 30, 5, 40
+    tgt = g.normal(size=(B, N + 1, V)).astype(np.float32)
+    am = tgt.argmax(axis=2)
+    tok = np.where(g.random((B, N)) < 0.7, am[:, :N], g.integers(0, V, size=(B, N))).astype(np.int32)
+    L = g.integers(0, N + 1, size=B).astype(np.int32)
+    T = np.zeros(B, np.float32)
+    rid = np.arange(B, dtype=np.uint32)
+    cp = stages.verify_coupled(tgt, tok, None, L, T, rid, 3)
+    ref = stages.verify("logits", tgt, g.normal(size=(B, N, V)).astype(np.float32), tok, None, L, T, rid, 3)
+    assert np.array_equal(cp["accepted"], ref["accepted"])
+    assert np.array_equal(cp["out_tokens"], ref["out_tokens"])
+
+
+@pytest.mark.parametrize("Vd", [40, 25])
+def test_coupled_verify_accepts_its_own_drafts(Vd):
+    # a target equal to the draft's processed logits (in target ids) draws, under the
+    # same noise, exactly the stage-2 tokens: every position is accepted
+    V, N, B = 40, 4, 12
+    c = _small(V=V, Vd=Vd, r=4, N=N, B=B, seed=5)
+    g = np.random.default_rng(6)
+    d2t = None if Vd == V else (g.permutation(V)[:Vd] - np.arange(Vd)).astype(np.int64)
+    inv = None if d2t is None else stages.build_inverse_map(d2t, Vd, V)
+    T = np.full(B, 0.8, np.float32)
+    rid = (np.arange(B) * 5 + 1).astype(np.uint32)
+    seed = 0x1234
+    mk = stages.markov_sample(c["base"], c["w1"], c["w2"], d2t, c["anchor"], T, rid, seed)
+    t_of_j = np.arange(Vd) + (0 if d2t is None else d2t)
+    tgt = np.full((B, N + 1, V), -np.inf, np.float32)
+    tgt[:, :N, t_of_j] = mk["processed"]
+    tgt[:, N] = g.normal(size=(B, V)).astype(np.float32)
+    cp = stages.verify_coupled(tgt, mk["tokens"], inv, None, T, rid, seed)
+    clear = (mk["gap"] > 1e-5).all(axis=1)        # no fp32 rounding near-tie in the chain
+    assert clear.sum() >= B - 1
+    assert (cp["accepted"][clear] == N).all()
+    # the bonus is the target's own draw at row N
+    for b in np.nonzero(clear)[0]:
+        key = tgt[b, N].astype(np.float64) / 0.8 + stages.coupled_noise(seed, N, int(rid[b]), V, inv)
+        assert cp["out_tokens"][b, N] == int(np.argmax(key))
+
+
+def test_coupled_verify_is_lossless_chi_square():
+    # every emitted token is the target's Gumbel-max draw, so out[0] ~ softmax(l_t / T)
+    V, B = 7, 6000
+    g = np.random.default_rng(8)
+    row = g.normal(size=V).astype(np.float32)
+    tgt = np.broadcast_to(np.concatenate([row[None], g.normal(size=(1, V)).astype(np.float32)])[None], (B, 2, V))
+    tok = np.zeros((B, 1), np.int32)                  # any fixed draft token
+    T = np.full(B, 0.9, np.float32)
+    cp = stages.verify_coupled(tgt, tok, None, None, T, np.arange(B, dtype=np.uint32), 77)
+    counts = np.bincount(cp["out_tokens"][:, 0], minlength=V)
+    assert _chi2_ok(counts, stages.probs_from_logits(row, 0.9))
+
+
+def test_coupled_verify_acceptance_at_most_one_minus_tv():
+    # drafts from stage 2 and the target under the same noise: a coupling of p_d and p_t,
+    # so the agreement rate cannot exceed sum min(p_t, p_d)
+    V, B = 9, 6000
+    g = np.random.default_rng(11)
+    base = np.broadcast_to(g.normal(size=(1, 1, V)).astype(np.float32), (B, 1, V)).copy()
+    zero = synth.bf16_bits(np.zeros((V, 2), np.float32))
+    T = np.ones(B, np.float32)
+    rid = np.arange(B, dtype=np.uint32)
+    mk = stages.markov_sample(base, zero, zero, None, np.zeros(B, np.int32), T, rid, 9)
+    trow = (base[0, 0] + g.normal(0, 0.8, size=V)).astype(np.float32)
+    tgt = np.broadcast_to(np.stack([trow, trow])[None], (B, 2, V))
+    cp = stages.verify_coupled(tgt, mk["tokens"], None, None, T, rid, 9)
+    rate = (cp["accepted"] >= 1).mean()
+    alpha = stages.accept_prob(stages.probs_from_logits(trow, 1.0), stages.probs_from_logits(base[0, 0], 1.0))
+    assert rate <= alpha + 4 * math.sqrt(alpha * (1 - alpha) / B)
+    assert rate > 0.5 * alpha                          # and it is a real coupling, not independence
