@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--workload", default="qwen3_8b_single",
                    help="tiny | qwen3_8b_single | batched | admission | reduced_vocab")
     p.add_argument("--graph", action="store_true", help="replay each step as one captured HIP graph")
+    p.add_argument("--verify", default="rejection", choices=("rejection", "coupled"),
+                   help="stage 3 rule: rejection sampling on p_t, p_d (default) or Gumbel-coupled verification")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -56,8 +58,9 @@ def src_hash(path: str) -> str:
 class Path:
     """Device buffers and the four C-ABI calls of one round."""
 
-    def __init__(self, w, torch, dsl, synth):
+    def __init__(self, w, torch, dsl, synth, verify_mode="rejection"):
         self.w, self.torch, self.dsl = w, torch, dsl
+        self.coupled = verify_mode == "coupled"
         dev = torch.device("cuda:0")
         rp = synth.request_params(w)
 
@@ -93,8 +96,9 @@ class Path:
         self.out_tokens = torch.empty((w.B, w.N + 1), dtype=torch.int32, device=dev)
         self.ws_markov = torch.empty(max(16, dsl.markov_workspace_size(w.B, w.N, w.Vd, w.r)),
                                      dtype=torch.uint8, device=dev)
-        self.ws_verify = torch.empty(max(16, dsl.verify_workspace_size(w.B, w.N, w.V)),
-                                     dtype=torch.uint8, device=dev)
+        vws = dsl.verify_coupled_workspace_size(w.B, w.N, w.V) if self.coupled else \
+            dsl.verify_workspace_size(w.B, w.N, w.V)
+        self.ws_verify = torch.empty(max(16, vws), dtype=torch.uint8, device=dev)
         # target logits [B, N+1, V]: this batch's base logits (row N repeats row N-1),
         # scattered to target ids, plus N(0, sigma_b) noise -- made once, untimed
         dsl.draft_logits(self.hidden, self.lm_head, out=self.logits.view(w.M, w.Vd))
@@ -124,10 +128,27 @@ class Path:
         rec(2)
         dsl.admit(self.conf, self.K, survival=self.survival, admit_len=self.admit_len)
         rec(3)
-        dsl.verify(dsl.INPUT_LOGITS, self.target, self.logits, self.logz, self.tokens, self.inv, self.admit_len,
-                   self.temp, self.rid, self.seed, accepted=self.accepted, out_tokens=self.out_tokens,
-                   workspace=self.ws_verify)
+        if self.coupled:
+            dsl.verify_coupled(self.target, self.tokens, self.inv, self.admit_len, self.temp, self.rid, self.seed,
+                               Vd=w.Vd, accepted=self.accepted, out_tokens=self.out_tokens,
+                               workspace=self.ws_verify)
+        else:
+            dsl.verify(dsl.INPUT_LOGITS, self.target, self.logits, self.logz, self.tokens, self.inv,
+                       self.admit_len, self.temp, self.rid, self.seed, accepted=self.accepted,
+                       out_tokens=self.out_tokens, workspace=self.ws_verify)
         rec(4)
+
+
+def stage_bytes(w, admit_len, coupled):
+    """Compulsory HBM bytes of stage 2 and stage 3 per step.
+    Stage 2: base logits read and processed logits written (8 B per entry), W2
+    once, one W1 row per position.  Stage 3: target rows k <= L_b (4 V each);
+    rejection sampling also reads one target and one draft row to sample from."""
+    k2 = 8 * w.B * w.N * w.Vd + 2 * w.r * w.Vd + 2 * w.r * w.B * w.N
+    k3 = 4 * w.V * int((np.asarray(admit_len) + 1).sum())
+    if not coupled:
+        k3 += w.B * (4 * w.V + 4 * w.Vd)
+    return k2, k3
 
 
 def k1_work(w):
@@ -244,7 +265,7 @@ def main():
         from draft_sampling_lossless_amd import build
         build.build()
     w = synth.get(args.workload)
-    path = Path(w, torch, dsl, synth)
+    path = Path(w, torch, dsl, synth, args.verify)
 
     graph = None
     if args.graph:
@@ -292,6 +313,7 @@ def main():
 
     positions = w.B * w.N
     value = positions / (ms_per_step * 1e-3)
+    k2_bytes, k3_bytes = stage_bytes(w, path.admit_len.cpu().numpy(), path.coupled)
     roof = k1_roofline(w, stage_ms[0])
     result = {
         "metric": "draft+verify positions/sec (B*N) and achieved HBM GB/s at V=151936",
@@ -310,8 +332,13 @@ def main():
                    "K": w.budget, "graph": bool(args.graph)},
         "stage_ms": {"draft_logits": round(stage_ms[0], 4), "markov_sample": round(stage_ms[1], 4),
                      "admit": round(stage_ms[2], 4), "verify": round(stage_ms[3], 4)},
+        "stage_hbm_gbs": {"markov_sample": round(k2_bytes / (stage_ms[1] * 1e-3) / 1e9, 1),
+                          "verify": round(k3_bytes / (stage_ms[3] * 1e-3) / 1e9, 1),
+                          "markov_bytes": k2_bytes, "verify_bytes": k3_bytes},
         "roofline": roof,
     }
+    if path.coupled:
+        result["config"]["verify"] = "coupled"
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -49,6 +49,9 @@ _SIGS = {
     "dspark_verify_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
     "dspark_verify": (_c_int, [_c_int] + [_c_void_p] * 8 + [_c_u64, _c_void_p, _c_void_p, _c_void_p] + [_c_int] * 4
                       + [_c_void_p, _c_size, _c_void_p]),
+    "dspark_verify_coupled_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
+    "dspark_verify_coupled": (_c_int, [_c_void_p] * 6 + [_c_u64, _c_void_p, _c_void_p] + [_c_int] * 4
+                              + [_c_void_p, _c_size, _c_void_p]),
     "dspark_admit": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
 }
 
@@ -232,6 +235,34 @@ def verify(input_kind: int, target: torch.Tensor, draft: torch.Tensor, draft_log
         B, N, V, Vd, ws.data_ptr(), ws.numel(), _stream(target)))
     if accept_prob is not None:
         return accepted, out_tokens, accept_prob
+    return accepted, out_tokens
+
+
+def verify_coupled_workspace_size(B: int, N: int, V: int) -> int:
+    return int(load().dspark_verify_coupled_workspace_size(B, N, V))
+
+
+def verify_coupled(target: torch.Tensor, draft_tokens: torch.Tensor, inv_map: Optional[torch.Tensor],
+                   verify_len: Optional[torch.Tensor], temperature: torch.Tensor, request_id: torch.Tensor, seed: int,
+                   Vd: Optional[int] = None, accepted: Optional[torch.Tensor] = None,
+                   out_tokens: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gumbel-coupled verification.  target [B, N+1, V] logits.  Returns (accepted [B], out_tokens [B, N+1])."""
+    B, N1, V = target.shape
+    N = N1 - 1
+    Vd = V if Vd is None else Vd
+    dev = target.device
+    if accepted is None:
+        accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace, verify_coupled_workspace_size(B, N, V), dev)
+    _check("dspark_verify_coupled", load().dspark_verify_coupled(
+        _ptr(target, "target", _F32, dev, (B, N + 1, V)), _ptr(draft_tokens, "draft_tokens", _I32, dev, (B, N)),
+        _ptr(inv_map, "inv_map", _I32, dev, (V,)), _ptr(verify_len, "verify_len", _I32, dev, (B,)),
+        _ptr(temperature, "temperature", _F32, dev, (B,)), _ptr(request_id, "request_id", _U32, dev, (B,)), seed,
+        _ptr(accepted, "accepted", _I32, dev, (B,)), _ptr(out_tokens, "out_tokens", _I32, dev, (B, N + 1)),
+        B, N, V, Vd, ws.data_ptr(), ws.numel(), _stream(target)))
     return accepted, out_tokens
 
 

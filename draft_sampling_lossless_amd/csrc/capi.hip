@@ -177,6 +177,40 @@ dspark_status dspark_verify(int input_kind, const float* target, const float* dr
                     "verify");
 }
 
+size_t dspark_verify_coupled_workspace_size(int B, int N, int V) {
+  if (B <= 0 || N <= 0 || V <= 0) return 0;
+  return dspark::coupled_workspace_bytes(B, N, V);
+}
+
+dspark_status dspark_verify_coupled(const float* target_logits, const int32_t* draft_tokens, const int32_t* inv_map,
+                                    const int32_t* verify_len, const float* temperature, const uint32_t* request_id,
+                                    uint64_t seed, int32_t* accepted, int32_t* out_tokens, int B, int N, int V, int Vd,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);
+  REQUIRE(B <= DSPARK_MAX_B, DSPARK_ERR_UNSUPPORTED, "B must be <= %d (got %d)", DSPARK_MAX_B, B);
+  REQUIRE(N >= 1, DSPARK_ERR_INVALID, "N must be >= 1 (got %d)", N);
+  REQUIRE(N <= DSPARK_MAX_N, DSPARK_ERR_UNSUPPORTED, "N must be <= %d (got %d)", DSPARK_MAX_N, N);
+  REQUIRE(V > 0 && V % 4 == 0, DSPARK_ERR_INVALID, "V must be a positive multiple of 4 (got %d)", V);
+  REQUIRE(Vd > 0 && Vd <= V, DSPARK_ERR_INVALID, "Vd must be in [1, V] (got %d)", Vd);
+  REQUIRE((int64_t)B * (N + 1) * V < ((int64_t)1 << 40), DSPARK_ERR_UNSUPPORTED, "B * (N+1) * V too large");
+  REQUIRE_PTR16(target_logits, "target_logits");
+  REQUIRE_PTR(draft_tokens, "draft_tokens");
+  if (Vd != V) REQUIRE_PTR16(inv_map, "inv_map (required when Vd != V)");
+  REQUIRE_PTR(temperature, "temperature");
+  REQUIRE_PTR(request_id, "request_id");
+  REQUIRE_PTR(accepted, "accepted");
+  REQUIRE_PTR(out_tokens, "out_tokens");
+  const size_t need = dspark_verify_coupled_workspace_size(B, N, V);
+  REQUIRE(workspace != nullptr, DSPARK_ERR_WORKSPACE, "workspace must not be NULL (%zu bytes needed)", need);
+  REQUIRE(aligned16(workspace), DSPARK_ERR_INVALID, "workspace must be 16-byte aligned");
+  REQUIRE(workspace_bytes >= need, DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
+          need);
+  return hip_status(dspark::launch_verify_coupled(target_logits, draft_tokens, Vd != V ? inv_map : nullptr,
+                                                  verify_len, temperature, request_id, seed, accepted, out_tokens,
+                                                  B, N, V, workspace, (hipStream_t)stream),
+                    "verify_coupled");
+}
+
 dspark_status dspark_admit(const float* cond_accept, int B, int N, int K, float* survival, int32_t* admit_len,
                            void* stream) {
   REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);

@@ -65,6 +65,13 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
                          int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
                          hipStream_t stream);
 
+// ---- Gumbel-coupled verification
+size_t coupled_workspace_bytes(int B, int N, int V);
+hipError_t launch_verify_coupled(const float* target, const int32_t* draft_tokens, const int32_t* inv_map,
+                                 const int32_t* verify_len, const float* temperature, const uint32_t* request_id,
+                                 uint64_t seed, int32_t* accepted, int32_t* out_tokens, int B, int N, int V,
+                                 void* workspace, hipStream_t stream);
+
 // ---- stage 4
 hipError_t launch_admit(const float* cond_accept, int B, int N, int K, float* survival, int32_t* admit_len,
                         hipStream_t stream);

@@ -199,6 +199,36 @@ dspark_status dspark_verify(int input_kind, const float* target, const float* dr
                             int B, int N, int V, int Vd,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- stage 3, coupled
+ * Gumbel-coupled verification [P1 §5: the target verifies with the same Gumbel seed
+ * the draft sampled with, so the output distribution is unchanged].  No draft
+ * probabilities are used; the draft tokens must come from dspark_markov_sample with
+ * the same seed and request ids.  Request b with L = verify_len[b] (N when NULL):
+ *   row k <= L:  y_k = argmax_v l_t[k](v) / T + G_k(v) (T == 0: argmax l_t[k]),
+ *                ties to the smaller v, where G_k(v) is the Gumbel variate stage 2
+ *                drew for the draft entry j that is target id v (u(seed, j, k,
+ *                request_id[b], 0)), and u(seed, v, k, request_id[b], 4) for an id
+ *                outside the draft vocabulary;
+ *   a = the first k < L with y_k != x_k, else L;
+ *   accepted[b] = a; out_tokens[b, :] = x_0 .. x_{a-1}, y_a, then -1 up to column N.
+ * Every emitted token is a Gumbel-max draw from softmax(l_t / T).  Keys are formed
+ * in float32 in base-2 units, as stage 2 forms them (the same argmax up to rounding).
+ *   target_logits [B, N+1, V] float32, device, 16-byte aligned; rows k <= L are read.
+ *   draft_tokens [B, N] int32 target ids; inv_map [V] int32 (16-byte aligned),
+ *            NULL iff Vd == V; verify_len [B] int32 in [0, N] or NULL;
+ *   temperature [B] float32 >= 0; request_id [B] uint32; accepted [B] int32 out;
+ *   out_tokens [B, N+1] int32 out; all device.
+ *   1 <= B <= DSPARK_MAX_B, 1 <= N <= DSPARK_MAX_N, V % 4 == 0, 1 <= Vd <= V.
+ *   workspace >= dspark_verify_coupled_workspace_size(B, N, V) bytes, device, 16-byte aligned.
+ */
+size_t dspark_verify_coupled_workspace_size(int B, int N, int V);
+dspark_status dspark_verify_coupled(const float* target_logits, const int32_t* draft_tokens,
+                                    const int32_t* inv_map, const int32_t* verify_len,
+                                    const float* temperature, const uint32_t* request_id,
+                                    uint64_t seed, int32_t* accepted, int32_t* out_tokens,
+                                    int B, int N, int V, int Vd,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- stage 4
  * Confidence-scheduled admission [P2 §6 (chain rule, pooled greedy sort), §7 (K fixed
  * ahead, sort at the last moment, non-anticipation)]:

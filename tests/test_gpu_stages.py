@@ -380,3 +380,56 @@ def test_admit_bit_exact(B, N, K):
     ref = stages.admit(c, K)
     assert np.array_equal(host(surv).view(np.uint32), ref["survival"].view(np.uint32))
     assert np.array_equal(host(L), ref["admit_len"])
+
+
+# ---------------------------------------------------------------- next rows: coupled verify
+
+def _compare_coupled(acc, out, ref, gap_tol=1e-4):
+    """Identical results, except where the oracle's decisive row was a near-tie."""
+    near = 0
+    for b in range(len(acc)):
+        if acc[b] == ref["accepted"][b] and np.array_equal(out[b], ref["out_tokens"][b]):
+            continue
+        k = min(int(acc[b]), int(ref["accepted"][b]))   # the first row the two read differently
+        assert ref["gap"][b, k] <= gap_tol, (
+            f"request {b}: gpu accepted={acc[b]} out={out[b].tolist()} vs oracle accepted={ref['accepted'][b]} "
+            f"out={ref['out_tokens'][b].tolist()} (row {k} gap {ref['gap'][b, k]:.3g})")
+        near += 1
+    return near
+
+
+@pytest.mark.parametrize("B,N,V,Vd,temps", [(64, 6, 1024, 1024, (0.0, 0.7, 1.0)), (40, 8, 2048, 1000, (0.0, 1.0)),
+                                            (4, 8, 151936, 151936, (1.0,)), (3, 1, 64, 64, (0.8,))])
+def test_verify_coupled_parity(B, N, V, Vd, temps):
+    say(f"verify coupled B={B} N={N} V={V} Vd={Vd} T={temps}")
+    c = _verify_inputs(B, N, V, Vd, temps, seed=B + 3 * N, reduced=Vd != V)
+    seed = 0x5EED
+    acc, out = dsl.verify_coupled(dev(c["tgt"]), dev(c["tok"]), None if c["inv"] is None else dev(c["inv"]),
+                                  dev(c["L"]), dev(c["temp"]), dev(c["rid"]), seed, Vd=Vd)
+    ref = stages.verify_coupled(c["tgt"], c["tok"], c["inv"], c["L"], c["temp"], c["rid"], seed)
+    near = _compare_coupled(host(acc), host(out), ref)
+    say(f"  {near} near-tie requests of {B}, accepted mean {host(acc).mean():.2f}")
+    assert near <= max(1, B // 50)
+
+
+@pytest.mark.parametrize("Vd", [2048, 1000])
+def test_verify_coupled_accepts_stage2_drafts(Vd):
+    # drafts from the GPU Markov sampler, target rows equal to its processed logits:
+    # under the shared noise the target draws the drafted tokens
+    B, N, V, r = 24, 6, 2048, 64
+    d2t = None
+    if Vd != V:
+        g = np.random.default_rng(4)
+        d2t = (g.permutation(V)[:Vd] - np.arange(Vd)).astype(np.int64)
+    c = _markov_case(B, N, V, Vd, r, (0.7, 1.0), seed=0x77, d2t=d2t)
+    tok, proc, logz = _run_markov_gpu(c)
+    t_of_j = np.arange(Vd) + (0 if d2t is None else d2t)
+    tgt = np.full((B, N + 1, V), -np.inf, np.float32)
+    tgt[:, :N, t_of_j] = proc
+    tgt[:, N] = np.random.default_rng(5).normal(size=(B, V)).astype(np.float32)
+    inv = None if d2t is None else stages.build_inverse_map(d2t, Vd, V)
+    acc, out = dsl.verify_coupled(dev(tgt), dev(tok), None if inv is None else dev(inv), None, dev(c["temp"]),
+                                  dev(c["rid"]), c["seed"], Vd=Vd)
+    acc = host(acc)
+    say(f"  accepted {np.count_nonzero(acc == N)} of {B} requests in full")
+    assert (acc == N).all()
