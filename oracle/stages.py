@@ -26,6 +26,9 @@ Next rows:
                          the draft sampled with: y_k = Gumbel-max sample of the
                          target row under the draft's noise; accept while y_k ==
                          x_k; the first mismatch (or the bonus row) emits y.
+  choose_k               [P2 §6, §7]: the verification budget K that maximises
+                         expected tokens per batch times the engine's steps per
+                         second at that batch size, by a full scan.
 
 Readings where the pages are silent (the same readings hold on the GPU side):
   * temperature T > 0 divides the logits; T = 0 means greedy (argmax, no
@@ -399,3 +402,42 @@ def admit(cond_accept, K: int) -> Dict[str, np.ndarray]:
     admitted[take] = True
     admit_len = admitted.reshape(B, N).sum(axis=1).astype(np.int32)
     return {"survival": s, "admit_len": admit_len, "admitted": admitted.reshape(B, N)}
+
+
+# ---------------------------------------------------------------- next rows: budget K
+
+def choose_k(survival, sps, B: Optional[int] = None) -> Dict[str, object]:
+    """Throughput-optimal verification budget [P2 §6: maximise expected tokens per
+    batch times SPS at that batch size; pool every request's candidates and admit
+    by survival; P2 §7: the SPS curve is jagged, so the search does not stop early].
+
+    survival [B, N] fp32 (stage 4's running products: non-increasing along k);
+    sps [S] steps per second of the target engine at a batch of n tokens, n = 0..S-1.
+    Readings: admitting the K best candidates costs a batch of B + K tokens (every
+    request verifies its current position plus its admitted drafts) and yields
+    B + (sum of their survival) expected tokens (every request emits one token
+    beyond its accepted drafts; a draft's survival is the probability it is
+    accepted).  objective(K) = (B + S_K) * sps[B + K] with S_K the sum of the K
+    largest survivals (fp64, sequential over the sorted values); K ranges over
+    0 .. min(B*N, S - 1 - B); the smallest K of the largest objective wins.
+
+    Returns k (int), objective (fp64), objectives [fp64 per K].
+    Pins: brute force over all prefix-closed admission sets on tiny inputs; a flat
+    SPS admits every candidate; an SPS that is zero past a capacity never exceeds
+    it; a jagged SPS whose first local maximum is not the global one.
+    """
+    s = np.asarray(survival, dtype=np.float32).astype(np.float64)
+    Bq = s.shape[0] if B is None else int(B)
+    flat = np.sort(s.ravel())[::-1]
+    sps = np.asarray(sps, dtype=np.float64)
+    kmax = min(flat.size, sps.size - 1 - Bq)
+    if kmax < 0:
+        raise ValueError("the SPS table does not reach the batch of B tokens")
+    prefix = 0.0
+    obj = np.empty(kmax + 1)
+    for K in range(kmax + 1):
+        if K > 0:
+            prefix += flat[K - 1]
+        obj[K] = (Bq + prefix) * sps[Bq + K]
+    k = int(np.argmax(obj))                        # the first maximum: the smallest K
+    return {"k": k, "objective": float(obj[k]), "objectives": obj}

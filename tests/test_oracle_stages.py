@@ -436,3 +436,59 @@ def test_coupled_verify_acceptance_at_most_one_minus_tv():
     alpha = stages.accept_prob(stages.probs_from_logits(trow, 1.0), stages.probs_from_logits(base[0, 0], 1.0))
     assert rate <= alpha + 4 * math.sqrt(alpha * (1 - alpha) / B)
     assert rate > 0.5 * alpha                          # and it is a real coupling, not independence
+
+
+# ---------------------------------------------------------------- next rows: budget K
+
+def _survival(B, N, g):
+    c = g.uniform(0.3, 1.0, size=(B, N)).astype(np.float32)
+    s = np.empty_like(c)
+    s[:, 0] = c[:, 0]
+    for k in range(1, N):
+        s[:, k] = (s[:, k - 1] * c[:, k]).astype(np.float32)
+    return s
+
+
+def test_choose_k_brute_force_over_prefix_sets():
+    import itertools
+    g = np.random.default_rng(31)
+    for trial in range(20):
+        B, N = int(g.integers(1, 4)), int(g.integers(1, 4))
+        s = _survival(B, N, g)
+        sps = g.uniform(0.2, 1.0, size=B * N + B + 2)
+        best = -1.0
+        best_k = None
+        for lens in itertools.product(range(N + 1), repeat=B):
+            K = sum(lens)
+            val = (B + sum(float(s[b, :lens[b]].astype(np.float64).sum()) for b in range(B))) * sps[B + K]
+            if val > best + 1e-12 or (abs(val - best) <= 1e-12 and K < best_k):
+                best, best_k = val, K
+        r = stages.choose_k(s, sps)
+        assert abs(r["objective"] - best) <= 1e-12 * max(1.0, best)
+        assert r["k"] == best_k
+
+
+def test_choose_k_flat_sps_admits_everything():
+    g = np.random.default_rng(3)
+    s = _survival(5, 6, g)
+    r = stages.choose_k(s, np.ones(100))
+    assert r["k"] == 30
+
+
+def test_choose_k_respects_a_capacity():
+    g = np.random.default_rng(4)
+    s = _survival(8, 8, g)
+    sps = np.ones(100)
+    sps[8 + 21:] = 0.0                                 # a batch above 28 tokens never runs
+    assert stages.choose_k(s, sps)["k"] == 20
+
+
+def test_choose_k_scans_past_a_local_maximum():
+    s = np.full((4, 8), 0.9, np.float32)               # 32 equally good candidates
+    n = np.arange(64, dtype=np.float64)
+    sps = np.where(n <= 12, 1.0, 0.5)                  # a cliff after 8 drafts ...
+    sps[20:37] = 0.9                                   # ... then a plateau (a tile boundary)
+    r = stages.choose_k(s, sps)
+    obj = r["objectives"]
+    first_local = next(k for k in range(1, obj.size - 1) if obj[k] >= obj[k - 1] and obj[k] > obj[k + 1])
+    assert first_local == 8 and r["k"] == 32 and obj[32] > obj[8]
