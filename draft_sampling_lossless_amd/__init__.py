@@ -52,6 +52,7 @@ _SIGS = {
     "dspark_verify_coupled_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
     "dspark_verify_coupled": (_c_int, [_c_void_p] * 6 + [_c_u64, _c_void_p, _c_void_p] + [_c_int] * 4
                               + [_c_void_p, _c_size, _c_void_p]),
+    "dspark_choose_k": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "dspark_admit": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
 }
 
@@ -264,6 +265,23 @@ def verify_coupled(target: torch.Tensor, draft_tokens: torch.Tensor, inv_map: Op
         _ptr(accepted, "accepted", _I32, dev, (B,)), _ptr(out_tokens, "out_tokens", _I32, dev, (B, N + 1)),
         B, N, V, Vd, ws.data_ptr(), ws.numel(), _stream(target)))
     return accepted, out_tokens
+
+
+def choose_k(survival: torch.Tensor, sps: torch.Tensor, k_out: Optional[torch.Tensor] = None,
+             objective_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Throughput-optimal budget.  survival [B, N] float32, sps [S] float32.
+    Returns (K [1] int32, objective [1] float64), both on the device."""
+    B, N = survival.shape
+    dev = survival.device
+    if k_out is None:
+        k_out = torch.empty(1, dtype=torch.int32, device=dev)
+    if objective_out is None:
+        objective_out = torch.empty(1, dtype=torch.float64, device=dev)
+    _check("dspark_choose_k", load().dspark_choose_k(
+        _ptr(survival, "survival", _F32, dev, (B, N)), B, N, _ptr(sps, "sps", _F32, dev), sps.numel(),
+        _ptr(k_out, "k_out", _I32, dev, (1,)), _ptr(objective_out, "objective_out", (torch.float64,), dev, (1,)),
+        _stream(survival)))
+    return k_out, objective_out
 
 
 # ---------------------------------------------------------------- stage 4

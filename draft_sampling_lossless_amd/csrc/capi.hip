@@ -226,4 +226,21 @@ dspark_status dspark_admit(const float* cond_accept, int B, int N, int K, float*
   return hip_status(dspark::launch_admit(cond_accept, B, N, K, survival, admit_len, (hipStream_t)stream), "admit");
 }
 
+dspark_status dspark_choose_k(const float* survival, int B, int N, const float* sps, int S, int32_t* k_out,
+                              double* objective_out, void* stream) {
+  REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);
+  REQUIRE(N >= 1, DSPARK_ERR_INVALID, "N must be >= 1 (got %d)", N);
+  REQUIRE(N <= DSPARK_MAX_N, DSPARK_ERR_UNSUPPORTED, "N must be <= %d (got %d)", DSPARK_MAX_N, N);
+  REQUIRE(B <= DSPARK_MAX_B, DSPARK_ERR_UNSUPPORTED, "B must be <= %d (got %d)", DSPARK_MAX_B, B);
+  REQUIRE((int64_t)B * N <= DSPARK_MAX_ADMIT, DSPARK_ERR_UNSUPPORTED, "B * N must be <= %d (got %lld)",
+          DSPARK_MAX_ADMIT, (long long)B * N);
+  REQUIRE(S >= B + 1, DSPARK_ERR_INVALID, "the SPS table must cover a batch of B tokens: S >= B + 1 (got S=%d, B=%d)",
+          S, B);
+  REQUIRE_PTR(survival, "survival");
+  REQUIRE_PTR(sps, "sps");
+  REQUIRE_PTR(k_out, "k_out");
+  return hip_status(dspark::launch_choose_k(survival, B, N, sps, S, k_out, objective_out, (hipStream_t)stream),
+                    "choose_k");
+}
+
 }  // extern "C"

@@ -72,6 +72,10 @@ hipError_t launch_verify_coupled(const float* target, const int32_t* draft_token
                                  uint64_t seed, int32_t* accepted, int32_t* out_tokens, int B, int N, int V,
                                  void* workspace, hipStream_t stream);
 
+// ---- verification budget
+hipError_t launch_choose_k(const float* survival, int B, int N, const float* sps, int S, int32_t* k_out,
+                           double* obj_out, hipStream_t stream);
+
 // ---- stage 4
 hipError_t launch_admit(const float* cond_accept, int B, int N, int K, float* survival, int32_t* admit_len,
                         hipStream_t stream);

@@ -244,6 +244,25 @@ dspark_status dspark_verify_coupled(const float* target_logits, const int32_t* d
 dspark_status dspark_admit(const float* cond_accept, int B, int N, int K, float* survival,
                            int32_t* admit_len, void* stream);
 
+/* ---------------------------------------------------------------- verification budget
+ * Throughput-optimal budget K [P2 §6 (maximise expected tokens per batch times SPS at
+ * that batch size; pool all requests' candidates, admit by survival), §7 (the SPS
+ * curve is jagged: scan every K; K is fixed from earlier scores)]:
+ *   objective(K) = (B + S_K) * sps[B + K], S_K = sum of the K largest survival values
+ *   (fp64), for K = 0 .. min(B*N, S-1-B); *k_out = the smallest K with the largest
+ *   objective, *objective_out = that objective (optional).
+ * Readings: a batch holds B + K tokens (each request's current position plus its
+ * admitted drafts) and yields B + S_K tokens in expectation.  The prefix sums are
+ * taken in a parallel order, so K can differ from a sequential sum only where two
+ * objectives agree to about 1e-15 relative.
+ *   survival [B, N] float32 (dspark_admit's output of an earlier round), device;
+ *   sps [S] float32 steps per second at a batch of n tokens, n = 0 .. S-1, device;
+ *   k_out [1] int32, objective_out [1] double or NULL, device.
+ *   B * N <= DSPARK_MAX_ADMIT, S >= B + 1.
+ */
+dspark_status dspark_choose_k(const float* survival, int B, int N, const float* sps, int S,
+                              int32_t* k_out, double* objective_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -235,6 +235,20 @@ def confidence(w: Workload) -> np.ndarray:
     return c.astype(np.float32)
 
 
+def sps_table(max_tokens: int, seed: int = 0, tile: int = 64, knee: int = 256) -> np.ndarray:
+    """Synthetic steps-per-second curve of a target engine, sps[n] for a batch of n
+    tokens (n = 0 .. max_tokens).  The pages give no table, only its shape: flat
+    while the forward pass is bandwidth-bound, then falling once it is
+    compute-bound, jagged at kernel tile boundaries.  Step time here: 10 ms up to
+    the knee, then +1.2 ms per extra tile of `tile` tokens, times a seeded +-3%
+    ripple per tile.  Returned as float32."""
+    n = np.arange(max_tokens + 1)
+    tiles = np.maximum(0, np.ceil(n / tile) * tile - knee) / tile
+    ripple = 1.0 + 0.03 * np.random.default_rng([seed, 77]).uniform(-1, 1, size=int(np.ceil((max_tokens + 1) / tile)) + 1)
+    step_ms = (10.0 + 1.2 * tiles) * ripple[n // tile]
+    return (1000.0 / step_ms).astype(np.float32)
+
+
 def generate(w: Workload, big: bool = True) -> Dict[str, object]:
     """All inputs of a workload (weights included when ``big``)."""
     out: Dict[str, object] = {"workload": w}

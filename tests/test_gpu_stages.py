@@ -433,3 +433,31 @@ def test_verify_coupled_accepts_stage2_drafts(Vd):
     acc = host(acc)
     say(f"  accepted {np.count_nonzero(acc == N)} of {B} requests in full")
     assert (acc == N).all()
+
+
+# ---------------------------------------------------------------- next rows: verification budget
+
+@pytest.mark.parametrize("B,N,knee", [(1, 8, 4), (64, 8, 256), (256, 16, 1024), (1024, 16, 4096), (3, 5, 8)])
+def test_choose_k_parity(B, N, knee):
+    say(f"choose_k B={B} N={N} knee={knee}")
+    g = np.random.default_rng(B * 31 + N)
+    c = (1.0 / (1.0 + np.exp(-g.normal(1.5, 1.0, size=(B, N))))).astype(np.float32)
+    surv = stages.admit(np.minimum.accumulate(c, axis=1), 0)["survival"]
+    sps = synth.sps_table(B * N + B + 64, seed=B, tile=max(1, knee // 4), knee=knee)
+    k, obj = dsl.choose_k(dev(surv), dev(sps))
+    k, obj = int(host(k)[0]), float(host(obj)[0])
+    ref = stages.choose_k(surv, sps)
+    objs = ref["objectives"]
+    say(f"  gpu K={k} oracle K={ref['k']} objective {obj:.6g}")
+    assert abs(objs[k] - ref["objective"]) <= 1e-12 * ref["objective"]   # an optimal K (near-ties aside)
+    assert abs(obj - objs[k]) <= 1e-12 * objs[k]
+    assert k == ref["k"] or abs(objs[k] - objs[ref["k"]]) <= 1e-12 * objs[k]
+
+
+def test_choose_k_scans_past_a_local_maximum_on_gpu():
+    s = np.full((4, 8), 0.9, np.float32)
+    n = np.arange(64)
+    sps = np.where(n <= 12, 1.0, 0.5).astype(np.float32)
+    sps[20:37] = 0.9
+    k, _ = dsl.choose_k(dev(s), dev(sps))
+    assert int(host(k)[0]) == stages.choose_k(s, sps)["k"] == 32
