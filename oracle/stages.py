@@ -29,6 +29,10 @@ Next rows:
   choose_k               [P2 §6, §7]: the verification budget K that maximises
                          expected tokens per batch times the engine's steps per
                          second at that batch size, by a full scan.
+  confidence_head        [P2 §6]: a linear projection of the backbone hidden
+                         state and the Markov embedding of the previous token,
+                         temperature-scaled per position, through a sigmoid:
+                         each position's conditional acceptance probability.
 
 Readings where the pages are silent (the same readings hold on the GPU side):
   * temperature T > 0 divides the logits; T = 0 means greedy (argmax, no
@@ -441,3 +445,38 @@ def choose_k(survival, sps, B: Optional[int] = None) -> Dict[str, object]:
         obj[K] = (Bq + prefix) * sps[Bq + K]
     k = int(np.argmax(obj))                        # the first maximum: the smallest K
     return {"k": k, "objective": float(obj[k]), "objectives": obj}
+
+
+# ---------------------------------------------------------------- next rows: confidence head
+
+def confidence_head(hidden_bits, w1_bits, draft_tokens, anchor, w_bits, bias: float, tau) -> np.ndarray:
+    """Per-position conditional acceptance probability [P2 §6: a linear projection
+    of the backbone hidden state plus the Markov embedding, calibrated by a
+    per-position temperature].
+
+    hidden_bits [B*N, H] bf16 (row b*N + k, the stage-1 input); w1_bits [V, r] bf16;
+    draft_tokens [B, N] target ids; anchor [B]; w_bits [H + r] bf16 (the first H
+    weights act on the hidden state, the last r on the embedding); bias fp32;
+    tau [N] fp32 > 0.  Position k of request b uses the embedding of its previous
+    token (k = 0: the anchor, the same token stage 2 starts from):
+        z = w[:H] . h[b*N + k] + w[H:] . W1[x_{k-1}] + bias        (fp64)
+        c[b, k] = fp32(1 / (1 + exp(-z / tau[k])))
+    Pins: w = 0 gives sigmoid(bias / tau) (0.5 at bias 0); logit(c) * tau does not
+    depend on tau; x_k moves c[k+1] only and the anchor c[0] only; the logit is
+    affine in h.
+    """
+    h = bf16_decode(hidden_bits)
+    w = bf16_decode(w_bits)
+    x = np.asarray(draft_tokens, dtype=np.int64)
+    B, N = x.shape
+    H = h.shape[1]
+    w1 = np.asarray(w1_bits)
+    tau = np.asarray(tau, dtype=np.float32).astype(np.float64)
+    c = np.empty((B, N), dtype=np.float32)
+    for b in range(B):
+        for k in range(N):
+            prev = int(anchor[b]) if k == 0 else int(x[b, k - 1])
+            e = bf16_decode(w1[prev])
+            z = float(w[:H] @ h[b * N + k]) + float(w[H:] @ e) + float(np.float32(bias))
+            c[b, k] = np.float32(1.0 / (1.0 + math.exp(-z / tau[k])))
+    return c

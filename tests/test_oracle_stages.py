@@ -492,3 +492,58 @@ def test_choose_k_scans_past_a_local_maximum():
     obj = r["objectives"]
     first_local = next(k for k in range(1, obj.size - 1) if obj[k] >= obj[k - 1] and obj[k] > obj[k + 1])
     assert first_local == 8 and r["k"] == 32 and obj[32] > obj[8]
+
+
+# ---------------------------------------------------------------- next rows: confidence head
+
+def _conf_case(B=3, N=4, H=32, V=20, r=8, seed=0):
+    g = np.random.default_rng(seed)
+    return dict(h=synth.bf16_bits(g.normal(size=(B * N, H)).astype(np.float32)),
+                w1=synth.bf16_bits(g.normal(size=(V, r)).astype(np.float32)),
+                x=g.integers(0, V, size=(B, N)).astype(np.int32), anchor=g.integers(0, V, size=B).astype(np.int32),
+                w=synth.bf16_bits(g.normal(0, 0.3, size=H + r).astype(np.float32)),
+                tau=g.uniform(0.5, 2.0, size=N).astype(np.float32))
+
+
+def test_confidence_zero_weights_is_sigmoid_of_bias():
+    c = _conf_case()
+    zero = synth.bf16_bits(np.zeros(c["w"].shape, np.float32))
+    out = stages.confidence_head(c["h"], c["w1"], c["x"], c["anchor"], zero, 0.0, c["tau"])
+    assert (out == np.float32(0.5)).all()
+    out = stages.confidence_head(c["h"], c["w1"], c["x"], c["anchor"], zero, 1.5, np.ones(4, np.float32))
+    assert np.allclose(out, 1.0 / (1.0 + math.exp(-1.5)), rtol=0, atol=1e-7)
+
+
+def test_confidence_temperature_scales_the_logit():
+    c = _conf_case(seed=1)
+    a = stages.confidence_head(c["h"], c["w1"], c["x"], c["anchor"], c["w"], 0.2, np.ones(4, np.float32))
+    b = stages.confidence_head(c["h"], c["w1"], c["x"], c["anchor"], c["w"], 0.2, np.full(4, 2.0, np.float32))
+    la, lb = np.log(a / (1 - a)), np.log(b / (1 - b))
+    assert np.allclose(lb * 2.0, la, atol=1e-5)
+
+
+def test_confidence_uses_the_previous_token():
+    c = _conf_case(seed=2)
+    base = stages.confidence_head(c["h"], c["w1"], c["x"], c["anchor"], c["w"], 0.0, c["tau"])
+    x2 = c["x"].copy()
+    x2[1, 1] = (x2[1, 1] + 7) % 20                      # change x_1 of request 1
+    moved = stages.confidence_head(c["h"], c["w1"], x2, c["anchor"], c["w"], 0.0, c["tau"]) != base
+    assert moved[1, 2] and moved.sum() == 1             # only position 2 of that request
+    a2 = c["anchor"].copy()
+    a2[0] = (a2[0] + 3) % 20
+    moved = stages.confidence_head(c["h"], c["w1"], c["x"], a2, c["w"], 0.0, c["tau"]) != base
+    assert moved[0, 0] and moved.sum() == 1
+
+
+def test_confidence_logit_is_affine_in_hidden():
+    c = _conf_case(seed=3, B=1, N=1, H=16, r=4)
+    g = np.random.default_rng(9)
+    h1 = g.integers(-4, 5, size=(1, 16)).astype(np.float32)   # small integers: exact in bf16 and sums
+    h2 = g.integers(-4, 5, size=(1, 16)).astype(np.float32)
+    tau = np.ones(1, np.float32)
+
+    def logit(h):
+        p = stages.confidence_head(synth.bf16_bits(h), c["w1"], c["x"], c["anchor"], c["w"], 0.0, tau)
+        return math.log(p[0, 0] / (1 - p[0, 0]))
+    zero = logit(np.zeros((1, 16), np.float32))
+    assert abs((logit(h1 + h2) - zero) - ((logit(h1) - zero) + (logit(h2) - zero))) < 1e-4
