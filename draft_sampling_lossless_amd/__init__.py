@@ -52,6 +52,7 @@ _SIGS = {
     "dspark_verify_coupled_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
     "dspark_verify_coupled": (_c_int, [_c_void_p] * 6 + [_c_u64, _c_void_p, _c_void_p] + [_c_int] * 4
                               + [_c_void_p, _c_size, _c_void_p]),
+    "dspark_confidence": (_c_int, [_c_void_p] * 5 + [ctypes.c_float] + [_c_void_p] * 2 + [_c_int] * 5 + [_c_void_p]),
     "dspark_choose_k": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "dspark_admit": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
 }
@@ -265,6 +266,23 @@ def verify_coupled(target: torch.Tensor, draft_tokens: torch.Tensor, inv_map: Op
         _ptr(accepted, "accepted", _I32, dev, (B,)), _ptr(out_tokens, "out_tokens", _I32, dev, (B, N + 1)),
         B, N, V, Vd, ws.data_ptr(), ws.numel(), _stream(target)))
     return accepted, out_tokens
+
+
+def confidence(hidden: torch.Tensor, w1: torch.Tensor, draft_tokens: torch.Tensor, anchor: torch.Tensor,
+               w: torch.Tensor, bias: float, tau: torch.Tensor, c_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Confidence head.  hidden [B*N, H] bf16, w1 [V, r] bf16, w [H + r] bf16, tau [N].  Returns c [B, N]."""
+    B, N = draft_tokens.shape
+    H = hidden.shape[1]
+    V, r = w1.shape
+    dev = hidden.device
+    if c_out is None:
+        c_out = torch.empty((B, N), dtype=torch.float32, device=dev)
+    _check("dspark_confidence", load().dspark_confidence(
+        _ptr(hidden, "hidden", _BF16, dev, (B * N, H)), _ptr(w1, "w1", _BF16, dev, (V, r)),
+        _ptr(draft_tokens, "draft_tokens", _I32, dev, (B, N)), _ptr(anchor, "anchor", _I32, dev, (B,)),
+        _ptr(w, "w", _BF16, dev, (H + r,)), float(bias), _ptr(tau, "tau", _F32, dev, (N,)),
+        _ptr(c_out, "c_out", _F32, dev, (B, N)), B, N, H, V, r, _stream(hidden)))
+    return c_out
 
 
 def choose_k(survival: torch.Tensor, sps: torch.Tensor, k_out: Optional[torch.Tensor] = None,

@@ -3,6 +3,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <cmath>
+
 #include "dspark.h"
 #include "kernels.hpp"
 
@@ -224,6 +226,28 @@ dspark_status dspark_admit(const float* cond_accept, int B, int N, int K, float*
   REQUIRE_PTR(survival, "survival");
   REQUIRE_PTR(admit_len, "admit_len");
   return hip_status(dspark::launch_admit(cond_accept, B, N, K, survival, admit_len, (hipStream_t)stream), "admit");
+}
+
+dspark_status dspark_confidence(const uint16_t* hidden, const uint16_t* w1, const int32_t* draft_tokens,
+                                const int32_t* anchor, const uint16_t* w, float bias, const float* tau,
+                                float* c_out, int B, int N, int H, int V, int r, void* stream) {
+  REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);
+  REQUIRE(B <= DSPARK_MAX_B, DSPARK_ERR_UNSUPPORTED, "B must be <= %d (got %d)", DSPARK_MAX_B, B);
+  REQUIRE(N >= 1 && N <= DSPARK_MAX_N, DSPARK_ERR_INVALID, "N must be in [1, %d] (got %d)", DSPARK_MAX_N, N);
+  REQUIRE(H > 0 && H % 8 == 0, DSPARK_ERR_INVALID, "H must be a positive multiple of 8 (got %d)", H);
+  REQUIRE(r >= 8 && r % 8 == 0, DSPARK_ERR_INVALID, "r must be a positive multiple of 8 (got %d)", r);
+  REQUIRE(V > 0, DSPARK_ERR_INVALID, "V must be positive (got %d)", V);
+  REQUIRE(std::isfinite(bias), DSPARK_ERR_INVALID, "bias must be finite");
+  REQUIRE_PTR16(hidden, "hidden");
+  REQUIRE_PTR16(w1, "w1");
+  REQUIRE_PTR(draft_tokens, "draft_tokens");
+  REQUIRE_PTR(anchor, "anchor");
+  REQUIRE_PTR16(w, "w");
+  REQUIRE_PTR(tau, "tau");
+  REQUIRE_PTR(c_out, "c_out");
+  return hip_status(dspark::launch_confidence(hidden, w1, draft_tokens, anchor, w, bias, tau, c_out, B, N, H, V, r,
+                                              (hipStream_t)stream),
+                    "confidence");
 }
 
 dspark_status dspark_choose_k(const float* survival, int B, int N, const float* sps, int S, int32_t* k_out,

@@ -72,6 +72,11 @@ hipError_t launch_verify_coupled(const float* target, const int32_t* draft_token
                                  uint64_t seed, int32_t* accepted, int32_t* out_tokens, int B, int N, int V,
                                  void* workspace, hipStream_t stream);
 
+// ---- confidence head
+hipError_t launch_confidence(const uint16_t* hidden, const uint16_t* w1, const int32_t* draft_tokens,
+                             const int32_t* anchor, const uint16_t* w, float bias, const float* tau, float* c_out,
+                             int B, int N, int H, int V, int r, hipStream_t stream);
+
 // ---- verification budget
 hipError_t launch_choose_k(const float* survival, int B, int N, const float* sps, int S, int32_t* k_out,
                            double* obj_out, hipStream_t stream);

@@ -244,6 +244,22 @@ dspark_status dspark_verify_coupled(const float* target_logits, const int32_t* d
 dspark_status dspark_admit(const float* cond_accept, int B, int N, int K, float* survival,
                            int32_t* admit_len, void* stream);
 
+/* ---------------------------------------------------------------- confidence head
+ * Conditional acceptance probability of each draft position [P2 §6: a linear
+ * projection of the backbone hidden state plus the Markov embedding, calibrated by
+ * temperature scaling per position]:
+ *   c[b, k] = 1 / (1 + exp(-(w[0:H] . h[b*N + k] + w[H:H+r] . W1[x_{k-1}] + bias) / tau[k]))
+ * with x_{-1} = anchor[b] (the token stage 2 starts from).  Float32 arithmetic.
+ * Its output is dspark_admit's cond_accept.
+ *   hidden [B*N, H] bf16 (the stage-1 input), w1 [V, r] bf16, w [H + r] bf16: device,
+ *            16-byte aligned; draft_tokens [B, N] int32, anchor [B] int32,
+ *            tau [N] float32 > 0, c_out [B, N] float32 out: device.
+ *   H % 8 == 0, r % 8 == 0, bias finite.  Previous tokens are clamped into [0, V).
+ */
+dspark_status dspark_confidence(const uint16_t* hidden, const uint16_t* w1, const int32_t* draft_tokens,
+                                const int32_t* anchor, const uint16_t* w, float bias, const float* tau,
+                                float* c_out, int B, int N, int H, int V, int r, void* stream);
+
 /* ---------------------------------------------------------------- verification budget
  * Throughput-optimal budget K [P2 §6 (maximise expected tokens per batch times SPS at
  * that batch size; pool all requests' candidates, admit by survival), §7 (the SPS

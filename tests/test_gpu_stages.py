@@ -4,6 +4,8 @@ Small cases compare every output; the full Qwen3-8B-shaped workloads compare
 sampled requests / entries (the stages never mix requests, except admission,
 which is always compared in full).
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -461,3 +463,23 @@ def test_choose_k_scans_past_a_local_maximum_on_gpu():
     sps[20:37] = 0.9
     k, _ = dsl.choose_k(dev(s), dev(sps))
     assert int(host(k)[0]) == stages.choose_k(s, sps)["k"] == 32
+
+
+# ---------------------------------------------------------------- next rows: confidence head
+
+@pytest.mark.parametrize("B,N,H,V,r", [(1, 8, 4096, 151936, 64), (64, 8, 4096, 32000, 256), (5, 3, 264, 100, 8),
+                                       (256, 16, 4096, 4096, 64)])
+def test_confidence_parity(B, N, H, V, r):
+    say(f"confidence B={B} N={N} H={H} V={V} r={r}")
+    g = np.random.default_rng(B + N + H)
+    hid = synth.bf16_bits(g.normal(size=(B * N, H)).astype(np.float32))
+    w1 = synth.bf16_bits(g.normal(0, 0.5, size=(V, r)).astype(np.float32))
+    w = synth.bf16_bits(g.normal(0, 1.0 / math.sqrt(H + r), size=H + r).astype(np.float32))
+    tok = g.integers(0, V, size=(B, N)).astype(np.int32)
+    anc = g.integers(0, V, size=B).astype(np.int32)
+    tau = g.uniform(0.7, 1.5, size=N).astype(np.float32)
+    c = host(dsl.confidence(dev(hid), dev(w1), dev(tok), dev(anc), dev(w), 0.3, dev(tau)))
+    ref = stages.confidence_head(hid, w1, tok, anc, w, 0.3, tau)
+    err = np.abs(c.astype(np.float64) - ref).max()
+    say(f"  max abs err {err:.2e}, c in [{ref.min():.3f}, {ref.max():.3f}]")
+    assert err <= 1e-6
