@@ -43,6 +43,10 @@ def parse():
     p.add_argument("--graph", action="store_true", help="replay each step as one captured HIP graph")
     p.add_argument("--verify", default="rejection", choices=("rejection", "coupled"),
                    help="stage 3 rule: rejection sampling on p_t, p_d (default) or Gumbel-coupled verification")
+    p.add_argument("--round", default="path", choices=("path", "full"),
+                   help="path: stages 1-4 with the workload's synthetic confidences and fixed K (default); "
+                        "full: also the confidence head (its output feeds admission) and the throughput-optimal "
+                        "K, computed from this round's survival and used two rounds later")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -58,9 +62,10 @@ def src_hash(path: str) -> str:
 class Path:
     """Device buffers and the four C-ABI calls of one round."""
 
-    def __init__(self, w, torch, dsl, synth, verify_mode="rejection"):
+    def __init__(self, w, torch, dsl, synth, verify_mode="rejection", full_round=False):
         self.w, self.torch, self.dsl = w, torch, dsl
         self.coupled = verify_mode == "coupled"
+        self.full = full_round
         dev = torch.device("cuda:0")
         rp = synth.request_params(w)
 
@@ -112,12 +117,36 @@ class Path:
         else:
             tids = torch.arange(w.Vd, device=dev, dtype=torch.int64) + self.d2t
             self.target[:, :, tids] += self.logits[:, rows]
+        if self.full:
+            # confidence head weights (random, like every weight here): w ~ N(0, 1/(H + r)),
+            # bias 1.5 and per-position temperatures; an SPS table of the target engine
+            g = np.random.default_rng([w.seed, 91])
+            self.wconf = up(synth.bf16_bits(g.normal(0, 1.0 / np.sqrt(w.H + w.r), size=w.H + w.r).astype(np.float32)))
+            self.cbias = 1.5
+            self.tau = up(np.linspace(1.0, 1.6, w.N).astype(np.float32))
+            self.sps = up(synth.sps_table(w.B * w.N + w.B + 64, seed=w.seed, tile=64, knee=max(64, w.B * 4)))
+            self.c_model = torch.empty((w.B, w.N), dtype=torch.float32, device=dev)
+            self.k_dev = torch.empty(1, dtype=torch.int32, device=dev)
+            self.k_obj = torch.empty(1, dtype=torch.float64, device=dev)
+            self.k_host = torch.empty(3, dtype=torch.int32, pin_memory=True)
+            self.k_ready = [torch.cuda.Event() for _ in range(3)]
+            self.round = 0
+            self.K_used = []
         torch.cuda.synchronize()
         self.setup_s = time.time() - t0
         self.ev = None
 
+    def budget(self):
+        """K for this round: fixed, or (full round) the K chosen two rounds ago."""
+        if not self.full or self.round < 2:
+            return self.K
+        slot = (self.round - 2) % 3
+        self.k_ready[slot].synchronize()        # long done: the GPU is at most a round behind
+        return int(self.k_host[slot])
+
     def step(self, events=None):
-        """One round.  events: optional list of 5 torch.cuda.Event bracketing the stages."""
+        """One round.  events: optional list of 5 (7 for a full round) torch.cuda.Event
+        bracketing the stages."""
         w, dsl = self.w, self.dsl
         rec = (lambda i: events[i].record()) if events else (lambda i: None)
         rec(0)
@@ -126,7 +155,16 @@ class Path:
         dsl.markov_sample(self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, self.seed,
                           draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov)
         rec(2)
-        dsl.admit(self.conf, self.K, survival=self.survival, admit_len=self.admit_len)
+        conf = self.conf
+        if self.full:
+            dsl.confidence(self.hidden, self.w1, self.tokens, self.anchor, self.wconf, self.cbias, self.tau,
+                           c_out=self.c_model)
+            conf = self.c_model
+            rec(5)
+        K = self.budget()
+        if self.full:
+            self.K_used.append(K)
+        dsl.admit(conf, K, survival=self.survival, admit_len=self.admit_len)
         rec(3)
         if self.coupled:
             dsl.verify_coupled(self.target, self.tokens, self.inv, self.admit_len, self.temp, self.rid, self.seed,
@@ -137,6 +175,14 @@ class Path:
                        self.admit_len, self.temp, self.rid, self.seed, accepted=self.accepted,
                        out_tokens=self.out_tokens, workspace=self.ws_verify)
         rec(4)
+        if self.full:
+            # the budget of two rounds ahead, from this round's survival
+            dsl.choose_k(self.survival, self.sps, k_out=self.k_dev, objective_out=self.k_obj)
+            slot = self.round % 3
+            self.k_host[slot:slot + 1].copy_(self.k_dev, non_blocking=True)
+            self.k_ready[slot].record()
+            self.round += 1
+            rec(6)
 
 
 def stage_bytes(w, admit_len, coupled):
@@ -264,8 +310,12 @@ def main():
     if not os.path.exists(dsl.LIB_PATH):
         from draft_sampling_lossless_amd import build
         build.build()
+    if args.graph and args.round == "full":
+        print(json.dumps({"error": "--round full chooses K on the host two rounds ahead; it cannot be "
+                                   "replayed as one captured graph"}))
+        sys.exit(2)
     w = synth.get(args.workload)
-    path = Path(w, torch, dsl, synth, args.verify)
+    path = Path(w, torch, dsl, synth, args.verify, args.round == "full")
 
     graph = None
     if args.graph:
@@ -302,14 +352,21 @@ def main():
 
     # per-stage durations with HIP events on the launch stream (eager steps)
     stage_ms = np.zeros(4)
+    extra_ms = np.zeros(2)
     nrep = max(5, min(args.steps, 50))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nrep)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(nrep)]
     for e in evs:
         path.step(e)
     torch.cuda.synchronize()
     for e in evs:
-        stage_ms += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
+        if path.full:   # order: 0 K1 1 K2 2 confidence 5 admit 3 verify 4 choose_k 6
+            stage_ms += [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[5].elapsed_time(e[3]),
+                         e[3].elapsed_time(e[4])]
+            extra_ms += [e[2].elapsed_time(e[5]), e[4].elapsed_time(e[6])]
+        else:
+            stage_ms += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
     stage_ms /= nrep
+    extra_ms /= nrep
 
     positions = w.B * w.N
     value = positions / (ms_per_step * 1e-3)
@@ -339,6 +396,12 @@ def main():
     }
     if path.coupled:
         result["config"]["verify"] = "coupled"
+    if path.full:
+        result["config"]["round"] = "full"
+        result["stage_ms"]["confidence"] = round(extra_ms[0], 4)
+        result["stage_ms"]["choose_k"] = round(extra_ms[1], 4)
+        result["budget_K"] = {"first": path.K_used[2] if len(path.K_used) > 2 else None,
+                              "last": path.K_used[-1], "of": w.B * w.N}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
