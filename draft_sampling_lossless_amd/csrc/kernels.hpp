@@ -36,9 +36,10 @@ hipError_t launch_markov_few(const FewPlan& p, float* logits, const uint16_t* w1
                              int N, int V, int Vd, int r, void* workspace, hipStream_t stream);
 
 struct MarkovPlan {
-  int chunks_per_wg;   // 64-wide vocabulary chunks per workgroup (per-step path)
-  int vslices;         // vocabulary slices (workgroups along the vocabulary)
+  int chunks_per_wg;   // 64-wide vocabulary chunks per workgroup, at most (per-step path)
+  int vslices;         // workgroups per request tile; workgroup v takes chunks v, v + vslices, ...
   int btiles;          // 64-request tiles
+  size_t tgt_offset;   // workspace offset of the int32 target-id table (reduced vocabulary)
   size_t partial_bytes;  // workspace bytes (the larger need of the two paths)
   FewPlan few;
 };

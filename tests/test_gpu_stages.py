@@ -117,6 +117,9 @@ def _run_markov_gpu(c):
     (5, 4, 4096, 1000, 64, (0.0, 1.0), True),
     (3, 3, 3000, 3000, 256, (0.7,), False),
     (2, 64, 1024, 1024, 16, (1.0,), False),
+    (40, 3, 2048, 2048, 128, (0.7, 0.0), False),
+    (24, 2, 3000, 1000, 200, (1.0,), True),
+    (65, 2, 1024, 1000, 96, (0.0,), True),
 ])
 def test_markov_small(B, N, V, Vd, r, temps, reduced):
     say(f"markov B={B} N={N} V={V} Vd={Vd} r={r} T={temps} reduced={reduced}")
