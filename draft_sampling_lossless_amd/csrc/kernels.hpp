@@ -40,6 +40,7 @@ struct MarkovPlan {
   int vslices;         // workgroups per request tile; workgroup v takes chunks v, v + vslices, ...
   int btiles;          // 64-request tiles
   size_t tgt_offset;   // workspace offset of the int32 target-id table (reduced vocabulary)
+  size_t spill_offset; // workspace offset of the spill row (stores of entries that do not exist)
   size_t partial_bytes;  // workspace bytes (the larger need of the two paths)
   FewPlan few;
 };

@@ -11,14 +11,16 @@
 //                 the W2 chunk as the A operand (staged in LDS by global->LDS DMA,
 //                 shared by the 4 waves) and the gathered W1 rows of the wave's
 //                 16 requests as the B operand, held in registers for the whole
-//                 pass.  A rows are ordered so that lane (n, g) of the result
-//                 holds request n and the 16 consecutive entries 16g .. 16g+15 of
-//                 the chunk: four float4 of base logits and four Philox blocks
-//                 per lane and chunk.  The next chunk's W2 and base logits are
-//                 requested before this chunk's epilogue runs.  Per lane a
-//                 running best (key, target id) and a base-2 log-sum-exp (m, s)
-//                 are kept; the four lanes of a request merge them and write one
-//                 partial per (request, workgroup).
+//                 pass.  Fragment f covers entries 16 f .. 16 f + 15, so lane
+//                 (n, g) holds request n, entries 16 f + 4 g .. +3: one float4 of
+//                 base logits and one Philox block per fragment, and the four lanes
+//                 of a request read 64 contiguous bytes per load instruction.  The
+//                 next chunk's W2 and base logits are requested before this chunk's
+//                 epilogue runs; every lane issues the same memory operations, so
+//                 nothing waits on them until the next chunk.  Per lane a running
+//                 best (key, block) and a base-2 log-sum-exp (m, s) are kept; the
+//                 four lanes of a request merge them and write one partial per
+//                 (request, workgroup).
 //   markov_merge  one wave per request reduces the partials, writes the token
 //                 and log Z.  The next step's kernel reads that token.
 //
@@ -42,7 +44,7 @@ namespace {
 
 using namespace mk;
 
-constexpr int kSlots = 1024;     // workgroups the grid is sized for: 4 per CU on 256 CUs
+constexpr int kMaxSlots = 2048;  // resident workgroups a launch may count on (8 per CU on 256 CUs)
 constexpr float kLseSlack = 64;  // the running reference may trail the maximum by this much (base 2)
 constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
 constexpr uint32_t kWeyl0 = 0x9E3779B9u, kWeyl1 = 0xBB67AE85u;
@@ -96,13 +98,20 @@ struct ChunkLds {
   __host__ __device__ static constexpr int pos(int f, int m) { return P >= 16 ? f % kRows : f * kPer + m / P; }
   __host__ __device__ static constexpr int offset(int f, int m) { return grp(f, m) * kGroup + pos(f, m) * P * 16; }
   // chunk row (vocabulary offset) that group p, position h holds; fragment f row m
-  // is vocabulary offset 16 (m >> 2) + 4 f + (m & 3)
+  // is vocabulary offset 16 f + m
   __host__ __device__ static constexpr int vocab(int p, int h) {
     const int f = P >= 16 ? (p / 16) * kRows + h : h / kPer;
     const int m = P >= 16 ? p % 16 : (h % kPer) * P + p;
-    return 16 * (m >> 2) + 4 * f + (m & 3);
+    return 16 * f + m;
   }
 };
+
+// four floats this thread stored earlier in the kernel (device-coherent loads, so a
+// stale vector-L1 line of the values loaded before the store is never returned)
+__device__ __forceinline__ void load_stored4(const float* p, float (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // one 16-byte global->LDS DMA per lane (lane i writes lds_base + 16 i); a plain
 // function, so the kernel template below stays instantiable by the host compiler
@@ -113,8 +122,8 @@ __device__ __forceinline__ void dma16(const uint16_t* src, char* lds_base) {
 template <int KS, bool kReduced>
 __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, const uint16_t* __restrict__ w1,
                                                    const uint16_t* __restrict__ w2, const int32_t* __restrict__ tgt_of,
-                                                   const int32_t* __restrict__ prev_tok, int prev_stride,
-                                                   const float* __restrict__ temperature,
+                                                   float* __restrict__ spill_row, const int32_t* __restrict__ prev_tok,
+                                                   int prev_stride, const float* __restrict__ temperature,
                                                    const uint32_t* __restrict__ request_id, uint32_t key0,
                                                    uint32_t key1, MarkovPartial* __restrict__ partial, int step,
                                                    int B, int N, int V, int Vd, int r, int nvs, int nbt) {
@@ -129,15 +138,47 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int nchunks = (Vd + kChunk - 1) / kChunk;
-  const int kc = r / 8;  // W2 pieces per row that hold data (the rest of a row is zero)
+  const int kc = r / 8;  // W2 pieces per row that hold data
   const int rq0 = bt * kReqPerWG + wave * kReqPerWave;
   const bool wave_active = rq0 < B;
   const bool lane_ok = rq0 + n < B;
   const int b = min(rq0 + n, B - 1);
 
-  if (kc != P) {  // rank not a multiple of 32: the padding pieces must read as zero
-    for (int p = tid; p < Lay::kBytes / 16; p += 256) reinterpret_cast<uint4*>(lds)[p] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
+  // DMA of chunk c: instruction t of this wave fills group 4 t + wave; lane L takes
+  // piece L % P of position L / P.  The chunk row of (t, wave, L) splits into
+  // vocab(4 t, 0) + wave + vocab(0, L / P), so a full chunk needs one lane offset.
+  // With a rank below 32 KS the pieces past the rank repeat the row's last piece:
+  // finite values that meet the zero B operand there.  Every wave issues exactly KS
+  // DMA instructions per chunk, so the vector-memory counter is known at each wait.
+  const int dma_piece = min(lane % P, kc - 1);
+  const int dma_row = Lay::vocab(0, lane / P);
+  const int dma_off = dma_row * r + dma_piece * 8;
+  auto issue_w2 = [&](int c) {
+    const int jc = c * kChunk;
+    if (jc + kChunk <= Vd) {
+      const uint16_t* src = w2 + (size_t)(jc + wave) * r;
+#pragma unroll
+      for (int t = 0; t < KS; ++t)
+        dma16(src + (size_t)Lay::vocab(4 * t, 0) * r + dma_off, lds + (t * 4 + wave) * Lay::kGroup);
+    } else {  // the last, partial chunk: rows past Vd load row Vd - 1 (never used)
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const int j = min(jc + wave + Lay::vocab(4 * t, 0) + dma_row, Vd - 1);
+        dma16(w2 + (size_t)j * r + dma_piece * 8, lds + (t * 4 + wave) * Lay::kGroup);
+      }
+    }
+  };
+
+  if (!wave_active) {
+    // a wave without requests (the last request tile) still stages its share of W2
+    for (int c = vs; c < nchunks; c += nvs) {
+      if (c == vs) issue_w2(c);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      asm volatile("s_barrier" ::: "memory");
+      asm volatile("s_barrier" ::: "memory");
+      if (c + nvs < nchunks) issue_w2(c + nvs);
+    }
+    return;
   }
 
   // B fragments: W1 row of request n, k = 32 s + 8 g .. +7 (zero past r)
@@ -164,83 +205,68 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   const uint32_t x1 = (uint32_t)(pr >> 32) ^ (uint32_t)step ^ key0, y1 = (uint32_t)pr;
 
   float bkey = -INFINITY, bm = -FLT_MAX, bthr = -FLT_MAX, bs = 0.0f;
-  // Without a target map ids grow along a lane, so the running best is kept per
-  // block of 4 (strict comparison: an earlier block wins ties) and the entry inside
-  // the winning block is found again after the pass.  bblk: first id of that block
-  // minus 16 g (uniform per chunk and block); the lane's first block stands in.
+  // The running best is kept per block of 4 entries: the block's largest key, compared
+  // strictly (an earlier block keeps a tie), and bblk = the block's first id minus 4 g.
+  // After the pass the entry inside the winning block is found again from the stored
+  // logits.  Without a target map ids grow along a lane, so this is the argmax with
+  // ties to the smallest id.  With one, ties are broken by target id: a tie between
+  // two blocks (or a lane with no finite key) sends the lane to an exact rescan.
   int bblk = vs * kChunk;
-  int btok = 0x7FFFFFFF;  // with a target map: the best target id so far
+  bool tie = false;
 
-  // DMA of chunk c: instruction t of this wave fills group 4 t + wave; lane L takes
-  // piece L % P of position L / P.  The chunk row of (t, wave, L) splits into
-  // vocab(4 t, 0) + wave + vocab(0, L / P), so a full chunk needs one lane offset.
-  const int dma_piece = lane % P;
-  const bool dma_ok = dma_piece < kc;
-  const int dma_row = Lay::vocab(0, lane / P);
-  const int dma_off = dma_row * r + dma_piece * 8;
-  auto issue_w2 = [&](int c) {
-    const int jc = c * kChunk;
-    if (jc + kChunk <= Vd) {
-      const uint16_t* src = w2 + (size_t)(jc + wave) * r;
+  // This lane's logits row as float4 (Vd is a multiple of 4).  Loads clamp to the
+  // row; stores of entries that do not exist (past Vd, or a lane without a request)
+  // go to a spill row in the workspace, so every lane issues the same loads and
+  // stores and the vector-memory counter stays exact.
+  const int vd4 = Vd / 4;
+  float4* const row4 = reinterpret_cast<float4*>(logits + ((size_t)b * N + step) * Vd);
+  float4* const st4 = lane_ok ? row4 : reinterpret_cast<float4*>(spill_row);
+  float4* const spill4 = reinterpret_cast<float4*>(spill_row);
+  auto load_base = [&](int c, float4 (&bv)[4]) {
+    const int j4 = c * (kChunk / 4) + g;
 #pragma unroll
-      for (int t = 0; t < KS; ++t)
-        if (dma_ok)
-          dma16(src + (size_t)Lay::vocab(4 * t, 0) * r + dma_off, lds + (t * 4 + wave) * Lay::kGroup);
-    } else {  // the last, partial chunk: rows past Vd load row Vd - 1 (never used)
-#pragma unroll
-      for (int t = 0; t < KS; ++t) {
-        const int j = min(jc + wave + Lay::vocab(4 * t, 0) + dma_row, Vd - 1);
-        if (dma_ok)
-          dma16(w2 + (size_t)j * r + dma_piece * 8, lds + (t * 4 + wave) * Lay::kGroup);
-      }
-    }
-  };
-  float* const row = logits + ((size_t)b * N + step) * Vd + 16 * g;  // this lane's 16 entries of a chunk
-  const int32_t* const trow = kReduced ? tgt_of + 16 * g : nullptr;
-  auto load_base = [&](int c, float4 (&bv)[4], int4 (&tv)[4]) {
-    const int jc = c * kChunk;
-    if (jc + kChunk <= Vd) {
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        bv[f] = *reinterpret_cast<const float4*>(row + jc + 4 * f);
-        if (kReduced) tv[f] = *reinterpret_cast<const int4*>(trow + jc + 4 * f);
-      }
-    } else {
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int o = min(jc + 16 * g + 4 * f, Vd - 4) - 16 * g;
-        bv[f] = *reinterpret_cast<const float4*>(row + o);
-        if (kReduced) tv[f] = *reinterpret_cast<const int4*>(trow + o);
-      }
-    }
+    for (int f = 0; f < 4; ++f) bv[f] = row4[min(j4 + 4 * f, vd4 - 1)];
   };
   // noise of the Philox block of entries j .. j+3 (j a multiple of 4)
   auto noise = [&](int j, float (&lg)[4]) {
-    const uint64_t p0 = (uint64_t)kPhiloxM0 * (uint32_t)(j >> 2);
-    const u32x4 w =
-        philox_rounds_1_9(u32x4{x1, y1, (uint32_t)(p0 >> 32) ^ kTagDraft ^ key1, (uint32_t)p0}, key0, key1);
-    lg[0] = neg_gumbel2(w.x);
-    lg[1] = neg_gumbel2(w.y);
-    lg[2] = neg_gumbel2(w.z);
-    lg[3] = neg_gumbel2(w.w);
+    if (any_noisy) {
+      const uint64_t p0 = (uint64_t)kPhiloxM0 * (uint32_t)(j >> 2);
+      const u32x4 w =
+          philox_rounds_1_9(u32x4{x1, y1, (uint32_t)(p0 >> 32) ^ kTagDraft ^ key1, (uint32_t)p0}, key0, key1);
+      lg[0] = neg_gumbel2(w.x);
+      lg[1] = neg_gumbel2(w.y);
+      lg[2] = neg_gumbel2(w.z);
+      lg[3] = neg_gumbel2(w.w);
+    } else {
+      lg[0] = lg[1] = lg[2] = lg[3] = 0.0f;
+    }
+  };
+  // y = l log2(e) / T and key = y + Gumbel (T == 0: key = y = l); the final search
+  // repeats exactly these operations on the stored logits
+  auto keys_of = [&](const float (&lg)[4], const float (&l)[4], float (&y)[4], float (&key)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[i] = __fmul_rn(l[i], c2);
+      key[i] = fmaf(lg[i], -gs, y[i]);
+    }
   };
 
-  // one chunk: bias on MFMA, then the epilogue over this lane's 16 entries; the
-  // next chunk's W2 pieces and base logits go out first (into `nb`, `nt`)
-  auto chunk = [&](int c, float4 (&cb)[4], int4 (&ct)[4], float4 (&nb)[4], int4 (&nt)[4]) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);    // this wave's DMA pieces of chunk c (and its base logits)
+  // One chunk.  The W2 DMA and base logits of the next chunk, then this chunk's
+  // stores, are issued at the start of the epilogue, so the wait at the top of the
+  // next chunk finds them complete unless the epilogue was shorter than the memory
+  // latency.
+  auto chunk = [&](int c, float4 (&cb)[4], float4 (&nb)[4]) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);    // DMA pieces and base logits of chunk c
     asm volatile("s_barrier" ::: "memory");  // every wave's pieces
     floatx4 acc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (wave_active) {
-        const char* arow = lds + Lay::offset(f, n) + 16 * g;
+      const char* arow = lds + Lay::offset(f, n) + 16 * g;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + 64 * s));
-          acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, efrag[s], acc[f], 0, 0, 0);
-        }
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + 64 * s));
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, efrag[s], acc[f], 0, 0, 0);
       }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -248,10 +274,9 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
     const int cn = c + nvs;
     if (cn < nchunks) {
       issue_w2(cn);
-      load_base(cn, nb, nt);
+      load_base(cn, nb);
     }
-    if (!wave_active) return;
-    const int jc = c * kChunk, j0 = jc + 16 * g;
+    const int jc = c * kChunk, j0 = jc + 4 * g, j4 = j0 / 4;  // block f: entries j0 + 16 f .. +3
     float l[4][4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -259,28 +284,19 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
       l[f][1] = cb[f].y + acc[f][1];
       l[f][2] = cb[f].z + acc[f][2];
       l[f][3] = cb[f].w + acc[f][3];
-      if (lane_ok && j0 + 4 * f < Vd)
-        *reinterpret_cast<float4*>(row + jc + 4 * f) = make_float4(l[f][0], l[f][1], l[f][2], l[f][3]);
+      float4* dst = (j4 + 4 * f < vd4) ? st4 + (j4 + 4 * f) : spill4 + (j4 + 4 * f);
+      *dst = make_float4(l[f][0], l[f][1], l[f][2], l[f][3]);
     }
     if (jc + kChunk > Vd) {  // the last, partial chunk: entries past Vd never win nor count
 #pragma unroll
       for (int f = 0; f < 4; ++f)
-        if (j0 + 4 * f >= Vd) l[f][0] = l[f][1] = l[f][2] = l[f][3] = -INFINITY;
+        if (j0 + 16 * f >= Vd) l[f][0] = l[f][1] = l[f][2] = l[f][3] = -INFINITY;
     }
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      float lg[4];
-      if (any_noisy) {
-        noise(j0 + 4 * f, lg);
-      } else {
-        lg[0] = lg[1] = lg[2] = lg[3] = 0.0f;
-      }
-      float y[4], key[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        y[i] = __fmul_rn(l[f][i], c2);
-        key[i] = fmaf(lg[i], -gs, y[i]);
-      }
+      float lg[4], y[4], key[4];
+      noise(j0 + 16 * f, lg);
+      keys_of(lg, l[f], y, key);
       const float mx = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
       const bool grow = mx > bthr;
       if (__ballot(grow)) {  // rare after a lane's first block
@@ -291,20 +307,11 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
       }
       bs += (__builtin_amdgcn_exp2f(y[0] - bm) + __builtin_amdgcn_exp2f(y[1] - bm)) +
             (__builtin_amdgcn_exp2f(y[2] - bm) + __builtin_amdgcn_exp2f(y[3] - bm));
-      if (kReduced) {
-        const int t[4] = {ct[f].x, ct[f].y, ct[f].z, ct[f].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (key_beats(key[i], t[i], bkey, btok)) {
-            bkey = key[i];
-            btok = t[i];
-          }
-      } else {
-        const float km = fmaxf(fmaxf(key[0], key[1]), fmaxf(key[2], key[3]));
-        if (km > bkey) {
-          bkey = km;
-          bblk = jc + 4 * f;
-        }
+      const float km = fmaxf(fmaxf(key[0], key[1]), fmaxf(key[2], key[3]));
+      if (kReduced) tie = tie || (km == bkey && km > -INFINITY);
+      if (km > bkey) {
+        bkey = km;
+        bblk = jc + 16 * f;
       }
       // one block at a time: interleaving the four blocks' Philox chains buys nothing
       // here (other waves fill the pipeline) and would hold four times the registers
@@ -313,35 +320,70 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   };
 
   float4 ba[4], bb[4];
-  int4 ta[4], tb[4];
   issue_w2(vs);
-  load_base(vs, ba, ta);
+  load_base(vs, ba);
   for (int c = vs; c < nchunks; c += 2 * nvs) {  // unrolled by two: the prefetch buffers alternate
-    chunk(c, ba, ta, bb, tb);
+    chunk(c, ba, bb);
     if (c + nvs >= nchunks) break;
-    chunk(c + nvs, bb, tb, ba, ta);
+    chunk(c + nvs, bb, ba);
   }
 
-  if (!kReduced && wave_active) {
-    // the entry of the winning block that holds bkey (the keys are recomputed with the
-    // same operations from the processed logits this lane stored); no winner: the
-    // block's first id, which is also what a strict argmax over all -inf keys returns
-    const int jb = bblk + 16 * g;
-    btok = jb;
-    if (bkey > -INFINITY) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      const float4 v = *reinterpret_cast<const float4*>(row + bblk);  // block jb, stored by this lane
-      const float lv[4] = {v.x, v.y, v.z, v.w};
-      float lg[4] = {0.f, 0.f, 0.f, 0.f};
-      if (any_noisy) noise(jb, lg);
-      int hit = 3;
+  // the entry of the winning block: its keys again from the logits this lane stored
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  int btok;
+  {
+    const int jb = bblk + 4 * g;
+    float lv[4];
+    load_stored4(reinterpret_cast<const float*>(row4) + min(jb, Vd - 4), lv);
+    float lg[4], y[4], key[4];
+    noise(jb, lg);
+    keys_of(lg, lv, y, key);
+    if (!kReduced) {
+      // no winner (every key -inf): the block's first id, as a strict argmax would give
+      int hit = 0;
 #pragma unroll
       for (int i = 3; i >= 0; --i)
-        if (fmaf(lg[i], -gs, __fmul_rn(lv[i], c2)) == bkey) hit = i;
+        if (key[i] == bkey) hit = i;
       btok = jb + hit;
+    } else {
+      const int4 tv = *reinterpret_cast<const int4*>(tgt_of + min(jb, Vd - 4));
+      const int t[4] = {tv.x, tv.y, tv.z, tv.w};
+      btok = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (key[i] == bkey) btok = min(btok, t[i]);
     }
   }
-  if (!wave_active) return;
+  if (kReduced) {
+    const bool rescan = tie || !(bkey > -INFINITY);
+    if (__ballot(rescan)) {  // rare: the exact argmax over this lane's entries, ties to the smaller target
+      if (rescan) {
+        bkey = -INFINITY;
+        btok = 0x7FFFFFFF;
+        for (int c = vs; c < nchunks; c += nvs) {
+          const int jc = c * kChunk;
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const int j = jc + 16 * f + 4 * g;
+            if (j >= Vd) continue;
+            float lv[4];
+            load_stored4(reinterpret_cast<const float*>(row4) + j, lv);
+            const int4 tv = *reinterpret_cast<const int4*>(tgt_of + j);
+            const int t[4] = {tv.x, tv.y, tv.z, tv.w};
+            float lg[4], y[4], key[4];
+            noise(j, lg);
+            keys_of(lg, lv, y, key);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (key_beats(key[i], t[i], bkey, btok)) {
+                bkey = key[i];
+                btok = t[i];
+              }
+          }
+        }
+      }
+    }
+  }
 
   // merge the four lanes (g) of request n: partners n ^ 16, then n ^ 32
   {
@@ -413,26 +455,58 @@ int ksteps_of(int r) {  // MFMA k steps of 32, rounded up to a power of two
   return k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : 8;
 }
 
-template <int KS>
-hipError_t launch_steps(bool reduced, dim3 grid, float* logits, const uint16_t* w1, const uint16_t* w2,
-                        const int32_t* tgt, const int32_t* anchor, const float* temperature,
-                        const uint32_t* request_id, uint32_t k0, uint32_t k1, MarkovPartial* partial,
-                        int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd, int r, int nvs, int nbt,
-                        hipStream_t stream) {
+// workgroups per request tile: the resident capacity of the chip spread over the
+// request tiles (a multiple of 8 for the XCD order), at most one per chunk
+int markov_slices(int chunks, int nbt, int slots) {
+  const int per = std::max(8, slots / nbt / 8 * 8);
+  return std::min(chunks, per);
+}
+
+template <int KS, bool kReduced>
+int resident_per_cu(size_t lds) {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!cached[dev]) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ, reinterpret_cast<const void*>(&markov_step<KS, kReduced>), 256, lds) != hipSuccess || occ <= 0)
+      occ = 1;
+    cached[dev] = occ;
+  }
+  return cached[dev];
+}
+
+template <int KS, bool kReduced>
+hipError_t launch_steps(float* logits, const uint16_t* w1, const uint16_t* w2, const int32_t* tgt,
+                        float* spill, const int32_t* anchor, const float* temperature, const uint32_t* request_id, uint32_t k0,
+                        uint32_t k1, MarkovPartial* partial, int32_t* draft_tokens, float* log_z, int B, int N, int V,
+                        int Vd, int r, int nbt, int max_slices, hipStream_t stream) {
   const size_t lds = ChunkLds<4 * KS>::kBytes;
+  const int chunks = (Vd + kChunk - 1) / kChunk;
+  const int slots = std::min(kMaxSlots, resident_per_cu<KS, kReduced>(lds) * cu_count_markov());
+  const int nvs = std::min(max_slices, markov_slices(chunks, nbt, slots));
+  const dim3 grid((nvs + 7) / 8 * 8 * nbt);
   for (int i = 0; i < N; ++i) {
     const int32_t* prev = (i == 0) ? anchor : draft_tokens + (i - 1);
     const int stride = (i == 0) ? 1 : N;
-    if (reduced)
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(markov_step<KS, true>), grid, dim3(256), lds, stream, logits, w1, w2, tgt, prev, stride,
-                         temperature, request_id, k0, k1, partial, i, B, N, V, Vd, r, nvs, nbt);
-    else
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(markov_step<KS, false>), grid, dim3(256), lds, stream, logits, w1, w2, tgt, prev, stride,
-                         temperature, request_id, k0, k1, partial, i, B, N, V, Vd, r, nvs, nbt);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(markov_step<KS, kReduced>), grid, dim3(256), lds, stream, logits, w1, w2, tgt,
+                       spill, prev, stride, temperature, request_id, k0, k1, partial, i, B, N, V, Vd, r, nvs, nbt);
     hipLaunchKernelGGL(markov_merge, dim3((B + 3) / 4), dim3(256), 0, stream, partial, temperature, draft_tokens,
                        log_z, i, B, N, nvs);
   }
   return hipGetLastError();
+}
+
+template <int KS>
+hipError_t launch_ks(bool reduced, float* logits, const uint16_t* w1, const uint16_t* w2, const int32_t* tgt,
+                     float* spill, const int32_t* anchor, const float* temperature, const uint32_t* request_id, uint32_t k0,
+                     uint32_t k1, MarkovPartial* partial, int32_t* draft_tokens, float* log_z, int B, int N, int V,
+                     int Vd, int r, int nbt, int max_slices, hipStream_t stream) {
+  return reduced ? launch_steps<KS, true>(logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
+                                          draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, stream)
+                 : launch_steps<KS, false>(logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
+                                           draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, stream);
 }
 
 }  // namespace
@@ -442,14 +516,16 @@ MarkovPlan plan_markov(int B, int N, int Vd, int r, int cus) {
   p.few = plan_markov_few(B, N, Vd, r, cus);
   p.btiles = (B + kReqPerWG - 1) / kReqPerWG;
   const int chunks = (Vd + kChunk - 1) / kChunk;
-  // workgroups per request tile: enough to fill the chip, at most one per chunk
-  const int want = std::min(chunks, (kSlots + p.btiles - 1) / p.btiles);
-  p.vslices = want;
-  p.chunks_per_wg = (chunks + want - 1) / want;
+  // the most workgroups per request tile any launch uses (the workspace holds one
+  // partial per request and workgroup)
+  p.vslices = markov_slices(chunks, p.btiles, kMaxSlots);
+  p.chunks_per_wg = (chunks + p.vslices - 1) / p.vslices;
   p.partial_bytes = (size_t)B * p.vslices * sizeof(MarkovPartial);
   p.partial_bytes = (p.partial_bytes + 255) / 256 * 256;
   p.tgt_offset = p.partial_bytes;
-  p.partial_bytes += (size_t)Vd * sizeof(int32_t);
+  p.partial_bytes += ((size_t)Vd * sizeof(int32_t) + 255) / 256 * 256;
+  p.spill_offset = p.partial_bytes;  // a logits row for stores of entries that do not exist
+  p.partial_bytes += (size_t)chunks * kChunk * sizeof(float);
   // the query (cus == 0) must cover whichever path a launch picks
   if (p.few.bytes > p.partial_bytes) p.partial_bytes = p.few.bytes;
   return p;
@@ -465,24 +541,23 @@ hipError_t launch_markov_sample(float* logits, const uint16_t* w1, const uint16_
                              B, N, V, Vd, r, workspace, stream);
   MarkovPartial* partial = static_cast<MarkovPartial*>(workspace);
   int32_t* tgt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.tgt_offset);
+  float* spill = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.spill_offset);
   const bool reduced = d2t != nullptr;
   if (reduced) hipLaunchKernelGGL(target_table, dim3((Vd + 255) / 256), dim3(256), 0, stream, d2t, Vd, tgt);
-  const int nvs8 = (p.vslices + 7) / 8 * 8;
-  const dim3 grid(nvs8 * p.btiles);
   const uint32_t k0 = (uint32_t)(seed & 0xFFFFFFFFu), k1 = (uint32_t)(seed >> 32);
   switch (ksteps_of(r)) {
     case 1:
-      return launch_steps<1>(reduced, grid, logits, w1, w2, tgt, anchor, temperature, request_id, k0, k1, partial,
-                             draft_tokens, log_z, B, N, V, Vd, r, p.vslices, p.btiles, stream);
+      return launch_ks<1>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, stream);
     case 2:
-      return launch_steps<2>(reduced, grid, logits, w1, w2, tgt, anchor, temperature, request_id, k0, k1, partial,
-                             draft_tokens, log_z, B, N, V, Vd, r, p.vslices, p.btiles, stream);
+      return launch_ks<2>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, stream);
     case 4:
-      return launch_steps<4>(reduced, grid, logits, w1, w2, tgt, anchor, temperature, request_id, k0, k1, partial,
-                             draft_tokens, log_z, B, N, V, Vd, r, p.vslices, p.btiles, stream);
+      return launch_ks<4>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, stream);
     default:
-      return launch_steps<8>(reduced, grid, logits, w1, w2, tgt, anchor, temperature, request_id, k0, k1, partial,
-                             draft_tokens, log_z, B, N, V, Vd, r, p.vslices, p.btiles, stream);
+      return launch_ks<8>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, stream);
   }
 }
 
