@@ -23,6 +23,7 @@
 //              alpha requested, rows k < L are streamed too for their partial sums.
 //              The last workgroup of a request (a ticket counter the accept kernel
 //              cleared) merges the partials and writes y and alpha.
+#include <float.h>
 #include <math.h>
 
 #include "dspark.h"
@@ -155,38 +156,55 @@ __global__ __launch_bounds__(256) void verify_rowstats(const float* __restrict__
   const float T = temperature[b];
   const bool hot = T > 0.0f;
   const float c2 = hot ? (1.0f / T) * kLog2e : 1.0f;
-  const float* rowp = target + (size_t)row * V;
-  const int lo = c * chunk, hi = min(V, lo + chunk);
+  const float4* r4 = reinterpret_cast<const float4*>(target + (size_t)row * V);
+  const int lo4 = c * (chunk / 4), hi4 = min(V, c * chunk + chunk) / 4;
+  const int tid = threadIdx.x;
+  constexpr int kB = 8;  // float4 loads per thread in flight
 
-  float m = -INFINITY, s = 0.0f, av = -INFINITY;
-  int ai = 0x7FFFFFFF;
-  for (int v = lo + 4 * threadIdx.x; v < hi; v += 4 * blockDim.x) {
-    const float4 q = *reinterpret_cast<const float4*>(rowp + v);
-    const float l[4] = {q.x, q.y, q.z, q.w};
+  // T > 0: base-2 log-sum-exp with a lazily raised reference m (every y seen is at
+  // most m + 64, so no term overflows); T == 0: the argmax, ties to the smaller index.
+  float m = -FLT_MAX, thr = -FLT_MAX, s = 0.0f, av = -INFINITY;
+  int ai = lo4 * 4 + 4 * tid;  // this thread's first index (a strict argmax over all -inf keeps it)
+  for (int i0 = lo4 + tid; i0 < hi4; i0 += 256 * kB) {
+    float4 q[kB];
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      if (amax_beats(l[f], v + f, av, ai)) {
-        av = l[f];
-        ai = v + f;
+    for (int u = 0; u < kB; ++u) q[u] = r4[min(i0 + 256 * u, hi4 - 1)];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const bool ok = i0 + 256 * u < hi4;
+      const float l[4] = {ok ? q[u].x : -INFINITY, ok ? q[u].y : -INFINITY, ok ? q[u].z : -INFINITY,
+                          ok ? q[u].w : -INFINITY};
+      if (hot) {
+        float y[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) y[f] = l[f] * c2;
+        const float mx = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+        const bool grow = mx > thr;
+        if (__ballot(grow)) {
+          const float sc = __builtin_amdgcn_exp2f(m - mx);
+          s = grow ? s * sc : s;
+          m = grow ? mx : m;
+          thr = grow ? mx + 64.0f : thr;
+        }
+        s += (__builtin_amdgcn_exp2f(y[0] - m) + __builtin_amdgcn_exp2f(y[1] - m)) +
+             (__builtin_amdgcn_exp2f(y[2] - m) + __builtin_amdgcn_exp2f(y[3] - m));
+      } else {
+        const int v = (i0 + 256 * u) * 4;
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          if (l[f] > av) {
+            av = l[f];
+            ai = v + f;
+          }
       }
-    if (hot) {
-      float y[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) y[f] = l[f] * c2;
-      const float mn = fmaxf(m, fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])));
-      float acc = s * __builtin_amdgcn_exp2f(m - mn);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) acc += __builtin_amdgcn_exp2f(y[f] - mn);
-      s = acc;
-      m = mn;
     }
   }
   wave_stat_merge(m, s, av, ai);
   __shared__ RowStat red[4];
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = RowStat{m, s, av, ai};
+  const int wave = tid >> 6;
+  if ((tid & 63) == 0) red[wave] = RowStat{m, s, av, ai};
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     RowStat a = red[0];
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) stat_merge(a.m, a.s, a.amax, a.aidx, red[w].m, red[w].s, red[w].amax, red[w].aidx);
     stats[(size_t)row * nchunks + c] = a;
@@ -367,45 +385,90 @@ __global__ __launch_bounds__(256) void verify_sample(int input_kind, const float
   const float2 st = rstat[(size_t)b * (N + 1) + (probs ? 0 : k)];
   const float* trow = target + ((size_t)b * (N + 1) + k) * V;
   const float* drow = draft + ((size_t)b * N + min(k, N - 1)) * Vd;
-  const int lo = c * chunk, hi = min(V, lo + chunk);
+  const float4* t4 = reinterpret_cast<const float4*>(trow);
+  const int lo4 = c * (chunk / 4), hi4 = min(V, c * chunk + chunk) / 4;
+  constexpr int kB = 4;  // float4 of the target row per thread in flight
 
   // Race candidates start as "nobody": r = 0 with E = 1 at index INT_MAX loses
   // to everything with r > 0, and index order decides among r = 0.
   float br = 0.0f, bE = 1.0f, fr = 0.0f, fE = 1.0f, asum = 0.0f;
   int bv = 0x7FFFFFFF, fv = 0x7FFFFFFF;
-  for (int v = lo + 4 * tid; v < hi; v += 4 * blockDim.x) {
-    const float4 q = *reinterpret_cast<const float4*>(trow + v);
-    float pt[4] = {q.x, q.y, q.z, q.w};
-    if (!probs) {
+  for (int i0 = lo4 + tid; i0 < hi4; i0 += 256 * kB) {
+    // every load of the batch first (clamped indices), then the arithmetic
+    float4 q[kB];
+    float dv[kB][4];
+    int jv[kB][4];
+    unsigned dmask = 0xFFFFu;  // bit 4 u + f: target id in the draft vocabulary
+    // (one loop per case: a branch inside the batch would split it into blocks and
+    // make the loads wait for each other)
+    if (!need_draft) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) pt[f] = __builtin_amdgcn_exp2f(pt[f] * c2 - st.x) * st.y;
-    }
-    float pd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (need_draft) {
+      for (int u = 0; u < kB; ++u) q[u] = t4[min(i0 + 256 * u, hi4 - 1)];
+    } else if (inv_map) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int j = inv_map ? inv_map[v + f] : v + f;
-        if (j >= 0) {
-          const float d = drow[j];
-          pd[f] = probs ? d : __builtin_amdgcn_exp2f(d * c2 - dlz2);
-        }
+      for (int u = 0; u < kB; ++u) {
+        const int i = min(i0 + 256 * u, hi4 - 1);
+        q[u] = t4[i];
+        const int4 jj = reinterpret_cast<const int4*>(inv_map)[i];
+        jv[u][0] = jj.x;
+        jv[u][1] = jj.y;
+        jv[u][2] = jj.z;
+        jv[u][3] = jj.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int i = min(i0 + 256 * u, hi4 - 1);
+        q[u] = t4[i];
+        const float4 d = reinterpret_cast<const float4*>(drow)[i];
+        dv[u][0] = d.x;
+        dv[u][1] = d.y;
+        dv[u][2] = d.z;
+        dv[u][3] = d.w;
       }
     }
-    if (do_alpha) {
+    if (need_draft && inv_map) {  // the gathers of the whole batch, unconditional (clamped)
 #pragma unroll
-      for (int f = 0; f < 4; ++f) asum += fminf(pt[f], pd[f]);
+      for (int u = 0; u < kB; ++u)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          dv[u][f] = drow[max(jv[u][f], 0)];
+          if (jv[u][f] < 0) dmask &= ~(1u << (4 * u + f));
+        }
     }
-    if (do_race) {
-      const u32x4 w = philox4x32_10(u32x4{(uint32_t)v >> 2, (uint32_t)k, req, tag}, key0, key1);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const float E = -plog2(uniform01(ws[f]));
-        if (jb.mode == kJobResid) {
-          race_update(fmaxf(0.0f, __fsub_rn(pt[f], pd[f])), E, v + f, br, bE, bv);
-          race_update(pt[f], E, v + f, fr, fE, fv);
-        } else {
-          race_update(pt[f], E, v + f, br, bE, bv);
+    for (int u = 0; u < kB; ++u) {
+      const int v = (i0 + 256 * u) * 4;
+      if (i0 + 256 * u >= hi4) continue;  // (the batch's tail past the chunk)
+      float pt[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+      if (!probs) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) pt[f] = __builtin_amdgcn_exp2f(pt[f] * c2 - st.x) * st.y;
+      }
+      float pd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (need_draft) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const float d = dv[u][f];
+          pd[f] = !((dmask >> (4 * u + f)) & 1u) ? 0.0f : (probs ? d : __builtin_amdgcn_exp2f(d * c2 - dlz2));
+        }
+      }
+      if (do_alpha) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) asum += fminf(pt[f], pd[f]);
+      }
+      if (do_race) {
+        const u32x4 w = philox4x32_10(u32x4{(uint32_t)v >> 2, (uint32_t)k, req, tag}, key0, key1);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const float E = -plog2(uniform01(ws[f]));
+          if (jb.mode == kJobResid) {
+            race_update(fmaxf(0.0f, __fsub_rn(pt[f], pd[f])), E, v + f, br, bE, bv);
+            race_update(pt[f], E, v + f, fr, fE, fv);
+          } else {
+            race_update(pt[f], E, v + f, br, bE, bv);
+          }
         }
       }
     }
