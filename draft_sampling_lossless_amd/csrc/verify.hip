@@ -26,6 +26,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "dspark.h"
 #include "device.hpp"
 #include "kernels.hpp"
@@ -556,7 +558,9 @@ int pick_chunks(long rows, int V) {
 
 VerifyPlan plan_verify(int B, int N, int V) {
   VerifyPlan p{};
-  p.stat_chunks = pick_chunks((long)B * (N + 1), V);
+  // rows past a request's verify length exit at once, so the live rows alone must
+  // fill the chip: chunks of at most 16K entries whatever the row count
+  p.stat_chunks = std::max(pick_chunks((long)B * (N + 1), V), (V + 16383) / 16384);
   p.stat_chunk = ((V + p.stat_chunks - 1) / p.stat_chunks + 3) / 4 * 4;
   p.sample_chunks = pick_chunks(B, V);
   p.sample_chunk = ((V + p.sample_chunks - 1) / p.sample_chunks + 3) / 4 * 4;
