@@ -15,7 +15,7 @@
 //    fragments) come from L1/L2.  No LDS.
 //  * tiled (M > 64): MFMA-bound.  128 x 128 output tiles, BK = 64, both operands
 //    staged through double-buffered LDS; 4 waves, each a 64 x 64 block of 16x16
-//    MFMA fragments.
+//    MFMA fragments; grouped tile order (8 row tiles at a time).
 //
 // MFMA 16x16x32 fragment layout (64 lanes, lane = 16 * g + n):
 //   A: lane holds 8 consecutive k of row n;  B: 8 consecutive k of column n;
@@ -232,13 +232,20 @@ __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, 
                                                 float* __restrict__ C, int M, int H, int Vd, int mtiles,
                                                 int ntiles) {
   __shared__ __attribute__((aligned(16))) char lds[2][2][TBM * TLDS_ROW];  // [buf][A|W]
-  // XCD-aware order: blocks are dispatched round-robin over 8 XCDs; give each XCD
-  // a contiguous run of output tiles so neighbouring tiles share LM-head rows in L2.
+  // XCD-aware, grouped order: blocks are dispatched round-robin over 8 XCDs; each
+  // XCD takes a contiguous run of the linear tile order, and that order walks groups
+  // of kGroupM row tiles column by column, so the ~64 workgroups an XCD runs at once
+  // cover about 8 row tiles x 8 column tiles and share both operands' k slices in
+  // its L2 (a column-major walk shares only the LM-head rows and re-reads the whole
+  // hidden matrix for every column tile).
+  constexpr int kGroupM = 8;
   const int total = mtiles * ntiles;
   const int per_xcd = (total + 7) / 8;
   const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (lin >= total) return;
-  const int nt = lin / mtiles, mt = lin % mtiles;
+  const int group = lin / (kGroupM * ntiles), first_m = group * kGroupM;
+  const int gm = min(mtiles - first_m, kGroupM), within = lin - group * kGroupM * ntiles;
+  const int mt = first_m + within % gm, nt = within / gm;
   const int m0 = mt * TBM, n0 = nt * TBN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
