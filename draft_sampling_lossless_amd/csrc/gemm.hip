@@ -312,6 +312,115 @@ __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, 
     }
 }
 
+// ------------------------------------------------------------------ big tiles
+
+// 256 x 256 output tiles, BK = 64, a two-stage LDS ring filled by global->LDS DMA
+// (every load instruction moves 8 rows x 128 B), four waves of 128 x 128 (8 x 8
+// fragments of 16x16, accumulators in AGPRs).  Per 64-k step a wave reads 32 KB of
+// fragments for 128 MFMAs, half the LDS bytes per MFMA of 64 x 64 wave tiles, and one
+// barrier covers 128 MFMAs.  LDS row = 64 k = eight 16-byte pieces; logical piece q
+// of row r sits at piece q ^ ((r >> 1) & 7), so the 16 rows one fragment reads at a k
+// offset fall into 16 distinct bank groups.  Requires H % 64 == 0.
+constexpr int BBM = 256, BBN = 256, BBK = 64, BNS = 2;
+constexpr int BSTAGE = (BBM + BBN) * BBK * 2;  // 64 KB
+constexpr int BLDS = BNS * BSTAGE;             // 128 KB
+
+__device__ __forceinline__ void dma16_g(const uint16_t* src, char* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
+__global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                                              float* __restrict__ C, int M, int H, int Vd, int mtiles,
+                                              int ntiles) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int kGroupM = 4;
+  const int total = mtiles * ntiles;
+  const int per_xcd = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int group = lin / (kGroupM * ntiles), first_m = group * kGroupM;
+  const int gm = min(mtiles - first_m, kGroupM), within = lin - group * kGroupM * ntiles;
+  const int mt = first_m + within % gm, nt = within / gm;
+  const int m0 = mt * BBM, n0 = nt * BBN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n = lane & 15, g = lane >> 4;
+
+  // DMA: instruction u (0..7) of this wave fills A rows (and W rows) 64 wave + 8 u .. +7;
+  // lane L takes row 8 u + L / 8 of the wave's 64, physical piece L % 8, which holds
+  // logical piece (L % 8) ^ ((row >> 1) & 7), row = 64 wave + 8 u + L / 8
+  const uint16_t* asrc[8];
+  const uint16_t* wsrc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int r = wave * 64 + 8 * u + (lane >> 3);
+    const int lg = (lane & 7) ^ ((r >> 1) & 7);
+    asrc[u] = A + (size_t)min(m0 + r, M - 1) * H + lg * 8;   // rows past M: a valid row, never stored
+    wsrc[u] = W + (size_t)min(n0 + r, Vd - 1) * H + lg * 8;  // rows past Vd: likewise
+  }
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % BNS) * BSTAGE;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      dma16_g(asrc[u] + kt * BBK, st + (wave * 64 + 8 * u) * 128);
+      dma16_g(wsrc[u] + kt * BBK, st + BBM * 128 + (wave * 64 + 8 * u) * 128);
+    }
+  };
+
+  floatx4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment reads: row (16 i + n) of the wave's 128 rows, logical piece 4 s + g
+  const int swz = (n >> 1) & 7;
+  const int arow = (wm * 128 + n) * 128, brow = BBM * 128 + (wn * 128 + n) * 128;
+
+  const int KT = H / BBK;
+  issue(0);
+  for (int kt = 0; kt < KT; ++kt) {
+    // this wave's 16 DMA instructions of stage kt are done; after the barrier every
+    // wave's are, and every wave has finished reading stage kt - 1, whose buffer
+    // stage kt + 1 reuses
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kt + 1 < KT) issue(kt + 1);
+    const char* st = smem + (kt % BNS) * BSTAGE;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // all 16 fragment reads of the half step first (one LDS latency per half step)
+      const int pc = ((4 * s + g) ^ swz) * 16;
+      bf16x8 af[8], bf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + arow + i * 16 * 128 + pc));
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + brow + j * 16 * 128 + pc));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int col = n0 + wn * 128 + 16 * j + n;
+    if (col >= Vd) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = m0 + wm * 128 + 16 * i + 4 * g + q;
+        if (row < M) C[(size_t)row * Vd + col] = acc[i][j][q];
+      }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, float* logits, int M, int H,
@@ -331,6 +440,20 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
       hipLaunchKernelGGL((k1_skinny<FR, 2>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd);
     else
       hipLaunchKernelGGL((k1_skinny<FR, 4>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd);
+  } else if (H % BBK == 0) {
+    static bool attr_set[64] = {false};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
+      if (e != hipSuccess) return e;
+      attr_set[dev] = true;
+    }
+    const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vd + BBN - 1) / BBN;
+    const int per_xcd = (mtiles * ntiles + 7) / 8;
+    hipLaunchKernelGGL(k1_big, dim3(per_xcd * 8), dim3(256), BLDS, stream, hidden, lm_head, logits, M, H, Vd, mtiles,
+                       ntiles);
   } else {
     const int mtiles = (M + TBM - 1) / TBM, ntiles = (Vd + TBN - 1) / TBN;
     const int total = mtiles * ntiles;

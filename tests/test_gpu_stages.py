@@ -54,7 +54,8 @@ def test_race_exponentials_bit_exact(n, pos, req, tag):
 @pytest.mark.parametrize("M,H,Vd", [(8, 256, 1024), (20, 264, 1000), (40, 256, 996), (1, 4096, 4096),
                                     (300, 200, 1004), (129, 4096, 640), (64, 64, 68),
                                     (8, 4096, 4100), (16, 512, 1000), (13, 1024, 72), (1, 2048, 65540),
-                                    (8, 4096, 8)])
+                                    (8, 4096, 8), (257, 128, 1000), (520, 96, 300), (96, 32, 260), (300, 64, 500),
+                                    (700, 4096, 2000)])
 def test_draft_logits_small(M, H, Vd):
     say(f"draft_logits M={M} H={H} Vd={Vd}")
     g = np.random.default_rng(M * 7 + H)
