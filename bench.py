@@ -219,7 +219,8 @@ def k1_roofline(w, k1_ms):
     if w.M <= 16 and w.H % 512 == 0 and w.H <= 4096:
         roof["kernel"] = "draft_logits (k1_stream)"
     else:
-        roof["kernel"] = "draft_logits (k1_skinny)" if w.M <= 64 else "draft_logits (k1_tiled)"
+        roof["kernel"] = ("draft_logits (k1_skinny)" if w.M <= 64 else
+                          "draft_logits (k1_big)" if w.H % 64 == 0 else "draft_logits (k1_tiled)")
     roof["traffic"] = measured_traffic(w)
     return roof
 
