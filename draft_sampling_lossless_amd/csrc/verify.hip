@@ -358,6 +358,26 @@ __device__ __forceinline__ void race_update(float r, float E, int v, float& br, 
   }
 }
 
+
+// A pruning threshold for the exponential race: the exact (r, E) of one real candidate,
+// the lane best with the largest approximate key r / E in this wave (uniform).  Any
+// entry with r * tE < tr * E_lo (E_lo a lower bound of its E) loses strictly to that
+// candidate, so it can never be the race's winner.
+__device__ __forceinline__ void race_threshold(float br, float bE, float& tr, float& tE) {
+  const float key = br * __builtin_amdgcn_rcpf(bE);  // r = 0 ("nobody"): key 0
+  const float kmax = wave_max_f32(key);
+  const uint64_t hit = __ballot(key == kmax);
+  const int src = hit ? (int)__builtin_ctzll(hit) : 0;
+  tr = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(br), src));
+  tE = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(bE), src));
+}
+
+// E = -plog2(u) >= -log2(u) (1 - 2^-20) >= (1 - u) / ln 2 (1 - 2^-20): -ln u >= 1 - u, and
+// the portable log2 is within a few ulp of log2.  kEloScale is 1/ln 2 rounded down,
+// times (1 - 2^-16); kPrune absorbs the rounding of the two products of the test.
+constexpr float kEloScale = 1.4426949f * (1.0f - 0x1p-16f);
+constexpr float kPrune = 1.0f - 0x1p-20f;
+
 __global__ __launch_bounds__(256) void verify_sample(int input_kind, const float* __restrict__ target,
                                                      const float* __restrict__ draft,
                                                      const float* __restrict__ draft_log_z,
@@ -395,6 +415,7 @@ __global__ __launch_bounds__(256) void verify_sample(int input_kind, const float
   // to everything with r > 0, and index order decides among r = 0.
   float br = 0.0f, bE = 1.0f, fr = 0.0f, fE = 1.0f, asum = 0.0f;
   int bv = 0x7FFFFFFF, fv = 0x7FFFFFFF;
+  float tr = 0.0f, tE = 1.0f, tfr = 0.0f, tfE = 1.0f;  // wave thresholds (nobody: prunes nothing)
   for (int i0 = lo4 + tid; i0 < hi4; i0 += 256 * kB) {
     // every load of the batch first (clamped indices), then the arithmetic
     float4 q[kB];
@@ -464,15 +485,24 @@ __global__ __launch_bounds__(256) void verify_sample(int input_kind, const float
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const float E = -plog2(uniform01(ws[f]));
-          if (jb.mode == kJobResid) {
-            race_update(fmaxf(0.0f, __fsub_rn(pt[f], pd[f])), E, v + f, br, bE, bv);
-            race_update(pt[f], E, v + f, fr, fE, fv);
-          } else {
-            race_update(pt[f], E, v + f, br, bE, bv);
+          const float u01 = uniform01(ws[f]);
+          const float elo = (1.0f - u01) * kEloScale;
+          const float rr = (jb.mode == kJobResid) ? fmaxf(0.0f, __fsub_rn(pt[f], pd[f])) : pt[f];
+          // (a threshold product near the denormal range never prunes)
+          const float lim = (tr * elo) * kPrune, limf = (tfr * elo) * kPrune;
+          const bool need = !(lim > 0x1p-100f && rr * tE < lim);
+          const bool needf = jb.mode == kJobResid && !(limf > 0x1p-100f && pt[f] * tfE < limf);
+          if (need || needf) {  // the exact log2 only for entries that can still win
+            const float E = -plog2(u01);
+            if (need) race_update(rr, E, v + f, br, bE, bv);
+            if (needf) race_update(pt[f], E, v + f, fr, fE, fv);
           }
         }
       }
+    }
+    if (do_race) {  // refresh the thresholds from this wave's bests
+      race_threshold(br, bE, tr, tE);
+      if (jb.mode == kJobResid) race_threshold(fr, fE, tfr, tfE);
     }
   }
   __shared__ RacePartial red[4];
