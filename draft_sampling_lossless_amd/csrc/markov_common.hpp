@@ -155,24 +155,6 @@ __device__ __forceinline__ MarkovPartial load_partial(const MarkovPartial* p) {
   return v;
 }
 
-// Grid barrier of the cooperative launch (every workgroup is resident).  The
-// __syncthreads() before it completes this workgroup's partial stores; one thread
-// arrives on a monotonic counter and waits until all G workgroups of this round
-// have.  The wait is bounded (about 0.1 s) so that a broken launch can never hang
-// the device; the co-residency of a cooperative launch makes it unreachable.
-__device__ __forceinline__ void grid_barrier(unsigned* ctr, unsigned target) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int spin = 0; spin < (1 << 22); ++spin) {
-      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  __syncthreads();
-}
-
-
 // Merge every workgroup's partial of request b (one wave; all lanes get the result).
 __device__ __forceinline__ MarkovPartial wave_merge(const MarkovPartial* __restrict__ part, int count, int lane) {
   float key = -INFINITY, m = -INFINITY, s = 0.0f;

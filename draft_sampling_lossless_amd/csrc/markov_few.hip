@@ -49,11 +49,12 @@
 //
 // Launch: an ordinary launch of one workgroup per slice (at most one per CU, by
 // its LDS size).  The grid barriers need every workgroup resident at once, which
-// an idle device gives but nothing guarantees, so the first workgroup to start
-// checks that all of them have started within a short window.  If they have, the
-// phases run as above; if not (the device is busy elsewhere), that workgroup runs
-// every phase for every slice by itself and the others return at once.  Either
-// way no workgroup ever waits for one that has not started.
+// an idle device gives but nothing guarantees.  Every workgroup runs phases A and
+// B of its own slice, which need no other workgroup; at the first barrier the
+// first workgroup to start checks that all of them arrive within a short window.
+// If they do, the phases go on as above; if not (the device is busy elsewhere),
+// that workgroup runs every phase for every slice by itself and the others
+// return.  Either way no workgroup ever waits for one that has not started.
 #include <math.h>
 #include <stdlib.h>
 
@@ -83,11 +84,26 @@ constexpr int kMisc = 512;       // ints of per-workgroup bookkeeping in LDS
 constexpr int kFixedScratch = 256 + 1024 + 4 * kMisc + 4 * kMaxSlice + 4 * kMaxSlices;  // + row / slice W2 norms
 constexpr uint64_t kArriveTicks = 5000;  // start-up window: 50 us of the 100 MHz real-time counter
 
+// Counters (32-bit words, zeroed before every launch).  Words 0..3: grid barrier
+// (groups arrived), workgroups done (groups finished), arrivals, mode.  Workgroup w
+// belongs to group w % kGroups; each group has its own barrier and done counters,
+// 128 bytes apart, so that no single address takes an atomic from every workgroup
+// (same-address atomics are served one at a time, ~20 ns each).
+constexpr int kGroups = 16;
+constexpr int kCtrWords = 32 + 32 * 2 * kGroups;
+__device__ __forceinline__ unsigned* ctr_group(unsigned* ctr, int kind, int grp) {
+  return ctr + 32 + 32 * (kind * kGroups + grp);
+}
+__device__ __forceinline__ unsigned group_size(int G, int grp) { return (unsigned)((G - grp + kGroups - 1) / kGroups); }
+__device__ __forceinline__ unsigned group_count(int G) { return (unsigned)min(G, kGroups); }
+constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0) (gfx9 encoding)
+
 // misc layout (ints)
 constexpr int kMsCnt = 0, kMsInc = 64, kMsOff = 128, kMsSel = 192, kMsPre = 256;  // [64] each ([65] for kMsPre)
 constexpr int kMsFs = 336, kMsFit = 337, kMsPairs = 338, kMsTot = 339, kMsRole = 340, kMsTicket = 341;
 constexpr int kMsPrev = 352, kMsFst = 368;  // [16] each (per-step pass)
 constexpr int kMsN1 = 384;                  // [16] floats: largest recorded W1 norm per request (phase B)
+constexpr int kMsT = 400, kMsRid = 416, kMsAnc = 432;  // [16] each: temperature, request id, anchor per request
 
 // a recorded entry is two words: (key bits << 32 | draft index (-1: none)) and
 // (||W1[t(j)]|| bits << 32 | ||W2[j]|| bits)
@@ -105,7 +121,7 @@ struct FewWs {
   MarkovPartial* partF;   // [2][B][G] per-step partials of that pass
   MarkovPartial* partD;   // [B*N][G] log-sum-exp partials of the processed rows
   uint32_t* rows;         // [B*N][r/2] W1 row (bf16 pairs) of each step's previous token
-  unsigned* ctr;          // [0] grid barrier, [1] workgroups done, [2] arrivals, [3] mode
+  unsigned* ctr;          // [kCtrWords] counters (see ctr_group)
 };
 
 struct FewArgs {
@@ -159,8 +175,13 @@ struct Lds {
   float* fk;          // [kPairs] full keys of (previous survivor, survivor) pairs
 };
 
-__global__ void zero_counters(unsigned* ctr) {
-  for (int q = 0; q < 4; ++q) ctr[q] = 0u;
+// per-request parameters (copied into LDS after phase B)
+__device__ __forceinline__ float req_temperature(const Lds& L, int b) { return reinterpret_cast<const float*>(L.misc)[kMsT + b]; }
+__device__ __forceinline__ uint32_t req_id(const Lds& L, int b) { return reinterpret_cast<const uint32_t*>(L.misc)[kMsRid + b]; }
+__device__ __forceinline__ int req_anchor(const Lds& L, int b) { return L.misc[kMsAnc + b]; }
+
+__global__ __launch_bounds__(256) void zero_counters(unsigned* ctr) {
+  for (int q = threadIdx.x; q < kCtrWords; q += 256) ctr[q] = 0u;
 }
 
 // half-width of a full key's interval around the bias-free key, per unit of W2
@@ -405,17 +426,193 @@ __device__ __forceinline__ float load_slice(const FewArgs& a, const Lds& L, cons
 }
 
 // ------------------------------------------------------------------------ phases A, B
-__device__ __forceinline__ void phase_ab(const FewArgs& a, const Lds& L, int vwg, int G) {
+// One batch of a slice's W2 pieces (power-of-two kc): the loads, issued on their own
+// so that other work can run while they are in flight ...
+__device__ __forceinline__ void w2_issue(const FewArgs& a, const Slice& sl, int p0, uint4 (&v)[kFly]) {
+  const int kc = a.r / 8;
+  const uint4* src = reinterpret_cast<const uint4*>(a.w2 + (size_t)sl.vbase * a.r);
+#pragma unroll
+  for (int u = 0; u < kFly; ++u) v[u] = load_clamped(src, p0 + (int)threadIdx.x + 256 * u, sl.nvalid * kc, kc);
+}
+
+// ... and their use: into LDS (slot-permuted per 64-chunk for the MFMA B operand),
+// each row's norm into w2n; returns this thread's largest squared row norm
+__device__ __forceinline__ float w2_consume(const FewArgs& a, const Lds& L, const Slice& sl, int p0,
+                                            const uint4 (&v)[kFly]) {
+  const int kc = a.r / 8, lg = __builtin_ctz(kc), row_bytes = 2 * a.r + 16;
+  const int pieces = sl.nch * kChunk * kc;
+  float n2 = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kFly; ++u) {
+    const int p = p0 + (int)threadIdx.x + 256 * u;
+    if (p < pieces) {  // uniform per wave
+      const int rho_all = p >> lg, piece = p & (kc - 1);
+      const float ss = group_sum(sumsq8(v[u]), kc);
+      n2 = fmaxf(n2, ss);
+      if (piece == 0) L.w2n[rho_all] = sqrtf(ss);
+      const int c = rho_all >> 6, rho = rho_all & (kChunk - 1);
+      const int slot = c * kChunk + (rho & 3) * 16 + (rho >> 2);
+      *reinterpret_cast<uint4*>(L.w2s + (size_t)slot * row_bytes + piece * 16) = v[u];
+    }
+  }
+  return n2;
+}
+
+// Rows row0 .. row0+kRowBatch-1: base logits at this thread's four entries, and
+// each row's temperature and request id.  Every load is issued here, unguarded
+// (clamped indices: invalid lanes and rows never use the value), so that one wait
+// covers them all.
+struct RowBatch {
+  float4 bv[kRowBatch];
+  float T[kRowBatch];
+  uint32_t rid[kRowBatch];
+};
+// (The per-row values are loaded per lane: as wave-uniform values the compiler
+// would move each into a scalar register at once, waiting for every load before.)
+__device__ __forceinline__ void load_rows(const FewArgs& a, const Slice& sl, int row0, RowBatch& rb) {
+  const int rows = a.B * a.N, jq = sl.vbase + 4 * (int)threadIdx.x;
+  int lane_zero = 0;
+  asm volatile("" : "+v"(lane_zero));
+#pragma unroll
+  for (int rr = 0; rr < kRowBatch; ++rr) {
+    const int row = min(row0 + rr, rows - 1);
+    rb.bv[rr] = *reinterpret_cast<const float4*>(a.logits + (size_t)row * a.Vd + min(jq, sl.vbase + sl.nvalid - 4));
+    rb.T[rr] = a.temperature[row / a.N + lane_zero];
+    rb.rid[rr] = a.request_id[row / a.N + lane_zero];
+  }
+}
+
+// bias-free keys of a row batch; every wave's best two entries of each row into
+// red64[(row * 4 + wave) * kTop ..]
+__device__ __forceinline__ void keys_batch(const FewArgs& a, const Slice& sl, int row0, const RowBatch& rb,
+                                           uint64_t* red64) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = a.N, rows = a.B * a.N;
+  const bool qv = 4 * tid < sl.nvalid;  // this thread's entries jq .. jq+3
+  const int jq = sl.vbase + 4 * tid;
+#pragma unroll
+  for (int rr = 0; rr < kRowBatch; ++rr) {
+    const int row = row0 + rr;
+    if (row >= rows) break;  // uniform
+    // this lane's best two entries (ties: smaller index), then the wave's: the
+    // lowest lane holding the maximum has the smallest index among equal keys
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+    const float T = rb.T[rr];
+    const uint32_t rid = rb.rid[rr];
+    if (qv) {
+      const int i = row - (row / N) * N;
+      float key[4];
+      keys4(rb.bv[rr], T > 0.0f, temp_scale(T), jq, i, rid, a.key0, a.key1, key);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) o[f] = ord_of(key[f]);
+    }
+    int f1 = 0;
+#pragma unroll
+    for (int f = 1; f < 4; ++f)
+      if (o[f] > o[f1]) f1 = f;
+    int f2 = (f1 == 0) ? 1 : 0;
+#pragma unroll
+    for (int f = 1; f < 4; ++f)
+      if (f != f1 && o[f] > o[f2]) f2 = f;
+    const uint32_t own1 = o[f1], own2 = o[f2];
+    const uint32_t m1 = wave_max_u32(own1);
+    const int l1 = __builtin_ctzll(__ballot(own1 == m1));
+    const int j1 = __builtin_amdgcn_readlane(jq + f1, l1);
+    const uint32_t cand = (lane == l1) ? own2 : own1;
+    const int cj = (lane == l1) ? jq + f2 : jq + f1;
+    const uint32_t m2 = wave_max_u32(cand);
+    const int l2 = __builtin_ctzll(__ballot(cand == m2));
+    const int j2 = __builtin_amdgcn_readlane(cj, l2);
+    if (lane == 0) {
+      red64[(rr * 4 + wave) * kTop] = m1 ? (((uint64_t)m1 << 32) | (uint32_t)~j1) : 0ull;
+      red64[(rr * 4 + wave) * kTop + 1] = m2 ? (((uint64_t)m2 << 32) | (uint32_t)~j2) : 0ull;
+    }
+  }
+}
+
+// the slice's best two entries of each row of the batch (from the waves' in
+// red64, written before the last barrier), and their records: key and index,
+// ||W2[j]|| (from LDS) and ||W1[t(j)]|| (kc lanes per entry)
+__device__ __forceinline__ void records_batch(const FewArgs& a, const Lds& L, const Slice& sl, int vwg, int G, int row0,
+                                              uint64_t* red64, float* n1r) {
+  const int tid = threadIdx.x;
   const int r = a.r, kc = r / 8, N = a.N, rows = a.B * a.N;
+  const bool pow2 = (kc & (kc - 1)) == 0;
+  const int lg = __builtin_ctz(kc);
+  uint64_t* best = red64 + kRowBatch * 4 * kTop;  // [kRowBatch][kTop] ranks of the slice
+  if (tid < kRowBatch && row0 + tid < rows) {
+    uint64_t t1 = 0, t2 = 0;
+    for (int w = 0; w < 4; ++w) merge2(t1, t2, red64[(tid * 4 + w) * kTop], red64[(tid * 4 + w) * kTop + 1]);
+    best[tid * kTop] = t1;
+    best[tid * kTop + 1] = t2;
+  }
+  __syncthreads();
+  const int ne = kRowBatch * kTop;
+  for (int p = tid; p < ne * kc; p += 256) {  // (whole groups of kc lanes)
+    const int e = pow2 ? (p >> lg) : p / kc, piece = p - e * kc;
+    const int row = row0 + e / kTop;
+    const uint64_t rk = best[e];
+    const bool ok = row < rows && (rk >> 32) != 0;
+    const int j = ok ? (int)~(uint32_t)rk : sl.vbase;
+    const int t = min(max(target_of(a.d2t, j), 0), a.V - 1);
+    float ss;
+    if (pow2) {
+      ss = group_sum(sumsq8(*reinterpret_cast<const uint4*>(a.w1 + (size_t)t * r + piece * 8)), kc);
+    } else {
+      ss = row_norm2(a.w1 + (size_t)t * r, r);  // (every lane of the entry; one stores)
+    }
+    if (piece == 0 && row < rows) {
+      uint64_t w0 = kEmptySlot, w1w = 0;
+      if (ok) {
+        const float n1e = sqrtf(ss);
+        w0 = ((uint64_t)__float_as_uint(key_of((uint32_t)(rk >> 32))) << 32) | (uint32_t)j;
+        w1w = ((uint64_t)__float_as_uint(n1e) << 32) | __float_as_uint(L.w2n[j - sl.vbase]);
+        const int b = row / N;
+        if (row - b * N < N - 1) atomicMax(reinterpret_cast<int*>(n1r) + b, __float_as_int(n1e));
+      }
+      uint64_t* dst = a.ws.rec + (((size_t)row * G + vwg) * kTop + (e % kTop)) * 2;
+      st_u64(dst, w0);
+      st_u64(dst + 1, w1w);
+    }
+  }
+  __syncthreads();
+}
+
+// Phases A and B of one slice.  The first row batch's base logits and the first
+// W2 batch are requested together, and that row batch's keys are computed while
+// the W2 rows are still in flight.
+__device__ __forceinline__ void phase_ab(const FewArgs& a, const Lds& L, int vwg, int G) {
+  const int tid = threadIdx.x;
+  const int r = a.r, kc = r / 8, rows = a.B * a.N;
   const bool pow2 = (kc & (kc - 1)) == 0;
   const int lg = __builtin_ctz(kc);
   const Slice sl = slice_of(a, vwg);
   float* n1r = reinterpret_cast<float*>(L.misc + kMsN1);  // per request (non-negative: int order = float order)
+  uint64_t* red64 = reinterpret_cast<uint64_t*>(L.redf);  // [kRowBatch][4 waves][kTop], then [kRowBatch][kTop]
+  float* red_n2 = L.redf + 192;                           // (past both)
   if (tid < 16) n1r[tid] = 0.0f;
-  const float n2 = block_max(load_slice<true>(a, L, sl), L.redf);
+  RowBatch rb;
+  load_rows(a, sl, 0, rb);
+  float n2 = 0.0f;
+  if (pow2) {
+    const int pieces = sl.nch * kChunk * kc;
+    uint4 v[kFly];
+    __builtin_amdgcn_sched_barrier(0);  // (every load issued before the keys use any)
+    w2_issue(a, sl, 0, v);
+    __builtin_amdgcn_sched_barrier(0);
+    keys_batch(a, sl, 0, rb, red64);
+    n2 = w2_consume(a, L, sl, 0, v);
+    for (int p0 = 256 * kFly; p0 < pieces; p0 += 256 * kFly) {
+      w2_issue(a, sl, p0, v);
+      n2 = fmaxf(n2, w2_consume(a, L, sl, p0, v));
+    }
+    __syncthreads();
+  } else {
+    keys_batch(a, sl, 0, rb, red64);
+    n2 = load_slice<true>(a, L, sl);
+  }
+  n2 = block_max(n2, red_n2);
   if (tid == 0) st_f(a.ws.norms + vwg, n2);
-  __syncthreads();  // (the reduction scratch is reused below)
   // the anchors' W1 norms (slice 0 only: each request's bound needs them once)
   if (vwg == 0) {
     if (pow2) {
@@ -430,92 +627,12 @@ __device__ __forceinline__ void phase_ab(const FewArgs& a, const Lds& L, int vwg
       atomicMax(reinterpret_cast<int*>(n1r) + tid, __float_as_int(sqrtf(row_norm2(a.w1 + (size_t)t * r, r))));
     }
   }
-  // bias-free keys; each row's best two entries of the slice
-  uint64_t* red64 = reinterpret_cast<uint64_t*>(L.redf);  // [kRowBatch][4 waves][kTop]
-  uint64_t* best = red64 + kRowBatch * 4 * kTop;          // [kRowBatch][kTop] ranks of the slice
-  const bool qv = 4 * tid < sl.nvalid;                    // this thread's entries jq .. jq+3
-  const int jq = sl.vbase + 4 * tid;
-  for (int row0 = 0; row0 < rows; row0 += kRowBatch) {
-    float4 bv[kRowBatch];
-#pragma unroll
-    for (int rr = 0; rr < kRowBatch; ++rr)  // (clamped: invalid lanes never use the value)
-      bv[rr] = *reinterpret_cast<const float4*>(a.logits + (size_t)min(row0 + rr, rows - 1) * a.Vd +
-                                                min(jq, sl.vbase + sl.nvalid - 4));
-#pragma unroll
-    for (int rr = 0; rr < kRowBatch; ++rr) {
-      const int row = row0 + rr;
-      if (row >= rows) break;  // uniform
-      // this lane's best two entries (ties: smaller index), then the wave's: the
-      // lowest lane holding the maximum has the smallest index among equal keys
-      uint32_t o[4] = {0u, 0u, 0u, 0u};
-      if (qv) {
-        const int b = row / N, i = row - b * N;
-        const float T = a.temperature[b];
-        float key[4];
-        keys4(bv[rr], T > 0.0f, temp_scale(T), jq, i, a.request_id[b], a.key0, a.key1, key);
-#pragma unroll
-        for (int f = 0; f < 4; ++f) o[f] = ord_of(key[f]);
-      }
-      int f1 = 0;
-#pragma unroll
-      for (int f = 1; f < 4; ++f)
-        if (o[f] > o[f1]) f1 = f;
-      int f2 = (f1 == 0) ? 1 : 0;
-#pragma unroll
-      for (int f = 1; f < 4; ++f)
-        if (f != f1 && o[f] > o[f2]) f2 = f;
-      const uint32_t own1 = o[f1], own2 = o[f2];
-      const uint32_t m1 = wave_max_u32(own1);
-      const int l1 = __builtin_ctzll(__ballot(own1 == m1));
-      const int j1 = __builtin_amdgcn_readlane(jq + f1, l1);
-      const uint32_t cand = (lane == l1) ? own2 : own1;
-      const int cj = (lane == l1) ? jq + f2 : jq + f1;
-      const uint32_t m2 = wave_max_u32(cand);
-      const int l2 = __builtin_ctzll(__ballot(cand == m2));
-      const int j2 = __builtin_amdgcn_readlane(cj, l2);
-      if (lane == 0) {
-        red64[(rr * 4 + wave) * kTop] = m1 ? (((uint64_t)m1 << 32) | (uint32_t)~j1) : 0ull;
-        red64[(rr * 4 + wave) * kTop + 1] = m2 ? (((uint64_t)m2 << 32) | (uint32_t)~j2) : 0ull;
-      }
-    }
+  records_batch(a, L, sl, vwg, G, 0, red64, n1r);
+  for (int row0 = kRowBatch; row0 < rows; row0 += kRowBatch) {
+    load_rows(a, sl, row0, rb);
+    keys_batch(a, sl, row0, rb, red64);
     __syncthreads();
-    if (tid < kRowBatch && row0 + tid < rows) {
-      uint64_t t1 = 0, t2 = 0;
-      for (int w = 0; w < 4; ++w) merge2(t1, t2, red64[(tid * 4 + w) * kTop], red64[(tid * 4 + w) * kTop + 1]);
-      best[tid * kTop] = t1;
-      best[tid * kTop + 1] = t2;
-    }
-    __syncthreads();
-    // the records: key and index, ||W2[j]|| (from LDS) and ||W1[t(j)]|| (kc lanes per row)
-    const int ne = kRowBatch * kTop;
-    for (int p = tid; p < ne * kc; p += 256) {  // (whole groups of kc lanes)
-      const int e = pow2 ? (p >> lg) : p / kc, piece = p - e * kc;
-      const int row = row0 + e / kTop;
-      const uint64_t rk = best[e];
-      const bool ok = row < rows && (rk >> 32) != 0;
-      const int j = ok ? (int)~(uint32_t)rk : sl.vbase;
-      const int t = min(max(target_of(a.d2t, j), 0), a.V - 1);
-      float ss;
-      if (pow2) {
-        ss = group_sum(sumsq8(*reinterpret_cast<const uint4*>(a.w1 + (size_t)t * r + piece * 8)), kc);
-      } else {
-        ss = row_norm2(a.w1 + (size_t)t * r, r);  // (every lane of the entry; one stores)
-      }
-      if (piece == 0 && row < rows) {
-        uint64_t w0 = kEmptySlot, w1w = 0;
-        if (ok) {
-          const float n1e = sqrtf(ss);
-          w0 = ((uint64_t)__float_as_uint(key_of((uint32_t)(rk >> 32))) << 32) | (uint32_t)j;
-          w1w = ((uint64_t)__float_as_uint(n1e) << 32) | __float_as_uint(L.w2n[j - sl.vbase]);
-          const int b = row / N;
-          if (row - b * N < N - 1) atomicMax(reinterpret_cast<int*>(n1r) + b, __float_as_int(n1e));
-        }
-        uint64_t* dst = a.ws.rec + (((size_t)row * G + vwg) * kTop + (e % kTop)) * 2;
-        st_u64(dst, w0);
-        st_u64(dst + 1, w1w);
-      }
-    }
-    __syncthreads();
+    records_batch(a, L, sl, vwg, G, row0, red64, n1r);
   }
   if (tid < a.B) st_f(a.ws.n1 + (size_t)tid * G + vwg, n1r[tid]);
 }
@@ -544,7 +661,6 @@ __device__ __forceinline__ void publish_row_from(const FewArgs& a, int b, int st
 __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, int G) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.N, r = a.r, cap = a.cap, kc = r / 8, half = r / 2;
-  const float c = temp_scale(a.temperature[b]);
   const int per = G * kTop;  // recorded entries of one step (<= 64 * kPerLane)
   const uint64_t* recb = a.ws.rec + (size_t)b * N * per * 2;
   int* cnt = L.misc + kMsCnt;
@@ -552,18 +668,9 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
   int* offp = L.misc + kMsOff;
   int* sel = L.misc + kMsSel;
   int* pre = L.misc + kMsPre;
-  // n1 for this request and every slice's largest W2 row norm
-  float n1 = 0.0f;
-  for (int q = tid; q < G; q += 256) {
-    n1 = fmaxf(n1, ld_f(a.ws.n1 + (size_t)b * G + q));
-    L.n2s[q] = sqrtf(ld_f(a.ws.norms + q));
-  }
-  n1 = block_max(n1, L.redf);  // (its barriers also publish n2s)
-  const float cb = bias_bound(c, n1);
-  // survivors of every step: one wave per step, two steps per round; compaction by
-  // ballot into the step's own LDS region
-  for (int i0 = wave; i0 < N; i0 += 8) {
-    uint64_t h[2][kPerLane], hn[2][kPerLane];
+  // recorded entries of steps i0 and i0 + 4 (this wave's steps of one round)
+  uint64_t h[2][kPerLane], hn[2][kPerLane];
+  auto load_recs = [&](int i0) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int i = min(i0 + 4 * st, N - 1);
@@ -574,6 +681,22 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
         hn[st][u] = ld_u64(e + 1);
       }
     }
+  };
+  // the first round's records are requested together with the norms below
+  load_recs(wave);
+  // n1 for this request and every slice's largest W2 row norm
+  float n1 = 0.0f;
+  for (int q = tid; q < G; q += 256) {
+    n1 = fmaxf(n1, ld_f(a.ws.n1 + (size_t)b * G + q));
+    L.n2s[q] = sqrtf(ld_f(a.ws.norms + q));
+  }
+  const float c = temp_scale(req_temperature(L, b));
+  n1 = block_max(n1, L.redf);  // (its barriers also publish n2s)
+  const float cb = bias_bound(c, n1);
+  // survivors of every step: one wave per step, two steps per round; compaction by
+  // ballot into the step's own LDS region
+  for (int i0 = wave; i0 < N; i0 += 8) {
+    if (i0 != wave) load_recs(i0);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int i = i0 + 4 * st;
@@ -635,7 +758,7 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
     // stage: W1[anchor] -> w1c row 0; survivor (i, q) (compact index pre[i] + q): its
     // W2 row -> w2c row i*cap+q, the W1 row of its target -> w1c row 1+i*cap+q
     const int np = kc * (1 + 2 * tot);
-    const int anc = min(max(a.anchor[b], 0), a.V - 1);
+    const int anc = min(max(req_anchor(L, b), 0), a.V - 1);
     for (int p0 = 0; p0 < np; p0 += 256 * kStage) {
       uint4 v[kStage];
       uint16_t* dst[kStage];
@@ -711,7 +834,7 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
     // too many survivors to stage or tabulate: lanes take recorded entries and
     // read weight rows from global memory, one step at a time
     if (wave == 0) {
-      int prev = a.anchor[b];
+      int prev = req_anchor(L, b);
       for (int i = 0; i < fs; ++i) {
         const uint16_t* e1 = a.w1 + (size_t)min(max(prev, 0), a.V - 1) * r;
         float bk = -INFINITY;
@@ -737,7 +860,7 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
       }
     }
     __syncthreads();
-    for (int i = 0; i < fs; ++i) publish_row_from(a, b, i, (i == 0) ? a.anchor[b] : sel[i - 1], tid, 256);
+    for (int i = 0; i < fs; ++i) publish_row_from(a, b, i, (i == 0) ? req_anchor(L, b) : sel[i - 1], tid, 256);
   }
   if (tid == 0) st_i(a.ws.fstep + b, fs);
   __syncthreads();
@@ -770,14 +893,14 @@ __device__ __forceinline__ void step_partial(const FewArgs& a, const Lds& L, con
     for (int i = 0; i < 4; ++i) {
       const int b = 4 * g + i;
       if (b >= B || fstl[b] > s) continue;
-      const float T = a.temperature[b];
+      const float T = req_temperature(L, b);
       float4 v = *reinterpret_cast<const float4*>(a.logits + ((size_t)b * N + s) * a.Vd + jb);
       v.x += acc[0][i];
       v.y += acc[1][i];
       v.z += acc[2][i];
       v.w += acc[3][i];
       float key[4];
-      keys4(v, T > 0.0f, temp_scale(T), jb, s, a.request_id[b], a.key0, a.key1, key);
+      keys4(v, T > 0.0f, temp_scale(T), jb, s, req_id(L, b), a.key0, a.key1, key);
 #pragma unroll
       for (int f = 0; f < 4; ++f)
         if (key_beats(key[f], tgt[f], bkey[i], btok[i])) {
@@ -842,7 +965,7 @@ __device__ __forceinline__ void phase_d(const FewArgs& a, const Lds& L, const Sl
       for (int i = 0; i < 4; ++i) cur[u][i] = pre[u][i];
     if (t + 1 < ntiles) load_tile(pre, a.logits, t + 1, tpr, B, N, a.Vd, sl.vbase, wave, n, g);
     const int b = t / tpr, st0 = (t - b * tpr) * 16;
-    const float c = temp_scale(a.temperature[b]);
+    const float c = temp_scale(req_temperature(L, b));
     // MFMA rows = steps st0 .. st0+15 of request b; lane row n is step st0 + n
     const int sn = st0 + n;
     bf16x8 efrag[kMaxKSteps];
@@ -895,39 +1018,99 @@ __device__ __forceinline__ void phase_d(const FewArgs& a, const Lds& L, const Sl
   }
 }
 
-// role of this workgroup: 0 return at once, 1 run its slice, 2 run every slice alone
-__device__ __forceinline__ int arrive(const FewArgs& a, int G, int* misc) {
+// Arrival at grid barrier `round` (1, 2, ...).  Every thread first waits for its
+// own stores, so that whatever this workgroup published before the barrier is in
+// memory when the barrier counts it; the last workgroup of each group to arrive
+// counts the group.
+__device__ __forceinline__ void barrier_arrive(unsigned* ctr, unsigned round, int G) {
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int grp = (int)blockIdx.x % kGroups;
+    const unsigned old = __hip_atomic_fetch_add(ctr_group(ctr, 0, grp), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1u == round * group_size(G, grp))
+      __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// thread 0: whether every group has arrived at barrier `round`
+__device__ __forceinline__ bool barrier_done(unsigned* ctr, unsigned round, int G) {
+  return ld_u(ctr) >= round * group_count(G);
+}
+
+// The wait is bounded (about 0.1 s) so that a broken launch can never hang the device.
+__device__ __forceinline__ void grid_barrier(unsigned* ctr, unsigned round, int G) {
+  barrier_arrive(ctr, round, G);
+  if (threadIdx.x == 0)
+    for (int spin = 0; spin < (1 << 22) && !barrier_done(ctr, round, G); ++spin) __builtin_amdgcn_s_sleep(1);
+  __syncthreads();
+}
+
+// Role of this workgroup at the first barrier: 0 return at once, 1 go on with its
+// slice, 2 run every slice alone.  The first workgroup to start (`first`) waits
+// for every group within a window; if the window ends first, it closes the
+// barrier (a flag bit in the group count) unless the count has just completed,
+// and runs alone.  Every workgroup goes on once the count is complete and returns
+// once the barrier is closed, so no workgroup ever waits for one that has not
+// started.  With `force_solo` the first workgroup closes the barrier before it
+// arrives itself, so the count can never complete.
+constexpr unsigned kClosed = 0x80000000u;
+__device__ __forceinline__ void close_first_barrier(unsigned* ctr) {
+  __hip_atomic_fetch_or(ctr, kClosed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int first_barrier_role(const FewArgs& a, int G, bool first, int* misc) {
   unsigned* ctr = a.ws.ctr;
   if (threadIdx.x == 0) {
-    const unsigned k = __hip_atomic_fetch_add(ctr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int role;
-    if (k == 0) {
-      unsigned mode = a.force_solo ? 2u : 1u;
-      if (!a.force_solo) {
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (ld_u(ctr + 2) < (unsigned)G) {
-          if (__builtin_amdgcn_s_memrealtime() - t0 > kArriveTicks) {
-            mode = 2u;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
+    const unsigned target = group_count(G);
+    int role = 0;
+    if (first && a.force_solo) {
+      role = 2;
+    } else if (first) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      for (;;) {
+        if (ld_u(ctr) >= target) {
+          role = 1;
+          break;
         }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kArriveTicks) {
+          const unsigned old = __hip_atomic_fetch_or(ctr, kClosed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          role = (old >= target) ? 1 : 2;  // (old has no flag: only this workgroup sets it)
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
-      st_u(ctr + 3, mode);
-      role = (int)mode;
     } else {
-      // the first workgroup decides within its window; the bound only guards a broken launch
-      unsigned mode = 0u;
-      for (int spin = 0; spin < (1 << 22) && mode == 0u; ++spin) {
-        mode = ld_u(ctr + 3);
-        if (mode == 0u) __builtin_amdgcn_s_sleep(1);
+      // the first workgroup settles it within its window; the bound only guards a broken launch
+      for (int spin = 0; spin < (1 << 22); ++spin) {
+        const unsigned v = ld_u(ctr);
+        if (v & kClosed) break;
+        if (v >= target) {
+          role = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
-      role = (mode == 1u) ? 1 : 0;
     }
     misc[kMsRole] = role;
   }
   __syncthreads();
   return misc[kMsRole];
+}
+
+// Whether this workgroup is the last one to finish (the counts of every group).
+__device__ __forceinline__ bool last_to_finish(unsigned* ctr, int G, int* misc) {
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int grp = (int)blockIdx.x % kGroups;
+    int last = 0;
+    const unsigned old = __hip_atomic_fetch_add(ctr_group(ctr, 1, grp), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1u == group_size(G, grp))
+      last = __hip_atomic_fetch_add(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == group_count(G);
+    misc[kMsTicket] = last;
+  }
+  __syncthreads();
+  return misc[kMsTicket] != 0;
 }
 
 __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
@@ -952,21 +1135,44 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
   L.tgt = reinterpret_cast<int*>(creg + cr.tgt);
   L.fk = reinterpret_cast<float*>(creg + cr.fk);
 
-  const int role = arrive(a, G, L.misc);
+  // arrival order (the first to start decides the mode at the first barrier); its
+  // value is only needed after phase A/B
+  // (the empty asm statements keep the compiler from waiting for it at once: a
+  // lane-varying address is left to that lane, and the result is first read after
+  // phase B)
+  unsigned arrival = 1u;
+  if (tid == 0) {
+    int zero = 0;
+    asm volatile("" : "+v"(zero));
+    arrival = __hip_atomic_fetch_add(a.ws.ctr + 2 + zero, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // per-request parameters, kept in LDS for the later phases (unguarded loads from a
+  // clamped index, stored once phase B no longer waits on anything)
+  const int pq = min(tid, B - 1);
+  const float p_t = a.temperature[pq];
+  const uint32_t p_rid = a.request_id[pq];
+  const int p_anc = a.anchor[pq];
+  phase_ab(a, L, wg, G);
+  if (tid < B) {
+    reinterpret_cast<float*>(L.misc)[kMsT + tid] = p_t;
+    reinterpret_cast<uint32_t*>(L.misc)[kMsRid + tid] = p_rid;
+    L.misc[kMsAnc + tid] = p_anc;
+  }
+  if (tid == 0 && arrival == 0u && a.force_solo) close_first_barrier(a.ws.ctr);
+  barrier_arrive(a.ws.ctr, 1u, G);
+  float4 pre[kMaxCPW][4];  // base logits of the first phase-D tile, read while the chain runs
+  load_tile(pre, a.logits, 0, (N + 15) / 16, B, N, a.Vd, slice_of(a, wg).vbase, wave, n, g);
+  const int role = first_barrier_role(a, G, arrival == 0u, L.misc);
   if (role == 0) return;
   const bool solo = role == 2;
   const int v0 = solo ? 0 : wg, v1 = solo ? G : wg + 1;  // slices this workgroup runs
-  unsigned round = 0;
-
-  for (int vwg = v0; vwg < v1; ++vwg) phase_ab(a, L, vwg, G);
-  float4 pre[kMaxCPW][4];  // base logits of the first phase-D tile, read while the chain runs
-  if (!solo) {
-    load_tile(pre, a.logits, 0, (N + 15) / 16, B, N, a.Vd, slice_of(a, wg).vbase, wave, n, g);
-    grid_barrier(a.ws.ctr, ++round * (unsigned)G);
-  }
+  unsigned round = 1;
+  if (solo)
+    for (int vwg = 0; vwg < G; ++vwg)
+      if (vwg != wg) phase_ab(a, L, vwg, G);
 
   for (int b = solo ? 0 : wg; b < B; b += solo ? 1 : G) phase_c(a, L, b, G);
-  if (!solo) grid_barrier(a.ws.ctr, ++round * (unsigned)G);
+  if (!solo) grid_barrier(a.ws.ctr, ++round, G);
 
   // per-step pass from the first incomplete step of any request
   int* prevs = L.misc + kMsPrev;
@@ -985,12 +1191,12 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
       if (solo) load_slice<false>(a, L, sl);
       step_partial(a, L, sl, vwg, G, s, fstl, efrag);
     }
-    if (!solo) grid_barrier(a.ws.ctr, ++round * (unsigned)G);
+    if (!solo) grid_barrier(a.ws.ctr, ++round, G);
   }
   if (fmin < N) {
     // tokens of the last step (s == N: nothing is published)
     step_prevs(a, G, N, fstl, prevs, writer);
-    if (!solo) grid_barrier(a.ws.ctr, ++round * (unsigned)G);
+    if (!solo) grid_barrier(a.ws.ctr, ++round, G);
   }
 
   for (int vwg = v0; vwg < v1; ++vwg) {
@@ -1003,17 +1209,11 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
   }
 
   // log Z: the last workgroup to finish its partials merges them
-  bool merge = solo;
-  if (!solo) {
-    if (tid == 0)
-      L.misc[kMsTicket] = (int)__hip_atomic_fetch_add(a.ws.ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    merge = (unsigned)L.misc[kMsTicket] == (unsigned)G - 1;
-  }
+  const bool merge = solo || last_to_finish(a.ws.ctr, G, L.misc);
   if (merge) {
     for (int row = wave; row < rows; row += 4) {
       const MarkovPartial q = wave_merge(a.ws.partD + (size_t)row * G, G, lane);
-      if (lane == 0) a.log_z[row] = log_z_of(q, a.temperature[row / N]);
+      if (lane == 0) a.log_z[row] = log_z_of(q, req_temperature(L, row / N));
     }
   }
 }
@@ -1059,7 +1259,7 @@ FewPlan plan_markov_few(int B, int N, int Vd, int r, int cus) {
   p.off_partF = take(2 * (size_t)B * G * sizeof(MarkovPartial));
   p.off_partD = take(rowsN * G * sizeof(MarkovPartial));
   p.off_rows = take(rowsN * (size_t)r * 2);
-  p.off_ctr = take(16);
+  p.off_ctr = take(kCtrWords * sizeof(unsigned));
   p.bytes = (B <= 16) ? off : 0;
   return p;
 }
@@ -1108,7 +1308,7 @@ hipError_t launch_markov_few(const FewPlan& p, float* logits, const uint16_t* w1
   // test hook: DSPARK_MARKOV_SOLO=1 runs every slice in one workgroup
   const char* solo = getenv("DSPARK_MARKOV_SOLO");
   a.force_solo = (solo && solo[0] == '1') ? 1 : 0;
-  hipLaunchKernelGGL(zero_counters, dim3(1), dim3(1), 0, stream, a.ws.ctr);
+  hipLaunchKernelGGL(zero_counters, dim3(1), dim3(256), 0, stream, a.ws.ctr);
   hipLaunchKernelGGL(markov_few, dim3(p.grid), dim3(256), p.lds, stream, a);
   return hipGetLastError();
 }
