@@ -37,6 +37,7 @@ namespace dspark {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0) (gfx9 encoding)
 
 struct RowStat {
   float m, s;     // base-2 log-sum-exp state of y = l * log2(e) / T
@@ -237,70 +238,71 @@ __global__ __launch_bounds__(256) void verify_accept(int input_kind, const float
   const bool hot = probs || T > 0.0f;
   const float c2 = (!probs && hot) ? (1.0f / T) * kLog2e : 1.0f;
 
-  // Merged statistics of target rows k <= L (logits mode): tpr threads per row
-  // each merge a strided share of the row's partials, then one thread per row.
-  __shared__ float row_m[DSPARK_MAX_N + 1], row_s[DSPARK_MAX_N + 1];
-  __shared__ int row_amax[DSPARK_MAX_N + 1];
-  __shared__ float pm[256], ps[256], pav[256];
-  __shared__ int pai[256];
-  __shared__ int s_a;
-  if (!probs) {
-    const int rows = L + 1, tpr = 256 / rows;
-    const int k = tid / tpr, sub = tid - k * tpr;
-    float m = -INFINITY, s = 0.0f, av = -INFINITY;
-    int ai = 0x7FFFFFFF;
-    if (k < rows) {
-      const RowStat* rp = stats + ((size_t)b * (N + 1) + k) * nchunks;
-      for (int c0 = sub; c0 < nchunks; c0 += 8 * tpr) {
-        RowStat q[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) q[u] = rp[min(c0 + u * tpr, nchunks - 1)];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (c0 + u * tpr < nchunks)
-            stat_merge(m, s, av, ai, opaque(q[u].m), opaque(q[u].s), opaque(q[u].amax), opaque(q[u].aidx));
-      }
-    }
-    pm[tid] = m;
-    ps[tid] = s;
-    pav[tid] = av;
-    pai[tid] = ai;
-    __syncthreads();
-    if (tid < rows) {
-      float m2 = -INFINITY, s2 = 0.0f, av2 = -INFINITY;
-      int ai2 = 0x7FFFFFFF;
-      for (int t = tid * tpr; t < (tid + 1) * tpr; ++t) stat_merge(m2, s2, av2, ai2, pm[t], ps[t], pav[t], pai[t]);
-      row_m[tid] = m2;
-      row_s[tid] = s2;
-      row_amax[tid] = ai2;
-      rstat[(size_t)b * (N + 1) + tid] = make_float2(m2, 1.0f / s2);
-    }
-    __syncthreads();
+  // The accept test's inputs (wave 3, lane k < L: the drafted id, its draft index,
+  // the target and draft values) are requested first; their chain of dependent
+  // loads runs while waves 0-2 merge the row statistics.
+  int x = 0, xj = -1;
+  float lt = 0.0f, ld = 0.0f, ldz = 0.0f;
+  if (wave == 3 && L > 0) {
+    const int k = min(lane, L - 1);
+    x = draft_tokens[(size_t)b * N + k];
+    const int xs = (x >= 0 && x < V) ? x : 0;
+    xj = inv_map ? inv_map[xs] : xs;
+    lt = target[((size_t)b * (N + 1) + k) * V + xs];
+    ld = draft[((size_t)b * N + k) * Vd + max(xj, 0)];
+    if (!probs) ldz = draft_log_z[(size_t)b * N + k];
   }
 
+  // Merged statistics of target rows k <= L (logits mode): eight lanes of waves
+  // 0-2 per row, each merging a strided share of the row's partials (all loads of
+  // a share at once), then the eight lanes by DPP.
+  __shared__ float row_m[DSPARK_MAX_N + 1], row_s[DSPARK_MAX_N + 1];
+  __shared__ int row_amax[DSPARK_MAX_N + 1];
+  __shared__ int s_a;
+  if (!probs && wave < 3) {
+    constexpr int kU = 20;  // partials per lane and round
+    const int rows = L + 1, sub = tid & 7;
+    for (int k0 = 0; k0 < rows; k0 += 24) {
+      const int k = k0 + (tid >> 3);
+      float m = -INFINITY, s = 0.0f, av = -INFINITY;
+      int ai = 0x7FFFFFFF;
+      const RowStat* rp = stats + ((size_t)b * (N + 1) + min(k, rows - 1)) * nchunks;
+      for (int c0 = sub; c0 < nchunks; c0 += 8 * kU) {
+        RowStat q[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) q[u] = rp[min(c0 + 8 * u, nchunks - 1)];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (c0 + 8 * u < nchunks)
+            stat_merge(m, s, av, ai, opaque(q[u].m), opaque(q[u].s), opaque(q[u].amax), opaque(q[u].aidx));
+      }
+      stat_stage<kDppSwap1>(m, s, av, ai);
+      stat_stage<kDppSwap2>(m, s, av, ai);
+      stat_stage<kDppMirror8>(m, s, av, ai);
+      if (sub == 0 && k < rows) {
+        row_m[k] = m;
+        row_s[k] = s;
+        row_amax[k] = ai;
+        rstat[(size_t)b * (N + 1) + k] = make_float2(m, 1.0f / s);
+      }
+    }
+  }
+  __syncthreads();
+
   // All L positions at once, one lane each; the first rejection decides.
-  if (wave == 0) {
+  if (wave == 3) {
     bool rej = false;
     float greedy_alpha = 0.0f;
     if (lane < L) {
       const int k = lane;
-      const int x = draft_tokens[(size_t)b * N + k];
-      const bool valid = x >= 0 && x < V;  // not a target id: rejected without reading anything
-      const int xs = valid ? x : 0;
-      const int j = inv_map ? inv_map[xs] : xs;
+      const bool valid = x >= 0 && x < V;  // not a target id: rejected without using anything
       float pt, pd;
       if (probs) {
-        pt = target[((size_t)b * (N + 1) + k) * V + xs];
-        pd = (j >= 0) ? draft[((size_t)b * N + k) * Vd + j] : 0.0f;
+        pt = lt;
+        pd = (xj >= 0) ? ld : 0.0f;
       } else if (hot) {
-        const float lt = target[((size_t)b * (N + 1) + k) * V + xs];
         pt = __builtin_amdgcn_exp2f(lt * c2 - row_m[k]) / row_s[k];
-        if (j >= 0) {
-          const float ld = draft[((size_t)b * N + k) * Vd + j];
-          pd = __builtin_amdgcn_exp2f(ld * c2 - draft_log_z[(size_t)b * N + k] * kLog2e);
-        } else {
-          pd = 0.0f;
-        }
+        pd = (xj >= 0) ? __builtin_amdgcn_exp2f(ld * c2 - ldz * kLog2e) : 0.0f;
       } else {
         pt = (x == row_amax[k]) ? 1.0f : 0.0f;
         pd = 1.0f;
@@ -537,7 +539,9 @@ __global__ __launch_bounds__(256) void verify_sample(int input_kind, const float
     }
     if (do_alpha) st_f(apart + slot, (ared[0] + ared[1]) + (ared[2] + ared[3]));
   }
-  // the request's last workgroup merges (its partial stores completed at the barrier)
+  // the request's last workgroup merges: every thread's stores complete before the
+  // barrier, and the ticket is taken after it
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
   if (tid == 0) s_ticket = __hip_atomic_fetch_add(tickets + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
