@@ -487,3 +487,48 @@ def test_confidence_parity(B, N, H, V, r):
     err = np.abs(c.astype(np.float64) - ref).max()
     say(f"  max abs err {err:.2e}, c in [{ref.min():.3f}, {ref.max():.3f}]")
     assert err <= 1e-6
+
+
+# ------------------------------------------------------------------ whole round in a HIP graph
+def _round_outputs(path):
+    return [t.detach().clone() for t in (path.tokens, path.logz, path.logits, path.survival, path.admit_len,
+                                          path.accepted, path.out_tokens)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,over,coupled", [
+    ("tiny", {}, False),                                                          # few-request Markov kernel
+    ("batched", dict(B=8, H=256, V=8192, Vd=8192, r=64), False),                  # few-request, several requests
+    ("reduced_vocab", dict(B=40, H=256, V=8192, Vd=2048, r=64, K=200), False),    # per-step Markov, target map
+    ("batched", dict(B=24, H=512, V=4096, Vd=4096, r=32), True),                  # coupled verification
+])
+def test_graph_replay_round(name, over, coupled):
+    """A whole round (stages 1-4) captured once in a HIP graph and replayed: every replay,
+    with eager work and synchronisations between replays, gives the eager round's outputs
+    bit for bit (the library allocates nothing and clears its counters with kernels)."""
+    import bench
+    import draft_sampling_lossless_amd as dsl
+    w = synth.get(name, **over)
+    say(f"graph replay {name} {over} coupled={coupled}")
+    path = bench.Path(w, torch, dsl, synth, "coupled" if coupled else "rejection", False)
+    path.step()
+    torch.cuda.synchronize()
+    ref = _round_outputs(path)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path.step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (path.tokens, path.logz, path.logits, path.out_tokens):
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _round_outputs(path)
+        for k, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"replay {rep}: output {k} differs from the eager round"
+        # eager work between replays
+        path.step()
+        x = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(x)
