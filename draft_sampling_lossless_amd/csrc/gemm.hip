@@ -109,6 +109,7 @@ __global__ __launch_bounds__(256) void k1_skinny(const uint16_t* __restrict__ A,
 // ------------------------------------------------------------------ stream
 
 constexpr int SNS = 3;                        // ring stages
+constexpr int kRawBufferDword3 = 0x00020000;  // buffer resource word 3: raw 32-bit data, no swizzle
 constexpr int SROW = 1024 + 16;               // LDS bytes per row of a stage (512 k + pad)
 constexpr int SSTAGE = 16 * SROW;             // one stage: 16 rows x 512 k
 constexpr int SLDS = SNS * SSTAGE + 4 * 64 * 4 * 4;  // ring + cross-wave reduction
@@ -150,9 +151,17 @@ __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A,
   for (int t = 0; t < SNS - 1 && t < T; ++t) issue(t);
   floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < T; ++t) {
-    // this wave's loads of stage t are done once at most (SNS-2) later stages are pending
-    if (t + SNS - 2 < T) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((SNS - 2) * 4) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // this wave's loads of stage t are done once at most (SNS-2) later stages are
+    // pending, plus wave 0's four block-end stores when they were issued after
+    // stage t's loads (at the end of stage t-1 or t-2): vector memory operations
+    // complete in issue order, so waiting on them too would drain the ring
+    const bool st_after = wave == 0 && ((t >= 1 && (t - 1) % spb == spb - 1) || (t >= 2 && (t - 2) % spb == spb - 1));
+    if (t + SNS - 2 < T) {
+      if (st_after) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((SNS - 2) * 4 + 4) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((SNS - 2) * 4) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     lds_barrier();  // every wave's share of stage t is in LDS; stage t-1's buffer is free
     if (t + SNS - 1 < T) issue(t + SNS - 1);
     const char* buf = ring + (t % SNS) * SSTAGE;
@@ -176,12 +185,15 @@ __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A,
 #pragma unroll
         for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const floatx4*>(red + (w * 64 + lane) * 4);
         const int j = (blockIdx.x + (t / spb) * gridDim.x) * 16 + n;
-        if (j < Vd) {
+        // always exactly four store instructions (the waits above count them): a
+        // lane outside the output gets an offset past the buffer's range, and the
+        // buffer store drops it
+        const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(C, (short)0, M * Vd * 4, kRawBufferDword3);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = 4 * g + i;
-            if (m < M) C[(size_t)m * Vd + j] = sum[i];
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * g + i;
+          const int off = (m < M && j < Vd) ? (m * Vd + j) * 4 : 0x7FFFFFF0;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum[i]), out, off, 0, 0);
         }
       }
       acc = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -426,7 +438,7 @@ __global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, co
 hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, float* logits, int M, int H,
                                int Vd, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  if (M <= 16 && H % 512 == 0 && H <= 4096) {
+  if (M <= 16 && H % 512 == 0 && H <= 4096 && (long)M * Vd * 4 < 0x7FFFFFF0L) {  // (32-bit store offsets)
     const int nblocks = (Vd + 15) / 16;
     const int grid = min(cu_count(), nblocks);
     hipLaunchKernelGGL(k1_stream, dim3(grid), dim3(256), SLDS, stream, hidden, lm_head, logits, M, H, Vd);
