@@ -1,21 +1,25 @@
 // Stage 1: draft base logits, logits[m, j] = sum_h hidden[m, h] * lm_head[j, h]
 // (bf16 in, fp32 accumulate and out) on gfx950 MFMA (v_mfma_f32_16x16x32_bf16).
 //
-// Three tilings, picked by the shape (M = B * N, the number of draft positions):
+// Four tilings, picked by the shape (M = B * N, the number of draft positions):
 //  * stream (M <= 16, H % 512 == 0, H <= 4096): bound by streaming the LM head
 //    from HBM (2 * Vd * H bytes, read once).  One persistent workgroup per CU
-//    walks 16-row blocks of the LM head; each block's rows arrive 512 k at a time
-//    (1 KB per row) through a 3-stage LDS ring filled by direct global->LDS loads,
-//    so every load instruction reads 1 KB contiguous and two stages stay in
-//    flight across the barriers.  The hidden rows sit in registers for the whole
-//    kernel (each wave always takes the same 4 k steps of a stage); the 4 waves'
-//    partial sums of a block are added in LDS.
+//    walks a contiguous run of 16-row blocks of the LM head; each block's rows
+//    arrive 512 k at a time (1 KB per row) through a 3-stage LDS ring filled by
+//    direct global->LDS loads, so every load instruction reads 1 KB contiguous and
+//    two stages stay in flight across the barriers.  The hidden rows sit in
+//    registers for the whole kernel (each wave always takes the same 4 k steps of
+//    a stage); the 4 waves' partial sums of a block are added in LDS, and the
+//    outputs stay in LDS until the stream is done.
 //  * skinny (other M <= 64): each wave owns 16*FR vocabulary rows and streams them
 //    straight from global memory into MFMA B fragments; the hidden rows (A
 //    fragments) come from L1/L2.  No LDS.
-//  * tiled (M > 64): MFMA-bound.  128 x 128 output tiles, BK = 64, both operands
-//    staged through double-buffered LDS; 4 waves, each a 64 x 64 block of 16x16
-//    MFMA fragments; grouped tile order (8 row tiles at a time).
+//  * big (M > 64, H % 64 == 0): MFMA-bound.  256 x 256 output tiles, BK = 64,
+//    two LDS stages filled by global->LDS loads; each wave a 128 x 128 quarter.
+//  * tiled (other M > 64): 128 x 128 output tiles, BK = 64, both operands staged
+//    through double-buffered LDS; 4 waves, each a 64 x 64 block of 16x16 MFMA
+//    fragments.  Both MFMA tilings take a grouped tile order (8 row tiles at a
+//    time), XCD by XCD.
 //
 // MFMA 16x16x32 fragment layout (64 lanes, lane = 16 * g + n):
 //   A: lane holds 8 consecutive k of row n;  B: 8 consecutive k of column n;
@@ -109,16 +113,18 @@ __global__ __launch_bounds__(256) void k1_skinny(const uint16_t* __restrict__ A,
 // ------------------------------------------------------------------ stream
 
 constexpr int SNS = 3;                        // ring stages
-constexpr int kRawBufferDword3 = 0x00020000;  // buffer resource word 3: raw 32-bit data, no swizzle
 constexpr int SROW = 1024 + 16;               // LDS bytes per row of a stage (512 k + pad)
 constexpr int SSTAGE = 16 * SROW;             // one stage: 16 rows x 512 k
-constexpr int SLDS = SNS * SSTAGE + 4 * 64 * 4 * 4;  // ring + cross-wave reduction
+constexpr int SRED = 4 * 64 * 4;              // floats of one block's partial sums (4 waves x 64 lanes x 4)
+constexpr int SFIXED = SNS * SSTAGE + 2 * SRED * 4;  // ring + two partial-sum buffers (bytes)
+constexpr int SOUT_MAX = 96 * 1024;           // bytes of outputs a workgroup may hold in LDS
 
 __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                  float* __restrict__ C, int M, int H, int Vd) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* ring = smem;
-  float* red = reinterpret_cast<float*>(smem + SNS * SSTAGE);
+  float* red = reinterpret_cast<float*>(smem + SNS * SSTAGE);  // [2][SRED], by block parity
+  float* outl = red + 2 * SRED;                                // [M][16 * blocks] this workgroup's outputs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int spb = H / 512;  // stages per 16-row block (<= 8)
@@ -133,13 +139,16 @@ __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A,
       af[st][u] = (st < spb && n < M) ? load_bf16x8(A + (size_t)n * H + k) : zero_bf16x8();
     }
 
+  // a contiguous run of 16-row blocks per workgroup
   const int nblocks = (Vd + 15) / 16;
-  const int myblocks = (nblocks - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int T = myblocks * spb;  // stages this workgroup consumes
-  // stage t: block blockIdx.x + (t / spb) * gridDim.x, k range (t % spb) * 512 .. +512;
-  // wave w loads rows w, w+4, w+8, w+12 of it (one 1 KB instruction each)
+  const int b0 = (int)((long)nblocks * blockIdx.x / gridDim.x);
+  const int b1 = (int)((long)nblocks * (blockIdx.x + 1) / gridDim.x);
+  const int nb = b1 - b0, L = 16 * nb;
+  const int T = nb * spb;  // stages this workgroup consumes
+  // stage t: block b0 + t / spb, k range (t % spb) * 512 .. +512; wave w loads rows
+  // w, w+4, w+8, w+12 of it (one 1 KB instruction each)
   auto issue = [&](int t) {
-    const int blk = blockIdx.x + (t / spb) * gridDim.x, kst = t % spb;
+    const int blk = b0 + t / spb, kst = t % spb;
     char* base = ring + (t % SNS) * SSTAGE;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -148,21 +157,26 @@ __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A,
       __builtin_amdgcn_global_load_lds(W + (size_t)j * H + kst * 512 + lane * 8, base + row * SROW, 16, 0, 0);
     }
   };
+  // a finished block: wave w adds the four waves' partial sums of output rows
+  // 4w .. 4w+3 (MFMA lane groups g = w) and keeps them in LDS
+  auto finish_block = [&](int blk_local) {
+    const float* rb = red + (blk_local & 1) * SRED;
+    const int i = lane >> 4, m = 4 * wave + i;
+    float v = rb[(16 * wave + n) * 4 + i];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += rb[(w * 64 + 16 * wave + n) * 4 + i];
+    if (m < M) outl[m * L + 16 * blk_local + n] = v;
+  };
+
   for (int t = 0; t < SNS - 1 && t < T; ++t) issue(t);
   floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < T; ++t) {
     // this wave's loads of stage t are done once at most (SNS-2) later stages are
-    // pending, plus wave 0's four block-end stores when they were issued after
-    // stage t's loads (at the end of stage t-1 or t-2): vector memory operations
-    // complete in issue order, so waiting on them too would drain the ring
-    const bool st_after = wave == 0 && ((t >= 1 && (t - 1) % spb == spb - 1) || (t >= 2 && (t - 2) % spb == spb - 1));
-    if (t + SNS - 2 < T) {
-      if (st_after) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((SNS - 2) * 4 + 4) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((SNS - 2) * 4) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    // pending (nothing else touches global memory inside the loop)
+    if (t + SNS - 2 < T) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((SNS - 2) * 4) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();  // every wave's share of stage t is in LDS; stage t-1's buffer is free
+    if (t >= 1 && (t - 1) % spb == spb - 1) finish_block((t - 1) / spb);  // its partials are visible now
     if (t + SNS - 1 < T) issue(t + SNS - 1);
     const char* buf = ring + (t % SNS) * SSTAGE;
     const int kst = t % spb;
@@ -177,28 +191,29 @@ __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A,
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st][u], b, acc, 0, 0, 0);
       }
     }
-    if (kst == spb - 1) {  // block done: add the 4 waves' partial sums
-      *reinterpret_cast<floatx4*>(red + (wave * 64 + lane) * 4) = acc;
-      lds_barrier();
-      if (wave == 0) {
-        floatx4 sum = acc;
-#pragma unroll
-        for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const floatx4*>(red + (w * 64 + lane) * 4);
-        const int j = (blockIdx.x + (t / spb) * gridDim.x) * 16 + n;
-        // always exactly four store instructions (the waits above count them): a
-        // lane outside the output gets an offset past the buffer's range, and the
-        // buffer store drops it
-        const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(C, (short)0, M * Vd * 4, kRawBufferDword3);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 4 * g + i;
-          const int off = (m < M && j < Vd) ? (m * Vd + j) * 4 : 0x7FFFFFF0;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum[i]), out, off, 0, 0);
-        }
-      }
+    if (kst == spb - 1) {  // block done: this wave's partial sums (the buffer alternates,
+                           // so a block's sums never overwrite ones still being read)
+      *reinterpret_cast<floatx4*>(red + ((t / spb) & 1) * SRED + (wave * 64 + lane) * 4) = acc;
       acc = floatx4{0.f, 0.f, 0.f, 0.f};
     }
   }
+  if (T > 0) {
+    lds_barrier();
+    finish_block(nb - 1);
+  }
+  __syncthreads();
+  // the outputs leave only after the whole stream: a contiguous run of each output
+  // row (writes interleaved with the stream cost it several percent)
+  const int jb = 16 * b0;
+  for (int m = 0; m < M; ++m)
+    for (int x = tid; x < L; x += 256)
+      if (jb + x < Vd) C[(size_t)m * Vd + jb + x] = outl[m * L + x];
+}
+
+size_t k1_stream_lds(int M, int Vd, int grid) {
+  const int nblocks = (Vd + 15) / 16;
+  const size_t maxb = (size_t)(nblocks + grid - 1) / grid;
+  return SFIXED + (size_t)M * 16 * maxb * 4;
 }
 
 int cu_count() {
@@ -438,10 +453,19 @@ __global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, co
 hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, float* logits, int M, int H,
                                int Vd, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  if (M <= 16 && H % 512 == 0 && H <= 4096 && (long)M * Vd * 4 < 0x7FFFFFF0L) {  // (32-bit store offsets)
-    const int nblocks = (Vd + 15) / 16;
-    const int grid = min(cu_count(), nblocks);
-    hipLaunchKernelGGL(k1_stream, dim3(grid), dim3(256), SLDS, stream, hidden, lm_head, logits, M, H, Vd);
+  const int sgrid = min(cu_count(), (Vd + 15) / 16);
+  const size_t slds = k1_stream_lds(M, Vd, sgrid);
+  if (M <= 16 && H % 512 == 0 && H <= 4096 && slds <= SFIXED + SOUT_MAX) {
+    static bool attr_set[64] = {false};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_stream),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, SFIXED + SOUT_MAX);
+      if (e != hipSuccess) return e;
+      attr_set[dev] = true;
+    }
+    hipLaunchKernelGGL(k1_stream, dim3(sgrid), dim3(256), slds, stream, hidden, lm_head, logits, M, H, Vd);
   } else if (M <= 64) {
     constexpr int FR = 2;
     const int waves = (Vd + 16 * FR - 1) / (16 * FR);
