@@ -55,7 +55,10 @@ def test_race_exponentials_bit_exact(n, pos, req, tag):
                                     (300, 200, 1004), (129, 4096, 640), (64, 64, 68),
                                     (8, 4096, 4100), (16, 512, 1000), (13, 1024, 72), (1, 2048, 65540),
                                     (8, 4096, 8), (257, 128, 1000), (520, 96, 300), (96, 32, 260), (300, 64, 500),
-                                    (700, 4096, 2000)])
+                                    (700, 4096, 2000),
+                                    # the stream kernel's LDS output buffer exactly full (96 KB per
+                                    # workgroup at 256 CUs), and one size past it (the skinny kernel)
+                                    (16, 512, 393216), (16, 512, 400000)])
 def test_draft_logits_small(M, H, Vd):
     say(f"draft_logits M={M} H={H} Vd={Vd}")
     g = np.random.default_rng(M * 7 + H)
@@ -259,7 +262,7 @@ def _verify_inputs(B, N, V, Vd, temps, seed, reduced=False, sigma=1.0):
 
 
 @pytest.mark.parametrize("B,N,V,Vd,reduced", [(200, 6, 1024, 1024, False), (64, 8, 2048, 1000, True),
-                                              (3, 1, 64, 64, False)])
+                                              (3, 1, 64, 64, False), (3, 64, 256, 256, False)])
 def test_verify_probs_bit_exact(B, N, V, Vd, reduced):
     say(f"verify probs B={B} N={N} V={V} Vd={Vd}")
     c = _verify_inputs(B, N, V, Vd, (0.7, 1.0), seed=B + N, reduced=reduced)
@@ -277,7 +280,11 @@ def test_verify_probs_bit_exact(B, N, V, Vd, reduced):
 
 @pytest.mark.parametrize("B,N,V,Vd,temps,reduced", [(200, 6, 1024, 1024, (0.0, 0.7, 1.0), False),
                                                     (64, 8, 2048, 1000, (0.0, 1.0), True),
-                                                    (16, 4, 4096, 4096, (0.0,), False)])
+                                                    (16, 4, 4096, 4096, (0.0,), False),
+                                                    # more than 24 target rows: several passes of the
+                                                    # acceptance kernel's statistics merge
+                                                    (6, 40, 1024, 1024, (0.7, 1.0), False),
+                                                    (4, 64, 512, 512, (0.0, 1.0), False)])
 def test_verify_logits_parity(B, N, V, Vd, temps, reduced):
     say(f"verify logits B={B} N={N} V={V} Vd={Vd} T={temps}")
     c = _verify_inputs(B, N, V, Vd, temps, seed=B * N + 1, reduced=reduced)
