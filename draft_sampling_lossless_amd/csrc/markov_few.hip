@@ -578,10 +578,27 @@ __device__ __forceinline__ void records_batch(const FewArgs& a, const Lds& L, co
   __syncthreads();
 }
 
+// thread 0: this workgroup's arrival number (the first workgroup to take one gets 0)
+__device__ __forceinline__ unsigned take_arrival_now(const FewArgs& a, bool take) {
+  unsigned arrival = 1u;
+  if (take && threadIdx.x == 0) {
+    // (a lane-varying address keeps the atomic to this lane, without the wave-wide
+    // reduction the compiler would otherwise wrap it in, which waits for the result)
+    int zero = 0;
+    asm volatile("" : "+v"(zero));
+    arrival = __hip_atomic_fetch_add(a.ws.ctr + 2 + zero, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return arrival;
+}
+
 // Phases A and B of one slice.  The first row batch's base logits and the first
 // W2 batch are requested together, and that row batch's keys are computed while
-// the W2 rows are still in flight.
-__device__ __forceinline__ void phase_ab(const FewArgs& a, const Lds& L, int vwg, int G) {
+// the W2 rows are still in flight.  With take_arrival, thread 0 also takes this
+// workgroup's arrival number (returned; 1 elsewhere), right after those loads:
+// vector memory operations complete in issue order, so an atomic issued before
+// them would hold up every wait on them while the other workgroups' atomics on
+// the same counter are served.
+__device__ __forceinline__ unsigned phase_ab(const FewArgs& a, const Lds& L, int vwg, int G, bool take_arrival) {
   const int tid = threadIdx.x;
   const int r = a.r, kc = r / 8, rows = a.B * a.N;
   const bool pow2 = (kc & (kc - 1)) == 0;
@@ -593,6 +610,7 @@ __device__ __forceinline__ void phase_ab(const FewArgs& a, const Lds& L, int vwg
   if (tid < 16) n1r[tid] = 0.0f;
   RowBatch rb;
   load_rows(a, sl, 0, rb);
+  unsigned arrival = 1u;
   float n2 = 0.0f;
   if (pow2) {
     const int pieces = sl.nch * kChunk * kc;
@@ -600,6 +618,7 @@ __device__ __forceinline__ void phase_ab(const FewArgs& a, const Lds& L, int vwg
     __builtin_amdgcn_sched_barrier(0);  // (every load issued before the keys use any)
     w2_issue(a, sl, 0, v);
     __builtin_amdgcn_sched_barrier(0);
+    arrival = take_arrival_now(a, take_arrival);
     keys_batch(a, sl, 0, rb, red64);
     n2 = w2_consume(a, L, sl, 0, v);
     for (int p0 = 256 * kFly; p0 < pieces; p0 += 256 * kFly) {
@@ -608,6 +627,7 @@ __device__ __forceinline__ void phase_ab(const FewArgs& a, const Lds& L, int vwg
     }
     __syncthreads();
   } else {
+    arrival = take_arrival_now(a, take_arrival);
     keys_batch(a, sl, 0, rb, red64);
     n2 = load_slice<true>(a, L, sl);
   }
@@ -635,6 +655,7 @@ __device__ __forceinline__ void phase_ab(const FewArgs& a, const Lds& L, int vwg
     records_batch(a, L, sl, vwg, G, row0, red64, n1r);
   }
   if (tid < a.B) st_f(a.ws.n1 + (size_t)tid * G + vwg, n1r[tid]);
+  return arrival;
 }
 
 // last index i in [0, n) of a strictly increasing table with tab[i] <= x
@@ -1135,24 +1156,15 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
   L.tgt = reinterpret_cast<int*>(creg + cr.tgt);
   L.fk = reinterpret_cast<float*>(creg + cr.fk);
 
-  // arrival order (the first to start decides the mode at the first barrier); its
-  // value is only needed after phase A/B
-  // (the empty asm statements keep the compiler from waiting for it at once: a
-  // lane-varying address is left to that lane, and the result is first read after
-  // phase B)
-  unsigned arrival = 1u;
-  if (tid == 0) {
-    int zero = 0;
-    asm volatile("" : "+v"(zero));
-    arrival = __hip_atomic_fetch_add(a.ws.ctr + 2 + zero, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
   // per-request parameters, kept in LDS for the later phases (unguarded loads from a
   // clamped index, stored once phase B no longer waits on anything)
   const int pq = min(tid, B - 1);
   const float p_t = a.temperature[pq];
   const uint32_t p_rid = a.request_id[pq];
   const int p_anc = a.anchor[pq];
-  phase_ab(a, L, wg, G);
+  // arrival order (the first to take a number decides the mode at the first barrier)
+  unsigned arrival = phase_ab(a, L, wg, G, true);
+  asm volatile("" : "+v"(arrival));  // (first read here, after phase B)
   if (tid < B) {
     reinterpret_cast<float*>(L.misc)[kMsT + tid] = p_t;
     reinterpret_cast<uint32_t*>(L.misc)[kMsRid + tid] = p_rid;
@@ -1169,7 +1181,7 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
   unsigned round = 1;
   if (solo)
     for (int vwg = 0; vwg < G; ++vwg)
-      if (vwg != wg) phase_ab(a, L, vwg, G);
+      if (vwg != wg) phase_ab(a, L, vwg, G, false);
 
   for (int b = solo ? 0 : wg; b < B; b += solo ? 1 : G) phase_c(a, L, b, G);
   if (!solo) grid_barrier(a.ws.ctr, ++round, G);
