@@ -27,7 +27,7 @@ struct FewPlan {
   int cap;             // survivors per step whose weight rows phase C can hold in LDS
   size_t lds;          // dynamic LDS bytes
   int gmax;            // workgroup count the workspace layout is sized for
-  size_t off_norms, off_n1, off_rec, off_fstep, off_partF, off_partD, off_rows, off_ctr, bytes;
+  size_t off_norms, off_n1, off_rec, off_fstep, off_partF, off_partD, off_rows, bytes;
 };
 FewPlan plan_markov_few(int B, int N, int Vd, int r, int cus);
 hipError_t launch_markov_few(const FewPlan& p, float* logits, const uint16_t* w1, const uint16_t* w2,

@@ -59,6 +59,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "device.hpp"
 #include "kernels.hpp"
@@ -84,13 +85,18 @@ constexpr int kMisc = 512;       // ints of per-workgroup bookkeeping in LDS
 constexpr int kFixedScratch = 256 + 1024 + 4 * kMisc + 4 * kMaxSlice + 4 * kMaxSlices;  // + row / slice W2 norms
 constexpr uint64_t kArriveTicks = 5000;  // start-up window: 50 us of the 100 MHz real-time counter
 
-// Counters (32-bit words, zeroed before every launch).  Words 0..3: grid barrier
-// (groups arrived), workgroups done (groups finished), arrivals, mode.  Workgroup w
+// Counters (32-bit words).  Words 0..3: grid barrier (groups arrived), workgroups
+// done (groups finished), arrivals, departures (solo mode only).  Workgroup w
 // belongs to group w % kGroups; each group has its own barrier and done counters,
 // 128 bytes apart, so that no single address takes an atomic from every workgroup
 // (same-address atomics are served one at a time, ~20 ns each).
+// A launch takes one of kCtrSets counter sets that the library keeps in device
+// memory (zero when the library is loaded) and leaves it zero when it ends: the
+// last workgroup to use the counters clears them.  So no launch has to clear
+// them first, and the caller's workspace holds no counters.
 constexpr int kGroups = 16;
 constexpr int kCtrWords = 32 + 32 * 2 * kGroups;
+constexpr int kCtrSets = 64;
 __device__ __forceinline__ unsigned* ctr_group(unsigned* ctr, int kind, int grp) {
   return ctr + 32 + 32 * (kind * kGroups + grp);
 }
@@ -101,6 +107,7 @@ constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0) (gfx9 encoding)
 // misc layout (ints)
 constexpr int kMsCnt = 0, kMsInc = 64, kMsOff = 128, kMsSel = 192, kMsPre = 256;  // [64] each ([65] for kMsPre)
 constexpr int kMsFs = 336, kMsFit = 337, kMsPairs = 338, kMsTot = 339, kMsRole = 340, kMsTicket = 341;
+constexpr int kMsLastOut = 342;
 constexpr int kMsPrev = 352, kMsFst = 368;  // [16] each (per-step pass)
 constexpr int kMsN1 = 384;                  // [16] floats: largest recorded W1 norm per request (phase B)
 constexpr int kMsT = 400, kMsRid = 416, kMsAnc = 432;  // [16] each: temperature, request id, anchor per request
@@ -121,7 +128,7 @@ struct FewWs {
   MarkovPartial* partF;   // [2][B][G] per-step partials of that pass
   MarkovPartial* partD;   // [B*N][G] log-sum-exp partials of the processed rows
   uint32_t* rows;         // [B*N][r/2] W1 row (bf16 pairs) of each step's previous token
-  unsigned* ctr;          // [kCtrWords] counters (see ctr_group)
+  unsigned* ctr;          // [kCtrWords] this launch's counter set (see ctr_group)
 };
 
 struct FewArgs {
@@ -180,9 +187,8 @@ __device__ __forceinline__ float req_temperature(const Lds& L, int b) { return r
 __device__ __forceinline__ uint32_t req_id(const Lds& L, int b) { return reinterpret_cast<const uint32_t*>(L.misc)[kMsRid + b]; }
 __device__ __forceinline__ int req_anchor(const Lds& L, int b) { return L.misc[kMsAnc + b]; }
 
-__global__ __launch_bounds__(256) void zero_counters(unsigned* ctr) {
-  for (int q = threadIdx.x; q < kCtrWords; q += 256) ctr[q] = 0u;
-}
+// every launch's counter sets, kCtrWords words each (zero-initialised when loaded)
+__device__ __attribute__((aligned(256))) unsigned g_few_counters[kCtrSets * kCtrWords];
 
 // half-width of a full key's interval around the bias-free key, per unit of W2
 // row norm, and an absolute slack: room for the float rounding of norms, dots
@@ -1118,6 +1124,27 @@ __device__ __forceinline__ int first_barrier_role(const FewArgs& a, int G, bool 
   return misc[kMsRole];
 }
 
+// Clears the counter set (the whole workgroup; uniform `last`).  Called only by the
+// last workgroup to use the counters, once every other workgroup's counter
+// operations are done.
+__device__ __forceinline__ void clear_counters(unsigned* ctr, bool last) {
+  if (last)
+    for (int q = threadIdx.x; q < kCtrWords; q += blockDim.x) st_u(ctr + q, 0u);
+}
+
+// Solo mode: every workgroup counts its departure once its counter operations are
+// done; the last of all gridDim.x workgroups clears the counters (a workgroup that
+// starts late still departs, so the count always completes).
+__device__ __forceinline__ void depart(unsigned* ctr, int* misc) {
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this workgroup's counter atomics are done
+    misc[kMsLastOut] =
+        __hip_atomic_fetch_add(ctr + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == gridDim.x;
+  }
+  __syncthreads();
+  clear_counters(ctr, misc[kMsLastOut] != 0);
+}
+
 // Whether this workgroup is the last one to finish (the counts of every group).
 __device__ __forceinline__ bool last_to_finish(unsigned* ctr, int G, int* misc) {
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -1175,7 +1202,10 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
   float4 pre[kMaxCPW][4];  // base logits of the first phase-D tile, read while the chain runs
   load_tile(pre, a.logits, 0, (N + 15) / 16, B, N, a.Vd, slice_of(a, wg).vbase, wave, n, g);
   const int role = first_barrier_role(a, G, arrival == 0u, L.misc);
-  if (role == 0) return;
+  if (role == 0) {  // (only in solo mode)
+    depart(a.ws.ctr, L.misc);
+    return;
+  }
   const bool solo = role == 2;
   const int v0 = solo ? 0 : wg, v1 = solo ? G : wg + 1;  // slices this workgroup runs
   unsigned round = 1;
@@ -1220,8 +1250,14 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
     phase_d(a, L, sl, vwg, G, pre);
   }
 
-  // log Z: the last workgroup to finish its partials merges them
+  // log Z: the last workgroup to finish its partials merges them.  In normal mode
+  // every other workgroup's last counter operation has been counted by then, so
+  // that workgroup clears the counters; in solo mode the last to depart does.
   const bool merge = solo || last_to_finish(a.ws.ctr, G, L.misc);
+  if (solo)
+    depart(a.ws.ctr, L.misc);
+  else
+    clear_counters(a.ws.ctr, merge);
   if (merge) {
     for (int row = wave; row < rows; row += 4) {
       const MarkovPartial q = wave_merge(a.ws.partD + (size_t)row * G, G, lane);
@@ -1271,7 +1307,6 @@ FewPlan plan_markov_few(int B, int N, int Vd, int r, int cus) {
   p.off_partF = take(2 * (size_t)B * G * sizeof(MarkovPartial));
   p.off_partD = take(rowsN * G * sizeof(MarkovPartial));
   p.off_rows = take(rowsN * (size_t)r * 2);
-  p.off_ctr = take(kCtrWords * sizeof(unsigned));
   p.bytes = (B <= 16) ? off : 0;
   return p;
 }
@@ -1307,7 +1342,19 @@ hipError_t launch_markov_few(const FewPlan& p, float* logits, const uint16_t* w1
   a.ws.partF = reinterpret_cast<MarkovPartial*>(w + p.off_partF);
   a.ws.partD = reinterpret_cast<MarkovPartial*>(w + p.off_partD);
   a.ws.rows = reinterpret_cast<uint32_t*>(w + p.off_rows);
-  a.ws.ctr = reinterpret_cast<unsigned*>(w + p.off_ctr);
+  // this launch's counter set: the next of the library's sets on this device
+  static std::atomic<unsigned*> ctr_base[64];
+  static std::atomic<unsigned> next_set[64];
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  unsigned* base = ctr_base[dev].load(std::memory_order_relaxed);
+  if (!base) {  // (concurrent first calls store the same address)
+    void* sym = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&sym, HIP_SYMBOL(g_few_counters));
+    if (e != hipSuccess) return e;
+    base = static_cast<unsigned*>(sym);
+    ctr_base[dev].store(base, std::memory_order_relaxed);
+  }
+  a.ws.ctr = base + (size_t)(next_set[dev].fetch_add(1u, std::memory_order_relaxed) % kCtrSets) * kCtrWords;
   a.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
   a.key1 = (uint32_t)(seed >> 32);
   a.B = B;
@@ -1320,7 +1367,6 @@ hipError_t launch_markov_few(const FewPlan& p, float* logits, const uint16_t* w1
   // test hook: DSPARK_MARKOV_SOLO=1 runs every slice in one workgroup
   const char* solo = getenv("DSPARK_MARKOV_SOLO");
   a.force_solo = (solo && solo[0] == '1') ? 1 : 0;
-  hipLaunchKernelGGL(zero_counters, dim3(1), dim3(256), 0, stream, a.ws.ctr);
   hipLaunchKernelGGL(markov_few, dim3(p.grid), dim3(256), p.lds, stream, a);
   return hipGetLastError();
 }

@@ -30,8 +30,12 @@
  *              inside kernels surface at the caller's next synchronisation.  The
  *              message of the last failure on the calling host thread is in
  *              dspark_last_error().  No C++ exception crosses this boundary.
- *   Threads    Calls are reentrant; the only global state is the thread-local
- *              error message.
+ *   Threads    Calls are reentrant.  Global state: the thread-local error message,
+ *              and per device 64 sets of grid-barrier counters (4.2 KB each, device
+ *              memory, zero when the library loads) for the few-request Markov
+ *              kernel: each dspark_markov_sample call with B <= 16 takes the next
+ *              set, and every launch leaves its set zero again, so 64 or more such
+ *              launches must not be in flight at once.
  *   Sampling   All randomness is Philox4x32-10 (Salmon et al., SC'11) with
  *                key = (seed & 0xffffffff, seed >> 32),
  *                counter = (index >> 2, position, request_id, tag), word index & 3,

@@ -207,6 +207,25 @@ def test_markov_deterministic():
                                   y.view(np.uint32) if y.dtype == np.float32 else y)
 
 
+def test_markov_few_counter_sets_reused(monkeypatch):
+    """The few-request kernel's barrier counters live in a ring of counter sets that each
+    launch leaves cleared.  Well over two rounds of the ring, alternating normal and
+    single-workgroup launches (which clear the counters on different paths), give the
+    first launch's outputs bit for bit."""
+    c = _markov_case(2, 5, 4096, 4096, 64, (0.0, 1.0), seed=11)
+    say("markov few: 150 launches over the counter sets")
+    ref = _run_markov_gpu(c)
+    for i in range(150):
+        if i % 3 == 2:
+            monkeypatch.setenv("DSPARK_MARKOV_SOLO", "1")
+        else:
+            monkeypatch.delenv("DSPARK_MARKOV_SOLO", raising=False)
+        got = _run_markov_gpu(c)
+        for x, y in zip(ref, got):
+            assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                                  y.view(np.uint32) if y.dtype == np.float32 else y), f"launch {i}"
+
+
 @pytest.mark.parametrize("name,nsample", [("qwen3_8b_single", 1), ("batched", 4), ("admission", 3),
                                           ("reduced_vocab", 6)])
 def test_markov_full_size_sampled(name, nsample):
