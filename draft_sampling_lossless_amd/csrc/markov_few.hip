@@ -16,7 +16,8 @@
 //
 // Every workgroup owns a slice of the draft vocabulary (at most 1024 entries):
 //   phase A  (all workgroups)  the W2 slice into LDS (kept for the whole kernel)
-//            and the norm of each of its rows.
+//            and the norm of each of its rows; its loads are in flight while the
+//            first row batch's keys of phase B are computed.
 //   phase B  (all)   bias-free keys of every (request, step) row of the slice; the
 //            slice's best two entries of each row are recorded with ||W2[j]|| and
 //            ||W1[t(j)]|| (the row j would use as a previous token).  Every entry
@@ -51,10 +52,12 @@
 // its LDS size).  The grid barriers need every workgroup resident at once, which
 // an idle device gives but nothing guarantees.  Every workgroup runs phases A and
 // B of its own slice, which need no other workgroup; at the first barrier the
-// first workgroup to start checks that all of them arrive within a short window.
-// If they do, the phases go on as above; if not (the device is busy elsewhere),
-// that workgroup runs every phase for every slice by itself and the others
-// return.  Either way no workgroup ever waits for one that has not started.
+// first workgroup to take an arrival number checks that all of them arrive within
+// a short window.  If they do, the phases go on as above; if not (the device is
+// busy elsewhere), that workgroup runs every phase for every slice by itself and
+// the others return.  Either way no workgroup ever waits for one that has not
+// started.  The barrier counters are one of the library's counter sets, which
+// every launch leaves cleared (see kCtrSets).
 #include <math.h>
 #include <stdlib.h>
 
