@@ -761,26 +761,40 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int fs = N;
-    for (int i = 0; i < N; ++i)
-      if (inc[i]) {
-        fs = i;
-        break;
+  // the plan (wave 0, lane i = step i; N <= 64): the first step left to the per-step
+  // pass (fs), each step's staged survivors nq and (previous, current) pairs, and
+  // their offsets by prefix sums (every step before fs has at least one survivor)
+  if (wave == 0) {
+    const int i = lane;
+    const bool act = i < N;
+    const int ci = act ? cnt[i] : 0;
+    const uint64_t incm = __ballot(act && inc[i] != 0);
+    const int fs = incm ? (int)__builtin_ctzll(incm) : N;
+    const bool in = i < fs;
+    const int nq = in ? min(ci, cap) : 0;
+    const int cprev = __shfl_up(ci, 1);
+    const int pr = in ? ((i == 0) ? 1 : min(cprev, cap)) * nq : 0;
+    const bool overflow = __ballot(in && ci > cap) != 0;
+    int sq = nq, sp = pr;  // inclusive prefix sums over the steps
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int aq = __shfl_up(sq, off), ap = __shfl_up(sp, off);
+      if (lane >= off) {
+        sq += aq;
+        sp += ap;
       }
-    int fit = 1, pairs = 0, tot = 0;
-    for (int i = 0; i < fs; ++i) {  // (every step before fs has at least one survivor)
-      fit &= cnt[i] <= cap;
-      const int nq = min(cnt[i], cap);
-      pre[i] = tot;
-      tot += nq;
-      offp[i] = pairs;
-      pairs += ((i == 0) ? 1 : min(cnt[i - 1], cap)) * nq;
     }
-    L.misc[kMsFs] = fs;
-    L.misc[kMsFit] = (fit && pairs <= kPairs) ? 1 : 0;
-    L.misc[kMsPairs] = pairs;
-    L.misc[kMsTot] = tot;
+    if (in) {
+      pre[i] = sq - nq;
+      offp[i] = sp - pr;
+    }
+    const int tot = __shfl(sq, 63), pairs = __shfl(sp, 63);
+    if (lane == 0) {
+      L.misc[kMsFs] = fs;
+      L.misc[kMsFit] = (!overflow && pairs <= kPairs) ? 1 : 0;
+      L.misc[kMsPairs] = pairs;
+      L.misc[kMsTot] = tot;
+    }
   }
   __syncthreads();
   const int fs = L.misc[kMsFs], pairs = L.misc[kMsPairs], tot = L.misc[kMsTot];
