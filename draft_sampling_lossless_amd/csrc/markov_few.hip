@@ -353,6 +353,22 @@ __device__ __forceinline__ void load_efrag_published(const uint32_t* row, bool v
   }
 }
 
+// A operand from the W1 row that phase C staged in this workgroup's LDS for the
+// previous token of `step` (step 0: the anchor; step i: survivor sel[i-1] of step
+// i-1); only after a staged chain that covers every step
+__device__ __forceinline__ void load_efrag_lds(const Lds& L, int step, bool valid, int r, int ksteps, int g, int cap,
+                                               bf16x8 (&efrag)[kMaxKSteps]) {
+  const int* sel = L.misc + kMsSel;
+  const int row = (step == 0) ? 0 : 1 + (step - 1) * cap + sel[step - 1];
+  const uint16_t* src = L.w1c + (size_t)row * r;
+#pragma unroll
+  for (int s = 0; s < kMaxKSteps; ++s) {
+    const int k = s * 32 + 8 * g;
+    efrag[s] = (s < ksteps && k < r && valid) ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + k))
+                                              : zero8();
+  }
+}
+
 // base logits of phase-D tile t (request t / tpr, steps 16 * (t % tpr) ..) that lane
 // (n, g) of `wave` combines with its MFMA results: chunk wave + 4u, entries 4n..4n+3,
 // steps 4g + i (indices clamped; lanes outside the tile never use the value)
@@ -688,7 +704,9 @@ __device__ __forceinline__ void publish_row_from(const FewArgs& a, int b, int st
 }
 
 // ------------------------------------------------------------------------ phase C
-__device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, int G) {
+// writer: this workgroup stores the request's outputs (tokens, first per-step
+// step, published rows); other workgroups that run the phase only keep its results
+__device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, int G, bool writer) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.N, r = a.r, cap = a.cap, kc = r / 8, half = r / 2;
   const int per = G * kTop;  // recorded entries of one step (<= 64 * kPerLane)
@@ -863,13 +881,13 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
           }
         }
         sel[i] = bq;
-        st_i(a.draft_tokens + (size_t)b * N + i, (bt == 0x7FFFFFFF) ? 0 : bt);
+        if (writer) st_i(a.draft_tokens + (size_t)b * N + i, (bt == 0x7FFFFFFF) ? 0 : bt);
         p = bq;
       }
     }
     __syncthreads();
     // publish the W1 rows of each step's previous token (step 0: the anchor)
-    for (int x = tid; x < fs * half; x += 256) {
+    for (int x = writer ? tid : fs * half; x < fs * half; x += 256) {
       const int i = x / half, k2 = x - i * half;
       const uint16_t* src = L.w1c + (size_t)((i == 0) ? 0 : 1 + (i - 1) * cap + sel[i - 1]) * r;
       st_u(a.ws.rows + (size_t)(b * N + i) * half + k2, reinterpret_cast<const uint32_t*>(src)[k2]);
@@ -898,15 +916,16 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
         wave_argmax(bk, bt);
         prev = (bt != 0x7FFFFFFF) ? bt : 0;
         if (lane == 0) {
-          st_i(a.draft_tokens + (size_t)b * N + i, prev);
+          if (writer) st_i(a.draft_tokens + (size_t)b * N + i, prev);
           sel[i] = prev;
         }
       }
     }
     __syncthreads();
-    for (int i = 0; i < fs; ++i) publish_row_from(a, b, i, (i == 0) ? req_anchor(L, b) : sel[i - 1], tid, 256);
+    if (writer)
+      for (int i = 0; i < fs; ++i) publish_row_from(a, b, i, (i == 0) ? req_anchor(L, b) : sel[i - 1], tid, 256);
   }
-  if (tid == 0) st_i(a.ws.fstep + b, fs);
+  if (writer && tid == 0) st_i(a.ws.fstep + b, fs);
   __syncthreads();
 }
 
@@ -995,7 +1014,7 @@ __device__ __forceinline__ void step_prevs(const FewArgs& a, int G, int s, const
 
 // ------------------------------------------------------------------------ phase D
 __device__ __forceinline__ void phase_d(const FewArgs& a, const Lds& L, const Slice& sl, int vwg, int G,
-                                        float4 (&pre)[kMaxCPW][4]) {
+                                        float4 (&pre)[kMaxCPW][4], bool rows_in_lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int r = a.r, ksteps = (r + 31) / 32, row_bytes = 2 * r + 16, B = a.B, N = a.N, half = r / 2;
@@ -1013,7 +1032,10 @@ __device__ __forceinline__ void phase_d(const FewArgs& a, const Lds& L, const Sl
     // MFMA rows = steps st0 .. st0+15 of request b; lane row n is step st0 + n
     const int sn = st0 + n;
     bf16x8 efrag[kMaxKSteps];
-    load_efrag_published(a.ws.rows + (size_t)(b * N + min(sn, N - 1)) * half, sn < N, r, ksteps, g, efrag);
+    if (rows_in_lds)
+      load_efrag_lds(L, min(sn, N - 1), sn < N, r, ksteps, g, a.cap, efrag);
+    else
+      load_efrag_published(a.ws.rows + (size_t)(b * N + min(sn, N - 1)) * half, sn < N, r, ksteps, g, efrag);
     float bm[4], bs[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1230,13 +1252,23 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
     for (int vwg = 0; vwg < G; ++vwg)
       if (vwg != wg) phase_ab(a, L, vwg, G, false);
 
-  for (int b = solo ? 0 : wg; b < B; b += solo ? 1 : G) phase_c(a, L, b, G);
-  if (!solo) grid_barrier(a.ws.ctr, ++round, G);
+  // With one request every workgroup runs phase C itself (workgroup 0 stores the
+  // outputs): when its staged chain covers every step, phase D takes the W1 rows
+  // from this workgroup's LDS, and neither the second barrier nor the published
+  // rows are needed.  (Every workgroup reaches the same decision: the same records,
+  // the same arithmetic.)
+  const bool redundant = !solo && B == 1;
+  if (redundant)
+    phase_c(a, L, 0, G, wg == 0);
+  else
+    for (int b = solo ? 0 : wg; b < B; b += solo ? 1 : G) phase_c(a, L, b, G, true);
+  const bool rows_in_lds = redundant && L.misc[kMsFs] == N && L.misc[kMsFit] != 0;
+  if (!solo && !rows_in_lds) grid_barrier(a.ws.ctr, ++round, G);
 
   // per-step pass from the first incomplete step of any request
   int* prevs = L.misc + kMsPrev;
   int* fstl = L.misc + kMsFst;
-  if (tid < B) fstl[tid] = ld_i(a.ws.fstep + tid);
+  if (tid < B) fstl[tid] = rows_in_lds ? N : ld_i(a.ws.fstep + tid);
   __syncthreads();
   int fmin = N;
   for (int b = 0; b < B; ++b) fmin = min(fmin, fstl[b]);
@@ -1264,7 +1296,7 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
       load_slice<false>(a, L, sl);
       load_tile(pre, a.logits, 0, (N + 15) / 16, B, N, a.Vd, sl.vbase, wave, n, g);
     }
-    phase_d(a, L, sl, vwg, G, pre);
+    phase_d(a, L, sl, vwg, G, pre, rows_in_lds);
   }
 
   // log Z: the last workgroup to finish its partials merges them.  In normal mode
