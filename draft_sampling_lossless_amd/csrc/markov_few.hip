@@ -115,18 +115,26 @@ constexpr int kMsPrev = 352, kMsFst = 368;  // [16] each (per-step pass)
 constexpr int kMsN1 = 384;                  // [16] floats: largest recorded W1 norm per request (phase B)
 constexpr int kMsT = 400, kMsRid = 416, kMsAnc = 432;  // [16] each: temperature, request id, anchor per request
 
-// a recorded entry is two words: (key bits << 32 | draft index (-1: none)) and
-// (||W1[t(j)]|| bits << 32 | ||W2[j]|| bits)
-constexpr uint64_t kEmptySlot = ((uint64_t)0xFF800000u << 32) | 0xFFFFFFFFull;
-__device__ __forceinline__ float slot_w2n(uint64_t n) { return __uint_as_float((uint32_t)n); }
-__device__ __forceinline__ float slot_w1n(uint64_t n) { return __uint_as_float((uint32_t)(n >> 32)); }
+// A recorded entry is one word: key bits << 32 | ||W2[j]|| rounded up to bf16
+// << 16 | j - (first draft index of its slice) (0xFFFF: none).  A candidate in
+// phase C carries the draft index itself: key bits << 32 | j.
+constexpr uint64_t kEmptySlot = ((uint64_t)0xFF800000u << 32) | 0xFFFFull;
 __device__ __forceinline__ float slot_key(uint64_t s) { return __uint_as_float((uint32_t)(s >> 32)); }
+__device__ __forceinline__ float rec_w2n(uint64_t s) { return __uint_as_float((uint32_t)s & 0xFFFF0000u); }
+__device__ __forceinline__ int rec_jl(uint64_t s) { return (int)((uint32_t)s & 0xFFFFu); }
 __device__ __forceinline__ int slot_j(uint64_t s) { return (int)(uint32_t)s; }
+// bf16 bits of the smallest bf16 >= x (x >= 0; inf and NaN stay)
+__device__ __forceinline__ uint32_t bf16_up(float x) {
+  const uint32_t b = __float_as_uint(x);
+  if ((b & 0x7F800000u) == 0x7F800000u) return b >> 16;
+  return (b + 0xFFFFu) >> 16;
+}
+static_assert(kMaxSlice <= 0xFFFF, "slice-local draft index must fit 16 bits");
 
 struct FewWs {
   float* norms;           // [G] largest squared W2 row norm of each slice
   float* n1;              // [B][G] largest W1 norm of each request's possible previous tokens, per slice
-  uint64_t* rec;          // [B*N][G][kTop][2] recorded entries
+  uint64_t* rec;          // [B*N][G][kTop] recorded entries
   int* fstep;             // [B] first step left to the per-step pass (N if none)
   MarkovPartial* partF;   // [2][B][G] per-step partials of that pass
   MarkovPartial* partD;   // [B*N][G] log-sum-exp partials of the processed rows
@@ -587,17 +595,15 @@ __device__ __forceinline__ void records_batch(const FewArgs& a, const Lds& L, co
       ss = row_norm2(a.w1 + (size_t)t * r, r);  // (every lane of the entry; one stores)
     }
     if (piece == 0 && row < rows) {
-      uint64_t w0 = kEmptySlot, w1w = 0;
+      uint64_t w0 = kEmptySlot;
       if (ok) {
         const float n1e = sqrtf(ss);
-        w0 = ((uint64_t)__float_as_uint(key_of((uint32_t)(rk >> 32))) << 32) | (uint32_t)j;
-        w1w = ((uint64_t)__float_as_uint(n1e) << 32) | __float_as_uint(L.w2n[j - sl.vbase]);
+        w0 = ((uint64_t)__float_as_uint(key_of((uint32_t)(rk >> 32))) << 32) |
+             (bf16_up(L.w2n[j - sl.vbase]) << 16) | (uint32_t)(j - sl.vbase);
         const int b = row / N;
         if (row - b * N < N - 1) atomicMax(reinterpret_cast<int*>(n1r) + b, __float_as_int(n1e));
       }
-      uint64_t* dst = a.ws.rec + (((size_t)row * G + vwg) * kTop + (e % kTop)) * 2;
-      st_u64(dst, w0);
-      st_u64(dst + 1, w1w);
+      st_u64(a.ws.rec + ((size_t)row * G + vwg) * kTop + (e % kTop), w0);
     }
   }
   __syncthreads();
@@ -710,24 +716,21 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.N, r = a.r, cap = a.cap, kc = r / 8, half = r / 2;
   const int per = G * kTop;  // recorded entries of one step (<= 64 * kPerLane)
-  const uint64_t* recb = a.ws.rec + (size_t)b * N * per * 2;
+  const uint64_t* recb = a.ws.rec + (size_t)b * N * per;
+  const int sw = a.CH * kChunk;  // draft entries per slice
   int* cnt = L.misc + kMsCnt;
   int* inc = L.misc + kMsInc;
   int* offp = L.misc + kMsOff;
   int* sel = L.misc + kMsSel;
   int* pre = L.misc + kMsPre;
   // recorded entries of steps i0 and i0 + 4 (this wave's steps of one round)
-  uint64_t h[2][kPerLane], hn[2][kPerLane];
+  uint64_t h[2][kPerLane];
   auto load_recs = [&](int i0) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int i = min(i0 + 4 * st, N - 1);
 #pragma unroll
-      for (int u = 0; u < kPerLane; ++u) {
-        const uint64_t* e = recb + ((size_t)i * per + min(lane + 64 * u, per - 1)) * 2;
-        h[st][u] = ld_u64(e);
-        hn[st][u] = ld_u64(e + 1);
-      }
+      for (int u = 0; u < kPerLane; ++u) h[st][u] = ld_u64(recb + (size_t)i * per + min(lane + 64 * u, per - 1));
     }
   };
   // the first round's records are requested together with the norms below
@@ -753,7 +756,7 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
       float lb = -INFINITY;
 #pragma unroll
       for (int u = 0; u < kPerLane; ++u)
-        if (lane + 64 * u < per) lb = fmaxf(lb, slot_key(h[st][u]) - cb * slot_w2n(hn[st][u]) - kKeySlack);
+        if (lane + 64 * u < per) lb = fmaxf(lb, slot_key(h[st][u]) - cb * rec_w2n(h[st][u]) - kKeySlack);
       lb = wave_max_f32(lb);
       // nothing above -inf recorded, or no usable bound: leave the step to the per-step pass
       const bool bad = !(lb > -INFINITY);
@@ -763,12 +766,13 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
       for (int u = 0; u < kPerLane; ++u) {
         const int e = lane + 64 * u;
         const float k = slot_key(h[st][u]);
-        const bool sv = e < per && k + cb * slot_w2n(hn[st][u]) + kKeySlack >= lb;
+        const bool sv = e < per && k + cb * rec_w2n(h[st][u]) + kKeySlack >= lb;
         const uint64_t m = __ballot(sv);
         // a slice whose unrecorded entries could still reach the bound
         cov |= __ballot(e < per && (e % kTop) == kTop - 1 && k + cb * L.n2s[e / kTop] + kKeySlack >= lb);
         const int pos = total + lanes_below(m);
-        if (sv && pos < cap) L.cands[i * cap + pos] = h[st][u];
+        if (sv && pos < cap)
+          L.cands[i * cap + pos] = (h[st][u] & 0xFFFFFFFF00000000ull) | (uint32_t)((e / kTop) * sw + rec_jl(h[st][u]));
         total += __popcll(m);
       }
       if (lane == 0) {
@@ -816,7 +820,7 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
   }
   __syncthreads();
   const int fs = L.misc[kMsFs], pairs = L.misc[kMsPairs], tot = L.misc[kMsTot];
-  if (L.misc[kMsFit]) {
+  if (__builtin_expect(L.misc[kMsFit] != 0, 1)) {
     // stage: W1[anchor] -> w1c row 0; survivor (i, q) (compact index pre[i] + q): its
     // W2 row -> w2c row i*cap+q, the W1 row of its target -> w1c row 1+i*cap+q
     const int np = kc * (1 + 2 * tot);
@@ -902,10 +906,10 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
         float bk = -INFINITY;
         int bt = 0x7FFFFFFF;
         for (int q = lane; q < per; q += 64) {
-          const uint64_t s = ld_u64(recb + ((size_t)i * per + q) * 2);
+          const uint64_t s = ld_u64(recb + (size_t)i * per + q);
           const float k = slot_key(s);
-          if (!(k + cb * slot_w2n(ld_u64(recb + ((size_t)i * per + q) * 2 + 1)) + kKeySlack >= L.thr[i])) continue;
-          const int j = slot_j(s);
+          if (!(k + cb * rec_w2n(s) + kKeySlack >= L.thr[i])) continue;
+          const int j = (q / kTop) * sw + rec_jl(s);
           const float full = k + c * dot_bf16(e1, a.w2 + (size_t)j * r, r);
           const int t = target_of(a.d2t, j);
           if (key_beats(full, t, bk, bt)) {
@@ -1241,14 +1245,14 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
   float4 pre[kMaxCPW][4];  // base logits of the first phase-D tile, read while the chain runs
   load_tile(pre, a.logits, 0, (N + 15) / 16, B, N, a.Vd, slice_of(a, wg).vbase, wave, n, g);
   const int role = first_barrier_role(a, G, arrival == 0u, L.misc);
-  if (role == 0) {  // (only in solo mode)
+  if (__builtin_expect(role == 0, 0)) {  // (only in solo mode)
     depart(a.ws.ctr, L.misc);
     return;
   }
   const bool solo = role == 2;
   const int v0 = solo ? 0 : wg, v1 = solo ? G : wg + 1;  // slices this workgroup runs
   unsigned round = 1;
-  if (solo)
+  if (__builtin_expect(solo, 0))
     for (int vwg = 0; vwg < G; ++vwg)
       if (vwg != wg) phase_ab(a, L, vwg, G, false);
 
@@ -1273,18 +1277,18 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
   int fmin = N;
   for (int b = 0; b < B; ++b) fmin = min(fmin, fstl[b]);
   const bool writer = solo || wg == 0;
-  for (int s = fmin; s < N; ++s) {
-    step_prevs(a, G, s, fstl, prevs, writer);
-    bf16x8 efrag[kMaxKSteps];
-    load_efrag(a.w1, (n < B) ? prevs[n] : 0, n < B && fstl[n] <= s, a.V, r, ksteps, g, efrag);
-    for (int vwg = v0; vwg < v1; ++vwg) {
-      const Slice sl = slice_of(a, vwg);
-      if (solo) load_slice<false>(a, L, sl);
-      step_partial(a, L, sl, vwg, G, s, fstl, efrag);
+  if (__builtin_expect(fmin < N, 0)) {
+    for (int s = fmin; s < N; ++s) {
+      step_prevs(a, G, s, fstl, prevs, writer);
+      bf16x8 efrag[kMaxKSteps];
+      load_efrag(a.w1, (n < B) ? prevs[n] : 0, n < B && fstl[n] <= s, a.V, r, ksteps, g, efrag);
+      for (int vwg = v0; vwg < v1; ++vwg) {
+        const Slice sl = slice_of(a, vwg);
+        if (solo) load_slice<false>(a, L, sl);
+        step_partial(a, L, sl, vwg, G, s, fstl, efrag);
+      }
+      if (!solo) grid_barrier(a.ws.ctr, ++round, G);
     }
-    if (!solo) grid_barrier(a.ws.ctr, ++round, G);
-  }
-  if (fmin < N) {
     // tokens of the last step (s == N: nothing is published)
     step_prevs(a, G, N, fstl, prevs, writer);
     if (!solo) grid_barrier(a.ws.ctr, ++round, G);
@@ -1292,7 +1296,7 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
 
   for (int vwg = v0; vwg < v1; ++vwg) {
     const Slice sl = slice_of(a, vwg);
-    if (solo) {
+    if (__builtin_expect(solo, 0)) {
       load_slice<false>(a, L, sl);
       load_tile(pre, a.logits, 0, (N + 15) / 16, B, N, a.Vd, sl.vbase, wave, n, g);
     }
@@ -1351,7 +1355,7 @@ FewPlan plan_markov_few(int B, int N, int Vd, int r, int cus) {
   const size_t rowsN = (size_t)B * N, G = (size_t)p.gmax;
   p.off_norms = take(G * sizeof(float));
   p.off_n1 = take((size_t)B * G * sizeof(float));
-  p.off_rec = take(rowsN * G * kTop * 2 * sizeof(uint64_t));
+  p.off_rec = take(rowsN * G * kTop * sizeof(uint64_t));
   p.off_fstep = take((size_t)B * sizeof(int));
   p.off_partF = take(2 * (size_t)B * G * sizeof(MarkovPartial));
   p.off_partD = take(rowsN * G * sizeof(MarkovPartial));
