@@ -181,7 +181,7 @@ __host__ __device__ inline CRegion cregion(int N, int cap, int r) {
 
 struct Lds {
   char* w2s;          // [S] W2 rows of the slice, slot-permuted per 64-chunk, row_bytes apart
-  float* w2n;         // [kMaxSlice] norms of those rows
+  float* w2n;         // [kMaxSlice] squared norms of those rows
   float* n2s;         // [kMaxSlices] largest W2 row norm of each slice (phase C)
   float* thr;         // [64] survivor thresholds (largest lower end) of the request in phase C
   float* redf;        // reduction scratch (1 KB)
@@ -259,15 +259,14 @@ __device__ __forceinline__ uint4 load_clamped(const uint4* src, int idx, int n, 
   return src[idx < n ? idx : n - row_pieces + (idx & (row_pieces - 1))];
 }
 
+// (bf16 pair dot products: the norms only bound biases, with a relative slack far
+// above their rounding)
 __device__ __forceinline__ float sumsq8(const uint4& v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float ss = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float a = __uint_as_float(w[q] << 16), b = __uint_as_float(w[q] & 0xFFFF0000u);
-    ss += a * a + b * b;
-  }
-  return ss;
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  float ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, v.x), __builtin_bit_cast(b2, v.x), 0.0f, false);
+  ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, v.y), __builtin_bit_cast(b2, v.y), ss, false);
+  ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, v.z), __builtin_bit_cast(b2, v.z), ss, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, v.w), __builtin_bit_cast(b2, v.w), ss, false);
 }
 
 __device__ __forceinline__ float row_norm2(const uint16_t* row, int r) {
@@ -430,7 +429,7 @@ __device__ __forceinline__ float load_slice(const FewArgs& a, const Lds& L, cons
           if (kNorm) {
             const float ss = group_sum(sumsq8(v[u]), kc);
             n2 = fmaxf(n2, ss);
-            if (piece == 0) L.w2n[rho_all] = sqrtf(ss);
+            if (piece == 0) L.w2n[rho_all] = ss;
           }
           const int c = rho_all >> 6, rho = rho_all & (kChunk - 1);
           const int slot = c * kChunk + (rho & 3) * 16 + (rho >> 2);
@@ -451,7 +450,7 @@ __device__ __forceinline__ float load_slice(const FewArgs& a, const Lds& L, cons
       for (int q = tid; q < sl.nch * kChunk; q += 256) {
         const float ss = row_norm2(a.w2 + (size_t)(sl.vbase + min(q, sl.nvalid - 1)) * r, r);
         n2 = fmaxf(n2, ss);
-        L.w2n[q] = sqrtf(ss);
+        L.w2n[q] = ss;
       }
   }
   __syncthreads();
@@ -469,10 +468,12 @@ __device__ __forceinline__ void w2_issue(const FewArgs& a, const Slice& sl, int 
 }
 
 // ... and their use: into LDS (slot-permuted per 64-chunk for the MFMA B operand),
-// each row's norm into w2n; returns this thread's largest squared row norm
+// each row's squared norm into w2n; returns this thread's largest squared row
+// norm.  KC: pieces per row when fixed at compile time (0: a.r / 8 at run time).
+template <int KC>
 __device__ __forceinline__ float w2_consume(const FewArgs& a, const Lds& L, const Slice& sl, int p0,
                                             const uint4 (&v)[kFly]) {
-  const int kc = a.r / 8, lg = __builtin_ctz(kc), row_bytes = 2 * a.r + 16;
+  const int kc = KC ? KC : a.r / 8, lg = __builtin_ctz(kc), row_bytes = 16 * (kc + 1);
   const int pieces = sl.nch * kChunk * kc;
   float n2 = 0.0f;
 #pragma unroll
@@ -482,13 +483,18 @@ __device__ __forceinline__ float w2_consume(const FewArgs& a, const Lds& L, cons
       const int rho_all = p >> lg, piece = p & (kc - 1);
       const float ss = group_sum(sumsq8(v[u]), kc);
       n2 = fmaxf(n2, ss);
-      if (piece == 0) L.w2n[rho_all] = sqrtf(ss);
+      if (piece == 0) L.w2n[rho_all] = ss;
       const int c = rho_all >> 6, rho = rho_all & (kChunk - 1);
       const int slot = c * kChunk + (rho & 3) * 16 + (rho >> 2);
       *reinterpret_cast<uint4*>(L.w2s + (size_t)slot * row_bytes + piece * 16) = v[u];
     }
   }
   return n2;
+}
+// (rank 64, eight pieces per row, has its own copy with the lane sums unrolled)
+__device__ __forceinline__ float w2_consume_any(const FewArgs& a, const Lds& L, const Slice& sl, int p0,
+                                                const uint4 (&v)[kFly]) {
+  return (a.r == 64) ? w2_consume<8>(a, L, sl, p0, v) : w2_consume<0>(a, L, sl, p0, v);
 }
 
 // Rows row0 .. row0+kRowBatch-1: base logits at this thread's four entries, and
@@ -599,7 +605,7 @@ __device__ __forceinline__ void records_batch(const FewArgs& a, const Lds& L, co
       if (ok) {
         const float n1e = sqrtf(ss);
         w0 = ((uint64_t)__float_as_uint(key_of((uint32_t)(rk >> 32))) << 32) |
-             (bf16_up(L.w2n[j - sl.vbase]) << 16) | (uint32_t)(j - sl.vbase);
+             (bf16_up(sqrtf(L.w2n[j - sl.vbase])) << 16) | (uint32_t)(j - sl.vbase);
         const int b = row / N;
         if (row - b * N < N - 1) atomicMax(reinterpret_cast<int*>(n1r) + b, __float_as_int(n1e));
       }
@@ -651,10 +657,10 @@ __device__ __forceinline__ unsigned phase_ab(const FewArgs& a, const Lds& L, int
     __builtin_amdgcn_sched_barrier(0);
     arrival = take_arrival_now(a, take_arrival);
     keys_batch(a, sl, 0, rb, red64);
-    n2 = w2_consume(a, L, sl, 0, v);
+    n2 = w2_consume_any(a, L, sl, 0, v);
     for (int p0 = 256 * kFly; p0 < pieces; p0 += 256 * kFly) {
       w2_issue(a, sl, p0, v);
-      n2 = fmaxf(n2, w2_consume(a, L, sl, p0, v));
+      n2 = fmaxf(n2, w2_consume_any(a, L, sl, p0, v));
     }
     __syncthreads();
   } else {
