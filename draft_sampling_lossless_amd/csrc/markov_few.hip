@@ -110,7 +110,8 @@ constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0) (gfx9 encoding)
 // misc layout (ints)
 constexpr int kMsCnt = 0, kMsInc = 64, kMsOff = 128, kMsSel = 192, kMsPre = 256;  // [64] each ([65] for kMsPre)
 constexpr int kMsFs = 336, kMsFit = 337, kMsPairs = 338, kMsTot = 339, kMsRole = 340, kMsTicket = 341;
-constexpr int kMsLastOut = 342;
+constexpr int kMsLastOut = 342, kMsRows = 343;
+constexpr int kMsRoff = 448;  // [64] first (previous survivor) row of each step in phase C
 constexpr int kMsPrev = 352, kMsFst = 368;  // [16] each (per-step pass)
 constexpr int kMsN1 = 384;                  // [16] floats: largest recorded W1 norm per request (phase B)
 constexpr int kMsT = 400, kMsRid = 416, kMsAnc = 432;  // [16] each: temperature, request id, anchor per request
@@ -802,26 +803,30 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
     const int nq = in ? min(ci, cap) : 0;
     const int cprev = __shfl_up(ci, 1);
     const int pr = in ? ((i == 0) ? 1 : min(cprev, cap)) * nq : 0;
+    const int np = in ? ((i == 0) ? 1 : min(cprev, cap)) : 0;  // previous survivors of step i
     const bool overflow = __ballot(in && ci > cap) != 0;
-    int sq = nq, sp = pr;  // inclusive prefix sums over the steps
+    int sq = nq, sp = pr, sr = np;  // inclusive prefix sums over the steps
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int aq = __shfl_up(sq, off), ap = __shfl_up(sp, off);
+      const int aq = __shfl_up(sq, off), ap = __shfl_up(sp, off), ar = __shfl_up(sr, off);
       if (lane >= off) {
         sq += aq;
         sp += ap;
+        sr += ar;
       }
     }
     if (in) {
       pre[i] = sq - nq;
       offp[i] = sp - pr;
+      L.misc[kMsRoff + i] = sr - np;
     }
-    const int tot = __shfl(sq, 63), pairs = __shfl(sp, 63);
+    const int tot = __shfl(sq, 63), pairs = __shfl(sp, 63), nrows = __shfl(sr, 63);
     if (lane == 0) {
       L.misc[kMsFs] = fs;
       L.misc[kMsFit] = (!overflow && pairs <= kPairs) ? 1 : 0;
       L.misc[kMsPairs] = pairs;
       L.misc[kMsTot] = tot;
+      L.misc[kMsRows] = nrows;
     }
   }
   __syncthreads();
@@ -875,24 +880,35 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
       L.fk[t] = slot_key(L.cands[i * cap + q]) + c * dot_bf16(e1, e2, r);
     }
     __syncthreads();
-    if (tid == 0) {  // the chain
+    // each step's winner for every previous survivor: the best (key, token) of the
+    // row, its index written over the row's first key (-1: no key beats the
+    // empty one)
+    const int* roff = L.misc + kMsRoff;
+    int* fki = reinterpret_cast<int*>(L.fk);
+    for (int x = tid; x < L.misc[kMsRows]; x += 256) {
+      const int i = search_le(roff, fs, x), pi = x - roff[i];
+      const int nq = min(cnt[i], cap), base = offp[i] + pi * nq;
+      float bk = -INFINITY;
+      int bt = 0x7FFFFFFF, bq = -1;
+      for (int q = 0; q < nq; ++q) {
+        const float k = L.fk[base + q];
+        const int t = L.tgt[i * cap + q];
+        if (key_beats(k, t, bk, bt)) {
+          bk = k;
+          bt = t;
+          bq = q;
+        }
+      }
+      fki[base] = bq;
+    }
+    __syncthreads();
+    if (tid == 0) {  // the chain through those winners
       int p = 0;
       for (int i = 0; i < fs; ++i) {
-        const int nq = min(cnt[i], cap);
-        float bk = -INFINITY;
-        int bt = 0x7FFFFFFF, bq = 0;
-        for (int q = 0; q < nq; ++q) {
-          const float k = L.fk[offp[i] + p * nq + q];
-          const int t = L.tgt[i * cap + q];
-          if (key_beats(k, t, bk, bt)) {
-            bk = k;
-            bt = t;
-            bq = q;
-          }
-        }
-        sel[i] = bq;
-        if (writer) st_i(a.draft_tokens + (size_t)b * N + i, (bt == 0x7FFFFFFF) ? 0 : bt);
-        p = bq;
+        const int bq = fki[offp[i] + p * min(cnt[i], cap)];
+        sel[i] = max(bq, 0);
+        if (writer) st_i(a.draft_tokens + (size_t)b * N + i, (bq < 0) ? 0 : L.tgt[i * cap + bq]);
+        p = max(bq, 0);
       }
     }
     __syncthreads();
