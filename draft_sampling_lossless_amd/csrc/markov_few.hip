@@ -328,6 +328,39 @@ __device__ __forceinline__ void chunk_bias(const char* chunk_rows, int row_bytes
   }
 }
 
+// The same for r == 32 * KS: every k is in range, so all B fragments of the chunk
+// are read first and the four entry groups' products run back to back.
+template <int KS>
+__device__ __forceinline__ void chunk_bias_k(const char* chunk_rows, int row_bytes, const bf16x8 (&efrag)[kMaxKSteps],
+                                             int n, int g, floatx4 (&acc)[4]) {
+  bf16x8 bfr[4][KS];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const char* rowp = chunk_rows + (size_t)(f * 16 + n) * row_bytes;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      bfr[f][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rowp + (s * 32 + 8 * g) * 2));
+  }
+  __builtin_amdgcn_sched_barrier(0);  // (every read issued before the first product)
+#pragma unroll
+  for (int f = 0; f < 4; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(efrag[s], bfr[f][s], acc[f], 0, 0, 0);
+}
+__device__ __forceinline__ void chunk_bias_any(const char* chunk_rows, int row_bytes, int ksteps, int r,
+                                               const bf16x8 (&efrag)[kMaxKSteps], int n, int g, floatx4 (&acc)[4]) {
+  if (r == 64)
+    chunk_bias_k<2>(chunk_rows, row_bytes, efrag, n, g, acc);
+  else if (r == 32)
+    chunk_bias_k<1>(chunk_rows, row_bytes, efrag, n, g, acc);
+  else if (r == 128)
+    chunk_bias_k<4>(chunk_rows, row_bytes, efrag, n, g, acc);
+  else
+    chunk_bias(chunk_rows, row_bytes, ksteps, r, efrag, n, g, acc);
+}
+
 // A operand from W1 row `prev` (read-only weights)
 __device__ __forceinline__ void load_efrag(const uint16_t* w1, int prev, bool valid, int V, int r, int ksteps, int g,
                                            bf16x8 (&efrag)[kMaxKSteps]) {
@@ -972,7 +1005,7 @@ __device__ __forceinline__ void step_partial(const FewArgs& a, const Lds& L, con
   }
   for (int cidx = wave; cidx < sl.nch; cidx += 4) {
     floatx4 acc[4];
-    chunk_bias(L.w2s + (size_t)cidx * kChunk * row_bytes, row_bytes, ksteps, r, efrag, n, g, acc);
+    chunk_bias_any(L.w2s + (size_t)cidx * kChunk * row_bytes, row_bytes, ksteps, r, efrag, n, g, acc);
     const int jb = sl.vbase + cidx * kChunk + 4 * n;
     if (jb >= a.Vd) continue;
     int tgt[4];
@@ -1073,7 +1106,7 @@ __device__ __forceinline__ void phase_d(const FewArgs& a, const Lds& L, const Sl
       const int cidx = wave + 4 * u;
       if (cidx >= sl.nch) break;  // uniform per wave
       floatx4 acc[4];
-      chunk_bias(L.w2s + (size_t)cidx * kChunk * row_bytes, row_bytes, ksteps, r, efrag, n, g, acc);
+      chunk_bias_any(L.w2s + (size_t)cidx * kChunk * row_bytes, row_bytes, ksteps, r, efrag, n, g, acc);
       const int jb = sl.vbase + cidx * kChunk + 4 * n;
       if (jb >= a.Vd) continue;
 #pragma unroll
