@@ -784,6 +784,10 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
   const float c = temp_scale(req_temperature(L, b));
   n1 = block_max(n1, L.redf);  // (its barriers also publish n2s)
   const float cb = bias_bound(c, n1);
+  // the widest bias of each of this lane's entries' slices (the same for every step)
+  float cbn[kPerLane];
+#pragma unroll
+  for (int u = 0; u < kPerLane; ++u) cbn[u] = cb * L.n2s[min(lane + 64 * u, per - 1) / kTop];
   // survivors of every step: one wave per step, two steps per round; compaction by
   // ballot into the step's own LDS region
   for (int i0 = wave; i0 < N; i0 += 8) {
@@ -800,20 +804,24 @@ __device__ __forceinline__ void phase_c(const FewArgs& a, const Lds& L, int b, i
       lb = wave_max_f32(lb);
       // nothing above -inf recorded, or no usable bound: leave the step to the per-step pass
       const bool bad = !(lb > -INFINITY);
-      int total = 0;
-      uint64_t cov = 0;
+      uint64_t cov = 0, m[kPerLane];
+      bool sv[kPerLane];
 #pragma unroll
       for (int u = 0; u < kPerLane; ++u) {
         const int e = lane + 64 * u;
         const float k = slot_key(h[st][u]);
-        const bool sv = e < per && k + cb * rec_w2n(h[st][u]) + kKeySlack >= lb;
-        const uint64_t m = __ballot(sv);
+        sv[u] = e < per && k + cb * rec_w2n(h[st][u]) + kKeySlack >= lb;
+        m[u] = __ballot(sv[u]);
         // a slice whose unrecorded entries could still reach the bound
-        cov |= __ballot(e < per && (e % kTop) == kTop - 1 && k + cb * L.n2s[e / kTop] + kKeySlack >= lb);
-        const int pos = total + lanes_below(m);
-        if (sv && pos < cap)
+        cov |= __ballot(e < per && (e % kTop) == kTop - 1 && k + cbn[u] + kKeySlack >= lb);
+      }
+      int total = 0;
+#pragma unroll
+      for (int u = 0; u < kPerLane; ++u) {
+        const int e = lane + 64 * u, pos = total + lanes_below(m[u]);
+        if (sv[u] && pos < cap)
           L.cands[i * cap + pos] = (h[st][u] & 0xFFFFFFFF00000000ull) | (uint32_t)((e / kTop) * sw + rec_jl(h[st][u]));
-        total += __popcll(m);
+        total += __popcll(m[u]);
       }
       if (lane == 0) {
         cnt[i] = total;
