@@ -139,21 +139,24 @@ __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A,
       af[st][u] = (st < spb && n < M) ? load_bf16x8(A + (size_t)n * H + k) : zero_bf16x8();
     }
 
-  // a contiguous run of 16-row blocks per workgroup
-  const int nblocks = (Vd + 15) / 16;
-  const int b0 = (int)((long)nblocks * blockIdx.x / gridDim.x);
-  const int b1 = (int)((long)nblocks * (blockIdx.x + 1) / gridDim.x);
-  const int nb = b1 - b0, L = 16 * nb;
+  // A contiguous run of LM-head rows per workgroup (the row counts differ by at most
+  // one, so no workgroup streams a whole block more than another), in 16-row blocks
+  // from its first row; the last block may be partial.
+  const int r0 = (int)((long)Vd * blockIdx.x / gridDim.x);
+  const int r1 = (int)((long)Vd * (blockIdx.x + 1) / gridDim.x);
+  const int nb = (r1 - r0 + 15) / 16, L = 16 * nb;
   const int T = nb * spb;  // stages this workgroup consumes
-  // stage t: block b0 + t / spb, k range (t % spb) * 512 .. +512; wave w loads rows
-  // w, w+4, w+8, w+12 of it (one 1 KB instruction each)
+  // stage t: block t / spb, k range (t % spb) * 512 .. +512; wave w loads rows
+  // w, w+4, w+8, w+12 of it (one 1 KB instruction each).  Rows past this run load
+  // its last row again (a cache hit, never stored), which keeps four loads per wave
+  // and stage for the ring's counted waits.
   auto issue = [&](int t) {
-    const int blk = b0 + t / spb, kst = t % spb;
+    const int blk = t / spb, kst = t % spb;
     char* base = ring + (t % SNS) * SSTAGE;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = wave + 4 * q;
-      const int j = min(blk * 16 + row, Vd - 1);  // rows past Vd load a valid row, never stored
+      const int j = min(r0 + blk * 16 + row, r1 - 1);
       __builtin_amdgcn_global_load_lds(W + (size_t)j * H + kst * 512 + lane * 8, base + row * SROW, 16, 0, 0);
     }
   };
@@ -204,15 +207,13 @@ __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A,
   __syncthreads();
   // the outputs leave only after the whole stream: a contiguous run of each output
   // row (writes interleaved with the stream cost it several percent)
-  const int jb = 16 * b0;
   for (int m = 0; m < M; ++m)
-    for (int x = tid; x < L; x += 256)
-      if (jb + x < Vd) C[(size_t)m * Vd + jb + x] = outl[m * L + x];
+    for (int x = tid; x < r1 - r0; x += 256) C[(size_t)m * Vd + r0 + x] = outl[m * L + x];
 }
 
 size_t k1_stream_lds(int M, int Vd, int grid) {
-  const int nblocks = (Vd + 15) / 16;
-  const size_t maxb = (size_t)(nblocks + grid - 1) / grid;
+  const size_t maxrows = ((size_t)Vd + grid - 1) / grid;  // the longest run of rows
+  const size_t maxb = (maxrows + 15) / 16;
   return SFIXED + (size_t)M * 16 * maxb * 4;
 }
 
