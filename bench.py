@@ -41,6 +41,10 @@ def parse():
     p.add_argument("--workload", default="qwen3_8b_single",
                    help="tiny | qwen3_8b_single | batched | admission | reduced_vocab")
     p.add_argument("--graph", action="store_true", help="replay each step as one captured HIP graph")
+    p.add_argument("--no-overlap", action="store_true",
+                   help="run the verify statistics and the admission on the launch stream, in order "
+                        "(by default they run on a second stream when B*N > 16; at one request the "
+                        "round is too short for the extra launches and the cross-stream wait to pay)")
     p.add_argument("--verify", default="rejection", choices=("rejection", "coupled"),
                    help="stage 3 rule: rejection sampling on p_t, p_d (default) or Gumbel-coupled verification")
     p.add_argument("--round", default="path", choices=("path", "full"),
@@ -62,10 +66,13 @@ def src_hash(path: str) -> str:
 class Path:
     """Device buffers and the four C-ABI calls of one round."""
 
-    def __init__(self, w, torch, dsl, synth, verify_mode="rejection", full_round=False):
+    def __init__(self, w, torch, dsl, synth, verify_mode="rejection", full_round=False, overlap=False):
         self.w, self.torch, self.dsl = w, torch, dsl
         self.coupled = verify_mode == "coupled"
         self.full = full_round
+        # overlap: the target-row statistics and the admission (which need neither stage 1
+        # nor stage 2 when the confidence is an input) run on a second stream beside them
+        self.overlap = overlap and not self.coupled and not full_round
         dev = torch.device("cuda:0")
         rp = synth.request_params(w)
 
@@ -135,6 +142,10 @@ class Path:
         torch.cuda.synchronize()
         self.setup_s = time.time() - t0
         self.ev = None
+        if self.overlap:
+            self.side = torch.cuda.Stream()               # (default priority)
+            self.ev_side, self.ev_main = torch.cuda.Event(), torch.cuda.Event()
+            self.ev_main.record()
 
     def budget(self):
         """K for this round: fixed, or (full round) the K chosen two rounds ago."""
@@ -148,6 +159,9 @@ class Path:
         """One round.  events: optional list of 5 (7 for a full round) torch.cuda.Event
         bracketing the stages."""
         w, dsl = self.w, self.dsl
+        if self.overlap and not events:
+            self.step_overlapped()
+            return
         rec = (lambda i: events[i].record()) if events else (lambda i: None)
         rec(0)
         dsl.draft_logits(self.hidden, self.lm_head, out=self.logits.view(w.M, w.Vd))
@@ -183,6 +197,25 @@ class Path:
             self.k_ready[slot].record()
             self.round += 1
             rec(6)
+
+
+    def step_overlapped(self):
+        """One round with the statistics pass and the admission on the side stream."""
+        w, dsl, torch = self.w, self.dsl, self.torch
+        main = torch.cuda.current_stream()
+        self.side.wait_event(self.ev_main)   # the previous round's verify has read both outputs
+        with torch.cuda.stream(self.side):
+            dsl.verify_stats(self.target, self.temp, self.ws_verify, w.N)
+            dsl.admit(self.conf, self.budget(), survival=self.survival, admit_len=self.admit_len)
+            self.ev_side.record(self.side)
+        dsl.draft_logits(self.hidden, self.lm_head, out=self.logits.view(w.M, w.Vd))
+        dsl.markov_sample(self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, self.seed,
+                          draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov)
+        main.wait_event(self.ev_side)
+        dsl.verify(dsl.INPUT_LOGITS, self.target, self.logits, self.logz, self.tokens, self.inv,
+                   self.admit_len, self.temp, self.rid, self.seed, accepted=self.accepted,
+                   out_tokens=self.out_tokens, workspace=self.ws_verify, stats_done=True)
+        self.ev_main.record(main)
 
 
 def stage_bytes(w, admit_len, coupled):
@@ -316,7 +349,8 @@ def main():
                                    "replayed as one captured graph"}))
         sys.exit(2)
     w = synth.get(args.workload)
-    path = Path(w, torch, dsl, synth, args.verify, args.round == "full")
+    overlap = not (args.graph or args.no_overlap) and w.B * w.N > 16
+    path = Path(w, torch, dsl, synth, args.verify, args.round == "full", overlap=overlap)
 
     graph = None
     if args.graph:
@@ -387,7 +421,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "V": w.V, "Vd": w.Vd, "r": w.r,
-                   "K": w.budget, "graph": bool(args.graph)},
+                   "K": w.budget, "graph": bool(args.graph),
+                   "side_stream": "verify statistics + admission" if path.overlap else None},
         "stage_ms": {"draft_logits": round(stage_ms[0], 4), "markov_sample": round(stage_ms[1], 4),
                      "admit": round(stage_ms[2], 4), "verify": round(stage_ms[3], 4)},
         "stage_hbm_gbs": {"markov_sample": round(k2_bytes / (stage_ms[1] * 1e-3) / 1e9, 1),

@@ -455,7 +455,9 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
                                int Vd, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   const int sgrid = min(cu_count(), (Vd + 15) / 16);
-  const size_t slds = k1_stream_lds(M, Vd, sgrid);
+  // (at least half of a CU's 160 KB: one stream workgroup per CU, also when another
+  // stream's kernels fill the chip at the same time; two on one CU would halve both)
+  const size_t slds = std::max(k1_stream_lds(M, Vd, sgrid), (size_t)(81 * 1024));
   if (M <= 16 && H % 512 == 0 && H <= 4096 && slds <= SFIXED + SOUT_MAX) {
     static bool attr_set[64] = {false};
     int dev = 0;
