@@ -41,10 +41,10 @@ def parse():
     p.add_argument("--workload", default="qwen3_8b_single",
                    help="tiny | qwen3_8b_single | batched | admission | reduced_vocab")
     p.add_argument("--graph", action="store_true", help="replay each step as one captured HIP graph")
-    p.add_argument("--no-overlap", action="store_true",
-                   help="run the verify statistics and the admission on the launch stream, in order "
-                        "(by default they run on a second stream when B*N > 16; at one request the "
-                        "round is too short for the extra launches and the cross-stream wait to pay)")
+    p.add_argument("--overlap", action="store_true",
+                   help="run the verify statistics and the admission on a second stream beside stages 1-2. "
+                        "Not the default: it assumes the target logits exist before the draft does, "
+                        "which a draft-then-verify loop does not have (the target scores the draft)")
     p.add_argument("--verify", default="rejection", choices=("rejection", "coupled"),
                    help="stage 3 rule: rejection sampling on p_t, p_d (default) or Gumbel-coupled verification")
     p.add_argument("--round", default="path", choices=("path", "full"),
@@ -349,7 +349,7 @@ def main():
                                    "replayed as one captured graph"}))
         sys.exit(2)
     w = synth.get(args.workload)
-    overlap = not (args.graph or args.no_overlap) and w.B * w.N > 16
+    overlap = args.overlap and not args.graph
     path = Path(w, torch, dsl, synth, args.verify, args.round == "full", overlap=overlap)
 
     graph = None
