@@ -27,6 +27,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "dspark.h"
 #include "device.hpp"
@@ -147,15 +148,10 @@ __device__ __forceinline__ RacePartial load_race(const RacePartial* p) {
 
 // ------------------------------------------------------------------ row statistics
 
-__global__ __launch_bounds__(256) void verify_rowstats(const float* __restrict__ target,
-                                                       const int32_t* __restrict__ verify_len,
-                                                       const float* __restrict__ temperature,
-                                                       RowStat* __restrict__ stats, int B, int N, int V,
-                                                       int nchunks, int chunk) {
-  const int row = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
-  const int b = row / (N + 1), k = row % (N + 1);
-  const int L = verify_len ? min(max(verify_len[b], 0), N) : N;
-  if (k > L) return;
+// This workgroup's partial statistics of chunk c of target row `row` (request b);
+// every thread calls it, thread 0 gets the result.
+__device__ __forceinline__ RowStat rowstats_part(const float* __restrict__ target, const float* __restrict__ temperature,
+                                                 int row, int b, int c, int V, int chunk) {
   const float T = temperature[b];
   const bool hot = T > 0.0f;
   const float c2 = hot ? (1.0f / T) * kLog2e : 1.0f;
@@ -207,29 +203,43 @@ __global__ __launch_bounds__(256) void verify_rowstats(const float* __restrict__
   const int wave = tid >> 6;
   if ((tid & 63) == 0) red[wave] = RowStat{m, s, av, ai};
   __syncthreads();
-  if (tid == 0) {
-    RowStat a = red[0];
+  RowStat a = red[0];
+  if (tid == 0)
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) stat_merge(a.m, a.s, a.amax, a.aidx, red[w].m, red[w].s, red[w].amax, red[w].aidx);
-    stats[(size_t)row * nchunks + c] = a;
-  }
+  return a;
+}
+
+__global__ __launch_bounds__(256) void verify_rowstats(const float* __restrict__ target,
+                                                       const int32_t* __restrict__ verify_len,
+                                                       const float* __restrict__ temperature,
+                                                       RowStat* __restrict__ stats, int B, int N, int V,
+                                                       int nchunks, int chunk) {
+  const int row = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+  const int b = row / (N + 1), k = row % (N + 1);
+  const int L = verify_len ? min(max(verify_len[b], 0), N) : N;
+  if (k > L) return;
+  const RowStat a = rowstats_part(target, temperature, row, b, c, V, chunk);
+  if (threadIdx.x == 0) stats[(size_t)row * nchunks + c] = a;
 }
 
 // ------------------------------------------------------------------ acceptance
 
-__global__ __launch_bounds__(256) void verify_accept(int input_kind, const float* __restrict__ target,
-                                                     const float* __restrict__ draft,
-                                                     const float* __restrict__ draft_log_z,
-                                                     const int32_t* __restrict__ draft_tokens,
-                                                     const int32_t* __restrict__ inv_map,
-                                                     const int32_t* __restrict__ verify_len,
-                                                     const float* __restrict__ temperature,
-                                                     const uint32_t* __restrict__ request_id, uint32_t key0,
-                                                     uint32_t key1, const RowStat* __restrict__ stats,
-                                                     float2* __restrict__ rstat, Job* __restrict__ jobs,
-                                                     unsigned* __restrict__ tickets, int32_t* __restrict__ accepted,
-                                                     int32_t* __restrict__ out_tokens, float* __restrict__ accept_prob,
-                                                     int B, int N, int V, int Vd, int nchunks, int sample_chunks) {
-  const int b = blockIdx.x;
+// The acceptance of request b by one 256-thread workgroup.  kCoherent: the
+// partial statistics were written by other workgroups of the same launch (loads
+// at device scope).
+template <bool kCoherent>
+__device__ __forceinline__ void accept_body(int b, int input_kind, const float* __restrict__ target,
+                                            const float* __restrict__ draft, const float* __restrict__ draft_log_z,
+                                            const int32_t* __restrict__ draft_tokens,
+                                            const int32_t* __restrict__ inv_map,
+                                            const int32_t* __restrict__ verify_len,
+                                            const float* __restrict__ temperature,
+                                            const uint32_t* __restrict__ request_id, uint32_t key0, uint32_t key1,
+                                            const RowStat* __restrict__ stats, float2* __restrict__ rstat,
+                                            Job* __restrict__ jobs, unsigned* __restrict__ tickets,
+                                            int32_t* __restrict__ accepted, int32_t* __restrict__ out_tokens,
+                                            float* __restrict__ accept_prob, int N, int V, int Vd, int nchunks,
+                                            int sample_chunks) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = verify_len ? min(max(verify_len[b], 0), N) : N;
   const uint32_t req = request_id[b];
@@ -270,7 +280,13 @@ __global__ __launch_bounds__(256) void verify_accept(int input_kind, const float
       for (int c0 = sub; c0 < nchunks; c0 += 8 * kU) {
         RowStat q[kU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) q[u] = rp[min(c0 + 8 * u, nchunks - 1)];
+        for (int u = 0; u < kU; ++u) {
+          const RowStat* e = rp + min(c0 + 8 * u, nchunks - 1);
+          if (kCoherent)
+            q[u] = RowStat{ld_f(&e->m), ld_f(&e->s), ld_f(&e->amax), ld_i(&e->aidx)};
+          else
+            q[u] = *e;
+        }
 #pragma unroll
         for (int u = 0; u < kU; ++u)
           if (c0 + 8 * u < nchunks)
@@ -348,6 +364,83 @@ __global__ __launch_bounds__(256) void verify_accept(int input_kind, const float
     tickets[b] = 0u;
     if (probs) rstat[(size_t)b * (N + 1)] = make_float2(0.0f, 1.0f);
   }
+}
+
+__global__ __launch_bounds__(256) void verify_accept(int input_kind, const float* __restrict__ target,
+                                                     const float* __restrict__ draft,
+                                                     const float* __restrict__ draft_log_z,
+                                                     const int32_t* __restrict__ draft_tokens,
+                                                     const int32_t* __restrict__ inv_map,
+                                                     const int32_t* __restrict__ verify_len,
+                                                     const float* __restrict__ temperature,
+                                                     const uint32_t* __restrict__ request_id, uint32_t key0,
+                                                     uint32_t key1, const RowStat* __restrict__ stats,
+                                                     float2* __restrict__ rstat, Job* __restrict__ jobs,
+                                                     unsigned* __restrict__ tickets, int32_t* __restrict__ accepted,
+                                                     int32_t* __restrict__ out_tokens, float* __restrict__ accept_prob,
+                                                     int N, int V, int Vd, int nchunks, int sample_chunks) {
+  accept_body<false>(blockIdx.x, input_kind, target, draft, draft_log_z, draft_tokens, inv_map, verify_len,
+                     temperature, request_id, key0, key1, stats, rstat, jobs, tickets, accepted, out_tokens,
+                     accept_prob, N, V, Vd, nchunks, sample_chunks);
+}
+
+// Statistics and acceptance in one launch (logits input, B <= kFusedMaxB): the
+// (row, chunk) workgroups of the statistics pass write their partials, and the
+// last of a request's workgroups to finish (tickets taken once every thread's
+// stores have completed) runs that request's acceptance.  Same-address atomics are
+// served one at a time, so a request's workgroups count in kTGroups groups (local
+// index mod kTGroups, counters 128 bytes apart) and the last of each group counts
+// the group at the request's top counter.  The tickets are the launch's set of the
+// library's per-device sets, zero when the library loads; the last workgroup of a
+// request puts that request's counters back to zero (every other workgroup of the
+// request has counted by then), so every launch leaves its set as it found it.
+constexpr int kFusedMaxB = 16, kTicketSets = 64, kTGroups = 16;
+constexpr int kTStride = 32;                              // words between counters (128 bytes)
+constexpr int kTWordsPerReq = (kTGroups + 1) * kTStride;  // [top, group 0 .. group 15]
+__device__ __attribute__((aligned(256))) unsigned g_stat_tickets[kTicketSets * kFusedMaxB * kTWordsPerReq];
+
+__global__ __launch_bounds__(256) void verify_stats_accept(
+    const float* __restrict__ target, const float* __restrict__ draft, const float* __restrict__ draft_log_z,
+    const int32_t* __restrict__ draft_tokens, const int32_t* __restrict__ inv_map,
+    const int32_t* __restrict__ verify_len, const float* __restrict__ temperature,
+    const uint32_t* __restrict__ request_id, uint32_t key0, uint32_t key1, RowStat* __restrict__ stats,
+    float2* __restrict__ rstat, Job* __restrict__ jobs, unsigned* __restrict__ tickets,
+    int32_t* __restrict__ accepted, int32_t* __restrict__ out_tokens, float* __restrict__ accept_prob,
+    unsigned* __restrict__ stat_tickets, int N, int V, int Vd, int nchunks, int chunk, int sample_chunks) {
+  const int row = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+  const int b = row / (N + 1), k = row % (N + 1);
+  const int L = verify_len ? min(max(verify_len[b], 0), N) : N;
+  if (k <= L) {  // (uniform: rows past L are not read, but their workgroups still count)
+    const RowStat a = rowstats_part(target, temperature, row, b, c, V, chunk);
+    if (threadIdx.x == 0) {
+      RowStat* e = stats + (size_t)row * nchunks + c;
+      st_f(&e->m, a.m);
+      st_f(&e->s, a.s);
+      st_f(&e->amax, a.amax);
+      st_i(&e->aidx, a.aidx);
+    }
+  }
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  unsigned* rt = stat_tickets + (size_t)b * kTWordsPerReq;  // [0]: top; [(1 + g) * kTStride]: group g
+  const int total = (N + 1) * nchunks, li = k * nchunks + c, grp = li % kTGroups;
+  if (threadIdx.x == 0) {
+    int last = 0;
+    const unsigned old =
+        __hip_atomic_fetch_add(rt + (1 + grp) * kTStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1u == (unsigned)((total - grp + kTGroups - 1) / kTGroups))
+      last = __hip_atomic_fetch_add(rt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u ==
+             (unsigned)min(total, kTGroups);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x <= kTGroups)  // (every workgroup of b has counted)
+    __hip_atomic_store(rt + threadIdx.x * kTStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  accept_body<true>(b, DSPARK_INPUT_LOGITS, target, draft, draft_log_z, draft_tokens, inv_map, verify_len,
+                    temperature, request_id, key0, key1, stats, rstat, jobs, tickets, accepted, out_tokens,
+                    accept_prob, N, V, Vd, nchunks, sample_chunks);
 }
 
 // ------------------------------------------------------------------ sampling rows
@@ -634,13 +727,35 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
   float* apart = reinterpret_cast<float*>(w);
   const uint32_t k0 = (uint32_t)(seed & 0xFFFFFFFFu), k1 = (uint32_t)(seed >> 32);
   const bool probs = input_kind == DSPARK_INPUT_PROBS;
-  if (!probs && !stats_done) {
-    hipLaunchKernelGGL(verify_rowstats, dim3((unsigned)((long)B * (N + 1) * p.stat_chunks)), dim3(256), 0, stream,
-                       target, verify_len, temperature, stats, B, N, V, p.stat_chunks, p.stat_chunk);
+  const unsigned stat_grid = (unsigned)((long)B * (N + 1) * p.stat_chunks);
+  if (!probs && !stats_done && B <= kFusedMaxB) {
+    // statistics and acceptance in one launch, with this launch's ticket set
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    static std::atomic<unsigned*> set_base[64];
+    static std::atomic<unsigned> next_set[64];
+    unsigned* base = set_base[dev].load(std::memory_order_relaxed);
+    if (!base) {  // (concurrent first calls store the same address)
+      void* sym = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&sym, HIP_SYMBOL(g_stat_tickets));
+      if (e != hipSuccess) return e;
+      base = static_cast<unsigned*>(sym);
+      set_base[dev].store(base, std::memory_order_relaxed);
+    }
+    unsigned* st = base + (size_t)(next_set[dev].fetch_add(1u, std::memory_order_relaxed) % kTicketSets) *
+                              kFusedMaxB * kTWordsPerReq;
+    hipLaunchKernelGGL(verify_stats_accept, dim3(stat_grid), dim3(256), 0, stream, target, draft, draft_log_z,
+                       draft_tokens, inv_map, verify_len, temperature, request_id, k0, k1, stats, rstat, jobs,
+                       tickets, accepted, out_tokens, accept_prob, st, N, V, Vd, p.stat_chunks, p.stat_chunk,
+                       p.sample_chunks);
+  } else {
+    if (!probs && !stats_done)
+      hipLaunchKernelGGL(verify_rowstats, dim3(stat_grid), dim3(256), 0, stream, target, verify_len, temperature,
+                         stats, B, N, V, p.stat_chunks, p.stat_chunk);
+    hipLaunchKernelGGL(verify_accept, dim3(B), dim3(256), 0, stream, input_kind, target, draft, draft_log_z,
+                       draft_tokens, inv_map, verify_len, temperature, request_id, k0, k1, stats, rstat, jobs,
+                       tickets, accepted, out_tokens, accept_prob, N, V, Vd, p.stat_chunks, p.sample_chunks);
   }
-  hipLaunchKernelGGL(verify_accept, dim3(B), dim3(256), 0, stream, input_kind, target, draft, draft_log_z,
-                     draft_tokens, inv_map, verify_len, temperature, request_id, k0, k1, stats, rstat, jobs, tickets,
-                     accepted, out_tokens, accept_prob, B, N, V, Vd, p.stat_chunks, p.sample_chunks);
   const int R = accept_prob ? N + 1 : 1;
   hipLaunchKernelGGL(verify_sample, dim3((unsigned)((long)B * R * p.sample_chunks)), dim3(256), 0, stream,
                      input_kind, target, draft, draft_log_z, inv_map, temperature, request_id, k0, k1, jobs, rstat,

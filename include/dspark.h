@@ -36,7 +36,9 @@
  *              memory, zero when the library loads) for the few-request Markov
  *              kernel: each dspark_markov_sample call with B <= 16 takes the next
  *              set, and every launch leaves its set zero again, so 64 or more such
- *              launches must not be in flight at once.
+ *              launches must not be in flight at once.  The same holds, with 64
+ *              sets of 34 KB of tickets, for dspark_verify with logits input and
+ *              B <= 16 (statistics and acceptance in one launch).
  *   Sampling   All randomness is Philox4x32-10 (Salmon et al., SC'11) with
  *                key = (seed & 0xffffffff, seed >> 32),
  *                counter = (index >> 2, position, request_id, tag), word index & 3,

@@ -303,7 +303,10 @@ def test_verify_probs_bit_exact(B, N, V, Vd, reduced):
                                                     # more than 24 target rows: several passes of the
                                                     # acceptance kernel's statistics merge
                                                     (6, 40, 1024, 1024, (0.7, 1.0), False),
-                                                    (4, 64, 512, 512, (0.0, 1.0), False)])
+                                                    (4, 64, 512, 512, (0.0, 1.0), False),
+                                                    # more than 256 requests: statistics and acceptance
+                                                    # in separate launches
+                                                    (300, 2, 256, 256, (0.0, 1.0), False)])
 def test_verify_logits_parity(B, N, V, Vd, temps, reduced):
     say(f"verify logits B={B} N={N} V={V} Vd={Vd} T={temps}")
     c = _verify_inputs(B, N, V, Vd, temps, seed=B * N + 1, reduced=reduced)
