@@ -147,6 +147,10 @@ def test_markov_small(B, N, V, Vd, r, temps, reduced):
     (3, 4, 4096, 4096, 64, (0.0, 1.0), 1.0),     # margin too wide for the recorded entries: per-step pass
     (2, 6, 4096, 1000, 32, (1.0,), 1.0),         # the same with a reduced vocabulary
     (1, 20, 151936, 151936, 64, (1.0,), 0.02),   # recorded entries in several rounds; two 16-step tiles
+    # one request (every workgroup runs the candidate phase itself): the per-step pass
+    # from the first step, and greedy steps on rows staged in LDS
+    (1, 6, 4096, 4096, 64, (1.0,), 1.0),
+    (1, 5, 8192, 8192, 64, (0.0,), 0.02),
 ])
 def test_markov_candidate_paths(B, N, V, Vd, r, temps, wstd):
     say(f"markov candidate paths B={B} N={N} V={V} Vd={Vd} r={r} std={wstd}")
