@@ -56,6 +56,8 @@ def test_race_exponentials_bit_exact(n, pos, req, tag):
                                     (8, 4096, 4100), (16, 512, 1000), (13, 1024, 72), (1, 2048, 65540),
                                     (8, 4096, 8), (257, 128, 1000), (520, 96, 300), (96, 32, 260), (300, 64, 500),
                                     (700, 4096, 2000),
+                                    # H = 4096, a few 16-row blocks per workgroup and a partial last one
+                                    (8, 4096, 20000), (3, 4096, 20004), (16, 4096, 12300),
                                     # the stream kernel's LDS output buffer exactly full (96 KB per
                                     # workgroup at 256 CUs), and one size past it (the skinny kernel)
                                     (16, 512, 393216), (16, 512, 400000)])
