@@ -75,6 +75,26 @@ def _target_ids(Vd: int, d2t: Optional[np.ndarray]) -> np.ndarray:
     return j if d2t is None else j + np.asarray(d2t, dtype=np.int64)
 
 
+def key_top2_gap(key) -> float:
+    """Distance of the winning Gumbel-max key from the runner-up, in key units
+    (natural-log units for keys l/T + G).  0 when the largest key is shared by
+    several entries, +inf when there is only one entry (no other can win).
+
+    This is what decides whether a disagreement between two implementations of the
+    same sampler is a rounding-order near-tie.
+    Pins: hand-worked keys (unique maximum, exact tie, single entry, -inf entries);
+    markov_sample's greedy gap on a hand-worked row; the Gumbel gap of a row with one
+    dominant logit lies in that logit's margin / T plus or minus the Gumbel range.
+    """
+    k = np.asarray(key, dtype=np.float64).ravel()
+    if k.size < 2:
+        return math.inf
+    best = k.max()
+    if np.count_nonzero(k == best) > 1:
+        return 0.0
+    return float(best - k[k < best].max())
+
+
 def build_inverse_map(d2t: Optional[np.ndarray], Vd: int, V: int) -> np.ndarray:
     """inv[v] = j if v = j + d2t[j], else -1 [P3 §3.2: target id = draft id + d2t].
 
@@ -112,7 +132,8 @@ def draft_logits(hidden_bits, lm_head_bits, chunk: int = 16384) -> np.ndarray:
 # ---------------------------------------------------------------- stage 2
 
 def markov_sample(base, w1_bits, w2_bits, d2t, anchor, temperature, request_id,
-                  seed: int, requests: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+                  seed: int, requests: Optional[Sequence[int]] = None,
+                  teacher: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Sequential low-rank Markov sampling [P1 §2.2, §3; P2 §4].
 
     base:        [B, N, Vd] fp32 base logits (rows of ``requests`` if given)
@@ -121,14 +142,21 @@ def markov_sample(base, w1_bits, w2_bits, d2t, anchor, temperature, request_id,
     d2t:         [Vd] int64 offsets or None (draft vocabulary == target vocabulary)
     anchor, temperature, request_id: per request [B]
     requests:    which requests' rows ``base`` holds (default: all, in order)
+    teacher:     optional [.., N] target ids of another run of the same sampler.
+                 Teacher forcing: step i then takes prev = teacher[.., i-1] (the
+                 anchor at i = 0) instead of its own previous draw, so every step
+                 can be compared with that run's step even after the two have drawn
+                 different tokens; the output adds ``teacher_deficit``.
 
     Step i of request b:  e = W1[prev];  bias_j = sum_k W2[j,k] e_k;
     l_j = base[b,i,j] + bias_j;  key_j = l_j / T + G_j (T > 0) or l_j (T = 0);
     x = t(argmax key), ties to the smaller t(j);  prev = x.
 
     Returns processed [.., N, Vd] fp32 (= base + bias), tokens [.., N] int32
-    (target ids), logZ [.., N] fp32, gap [.., N] fp64 (best minus second-best
-    key, in the key's natural-log units).
+    (target ids), logZ [.., N] fp32, gap [.., N] fp64 (key_top2_gap of the step's
+    keys, natural-log units); with a teacher also teacher_deficit [.., N] fp64: the
+    best key minus the key of the teacher's token at that step (0 when the teacher
+    drew the same token; +inf when its token is outside the draft vocabulary).
     Pins: equals an explicit V x Vd bigram table lookup on tiny V; W1 = 0 gives
     independent per-position sampling; the anchor only changes step 0's bias;
     chi-square of samples against softmax(l/T); T = 0 gives the argmax.
@@ -144,6 +172,10 @@ def markov_sample(base, w1_bits, w2_bits, d2t, anchor, temperature, request_id,
     tokens = np.empty((nb, N), dtype=np.int32)
     logZ = np.empty((nb, N), dtype=np.float32)
     gap = np.empty((nb, N), dtype=np.float64)
+    deficit = np.full((nb, N), np.nan)
+    if teacher is not None:
+        teacher = np.asarray(teacher, dtype=np.int64)
+        j_of_t = {int(t): j for j, t in enumerate(t_of_j)}
     for n, b in enumerate(reqs):
         prev = int(anchor[b])
         T = float(np.float32(temperature[b]))
@@ -164,11 +196,18 @@ def markov_sample(base, w1_bits, w2_bits, d2t, anchor, temperature, request_id,
                 logZ[n, i] = np.float32(l.max())
             best = key.max()
             x = int(t_of_j[key == best].min())
-            below = key[key < best]
-            gap[n, i] = (best - below.max()) if (np.count_nonzero(key == best) == 1 and below.size) else 0.0
+            gap[n, i] = key_top2_gap(key)
             tokens[n, i] = x
-            prev = x
-    return {"processed": processed, "tokens": tokens, "logZ": logZ, "gap": gap}
+            if teacher is None:
+                prev = x
+            else:
+                jt = j_of_t.get(int(teacher[n, i]))
+                deficit[n, i] = math.inf if jt is None else float(best - key[jt])
+                prev = int(teacher[n, i])
+    out = {"processed": processed, "tokens": tokens, "logZ": logZ, "gap": gap}
+    if teacher is not None:
+        out["teacher_deficit"] = deficit
+    return out
 
 
 # ---------------------------------------------------------------- stage 3

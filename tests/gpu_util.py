@@ -37,18 +37,27 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def compare_markov(gpu_tok, gpu_proc, gpu_logz, ref, gap_tol=1e-2, proc_rtol=1e-5, logz_rtol=2e-5):
-    """Compare stage-2 outputs request by request, position by position.
+# every Markov comparison of the session: (label, positions compared, near-tie mismatches);
+# written out at the end of the session (tests/conftest.py) as the residual mismatch rate
+MARKOV_RECORD = []
 
-    Positions are compared up to the first token mismatch.  A mismatch must sit
-    where the oracle's Gumbel top-2 gap is <= gap_tol; after it the two chains
-    have different prefixes and are not comparable.  Returns (checked, near_ties).
+
+def compare_markov(gpu_tok, gpu_proc, gpu_logz, ref, gap_tol=1e-2, proc_rtol=1e-5, logz_rtol=2e-5, label=""):
+    """Compare stage-2 outputs position by position, teacher-forced.
+
+    ``ref`` must be the oracle run with teacher=gpu_tok: its step i then starts from
+    the GPU's token i-1, so every position stays comparable after a disagreement.
+    Processed logits and log Z must match at every position.  A token may differ only
+    at a near-tie of the oracle's keys: the oracle's top-2 gap is <= gap_tol AND the
+    GPU's token has an oracle key within gap_tol of the best one (it was one of the
+    near-tied candidates).  Such mismatches are counted; at most max(1, checked // 50)
+    are allowed.  Returns (checked, near_ties).
     """
+    assert "teacher_deficit" in ref, "compare_markov needs the oracle run teacher-forced on the GPU tokens"
     checked, near = 0, 0
     B, N = ref["tokens"].shape
     for b in range(B):
         for i in range(N):
-            # processed logits and log Z at position i depend on the prefix before i only
             p_ref = ref["processed"][b, i].astype(np.float64)
             p_gpu = gpu_proc[b, i].astype(np.float64)
             err = np.abs(p_gpu - p_ref) / np.maximum(1.0, np.abs(p_ref))
@@ -57,11 +66,13 @@ def compare_markov(gpu_tok, gpu_proc, gpu_logz, ref, gap_tol=1e-2, proc_rtol=1e-
             assert abs(lz_g - lz_r) <= logz_rtol * max(1.0, abs(lz_r)), f"log Z b={b} i={i}: {lz_g} vs {lz_r}"
             checked += 1
             if gpu_tok[b, i] != ref["tokens"][b, i]:
-                assert ref["gap"][b, i] <= gap_tol, (
+                gap, deficit = ref["gap"][b, i], ref["teacher_deficit"][b, i]
+                assert gap <= gap_tol and deficit <= gap_tol, (
                     f"token mismatch b={b} i={i}: gpu {gpu_tok[b, i]} oracle {ref['tokens'][b, i]} "
-                    f"at gap {ref['gap'][b, i]:.4g}")
+                    f"(oracle top-2 gap {gap:.4g}, gpu token {deficit:.4g} below the best key)")
                 near += 1
-                break
+    assert near <= max(1, checked // 50), f"{near} near-tie mismatches in {checked} positions"
+    MARKOV_RECORD.append((label, checked, near))
     return checked, near
 
 

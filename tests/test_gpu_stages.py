@@ -135,8 +135,9 @@ def test_markov_small(B, N, V, Vd, r, temps, reduced):
         d2t = (g.permutation(V)[:Vd] - np.arange(Vd)).astype(np.int64)
     c = _markov_case(B, N, V, Vd, r, temps, seed=0x1234, d2t=d2t)
     tok, proc, logz = _run_markov_gpu(c)
-    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], d2t, c["anchor"], c["temp"], c["rid"], c["seed"])
-    checked, near = compare_markov(tok, proc, logz, ref)
+    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], d2t, c["anchor"], c["temp"], c["rid"], c["seed"],
+                               teacher=tok)
+    checked, near = compare_markov(tok, proc, logz, ref, label=f"small B={B} N={N} Vd={Vd} r={r} T={temps}")
     say(f"  compared {checked} positions, {near} near-tie mismatches")
     if d2t is not None:
         image = set((np.arange(Vd) + d2t).tolist())
@@ -162,8 +163,9 @@ def test_markov_candidate_paths(B, N, V, Vd, r, temps, wstd):
         d2t = (g.permutation(V)[:Vd] - np.arange(Vd)).astype(np.int64)
     c = _markov_case(B, N, V, Vd, r, temps, seed=0x777, d2t=d2t, wstd=wstd)
     tok, proc, logz = _run_markov_gpu(c)
-    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], d2t, c["anchor"], c["temp"], c["rid"], c["seed"])
-    checked, near = compare_markov(tok, proc, logz, ref)
+    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], d2t, c["anchor"], c["temp"], c["rid"], c["seed"],
+                               teacher=tok)
+    checked, near = compare_markov(tok, proc, logz, ref, label=f"candidate paths B={B} N={N} Vd={Vd} std={wstd}")
     say(f"  compared {checked} positions, {near} near-tie mismatches")
 
 
@@ -180,8 +182,9 @@ def test_markov_unstaged_chain():
     say(f"markov unstaged chain B={B} N={N} V={V} r={r}")
     c = _markov_case(B, N, V, Vd, r, (1.0,), seed=0x99, base=base, wstd=0.33)
     tok, proc, logz = _run_markov_gpu(c)
-    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], None, c["anchor"], c["temp"], c["rid"], c["seed"])
-    checked, near = compare_markov(tok, proc, logz, ref)
+    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], None, c["anchor"], c["temp"], c["rid"], c["seed"],
+                               teacher=tok)
+    checked, near = compare_markov(tok, proc, logz, ref, label="unstaged chain")
     say(f"  compared {checked} positions, {near} near-tie mismatches")
     assert set(tok.ravel().tolist()) <= set(pick.tolist())
 
@@ -197,8 +200,9 @@ def test_markov_few_solo(B, N, V, Vd, r, temps, wstd, monkeypatch):
     say(f"markov few solo B={B} N={N} V={V} r={r} std={wstd}")
     c = _markov_case(B, N, V, Vd, r, temps, seed=0x51, wstd=wstd)
     tok, proc, logz = _run_markov_gpu(c)
-    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], None, c["anchor"], c["temp"], c["rid"], c["seed"])
-    checked, near = compare_markov(tok, proc, logz, ref)
+    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], None, c["anchor"], c["temp"], c["rid"], c["seed"],
+                               teacher=tok)
+    checked, near = compare_markov(tok, proc, logz, ref, label=f"few solo B={B} std={wstd}")
     say(f"  compared {checked} positions, {near} near-tie mismatches")
 
 
@@ -251,8 +255,8 @@ def test_markov_full_size_sampled(name, nsample):
     tok, logz = host(tok)[reqs], host(logz)[reqs]
     proc = host(base[torch.as_tensor(reqs).cuda()])
     ref = stages.markov_sample(sb, w1, w2, d2t, rp["anchor"], rp["temperature"], rp["request_id"],
-                               w.philox_seed, requests=reqs)
-    checked, near = compare_markov(tok, proc, logz, ref)
+                               w.philox_seed, requests=reqs, teacher=tok)
+    checked, near = compare_markov(tok, proc, logz, ref, label=f"full size {name} requests {reqs.tolist()}")
     say(f"  requests {reqs.tolist()}: compared {checked} positions, {near} near-tie mismatches")
 
 

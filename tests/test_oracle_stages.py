@@ -547,3 +547,98 @@ def test_confidence_logit_is_affine_in_hidden():
         return math.log(p[0, 0] / (1 - p[0, 0]))
     zero = logit(np.zeros((1, 16), np.float32))
     assert abs((logit(h1 + h2) - zero) - ((logit(h1) - zero) + (logit(h2) - zero))) < 1e-4
+
+
+# ---------------------------------------------------------------- near-tie helpers and teacher forcing
+# The GPU parity tests forgive a token disagreement only at a near-tie, measured by these
+# helpers, so they are pinned to hand-worked values here.
+
+def test_key_top2_gap_hand_worked():
+    assert stages.key_top2_gap([0.5, 2.0, 1.25, -1.0]) == 0.75          # unique maximum
+    assert stages.key_top2_gap([3.0, 1.0, 3.0]) == 0.0                  # exact tie at the top
+    assert stages.key_top2_gap([1.0, 3.0, 1.0]) == 2.0                  # tie below the top is irrelevant
+    assert stages.key_top2_gap([7.0]) == math.inf                       # one entry: nothing else can win
+    assert stages.key_top2_gap([-np.inf, 4.0, -np.inf]) == math.inf     # the runner-up is impossible
+    assert stages.key_top2_gap([2.0, -np.inf, 1.5]) == 0.5
+
+
+def test_race_top2_margin_hand_worked():
+    # r / E = [1, 2, 3]: best 3, runner-up 2, relative gap 1/3
+    assert variates.race_top2_margin([1.0, 2.0, 3.0], [1.0, 1.0, 1.0]) == pytest.approx(1.0 / 3.0, rel=1e-15)
+    # r / E = [2/4, 3/2, 1/1] = [0.5, 1.5, 1]: relative gap (1.5 - 1) / 1.5
+    assert variates.race_top2_margin([2.0, 3.0, 1.0], [4.0, 2.0, 1.0]) == pytest.approx(1.0 / 3.0, rel=1e-15)
+    # relative units: scaling every weight leaves it unchanged; an exact tie gives 0
+    assert variates.race_top2_margin([10.0, 20.0, 30.0], [1.0, 1.0, 1.0]) == pytest.approx(1.0 / 3.0, rel=1e-15)
+    assert variates.race_top2_margin([1.0, 2.0, 2.0], [1.0, 2.0, 2.0]) == 0.0
+    assert variates.race_top2_margin([0.25], [1.0]) == math.inf          # single candidate
+    assert variates.race_top2_margin([0.0, 0.0], [1.0, 2.0]) == math.inf  # nothing can win
+
+
+def test_markov_gap_greedy_hand_worked():
+    # W1 = 0: no bias, so at T = 0 the key is the base logit itself
+    V, r = 4, 8
+    base = np.array([[[0.5, 2.0, 1.25, -1.0], [3.0, 3.0, 0.0, 1.0]]], np.float32)
+    w1 = np.zeros((V, r), np.uint16)
+    w2 = synth.bf16_bits(np.random.default_rng(0).normal(size=(V, r)).astype(np.float32))
+    out = stages.markov_sample(base, w1, w2, None, [1], [0.0], [0], seed=0)
+    assert out["tokens"].tolist() == [[1, 0]]        # the tie at step 1 goes to the smaller id
+    assert out["gap"][0, 0] == 0.75 and out["gap"][0, 1] == 0.0
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0, 2.0])
+def test_markov_gap_units_with_gumbel_noise(T):
+    # one logit 1000 above the rest: the gap is 1000 / T plus the difference of two
+    # Gumbel draws, each within [-ln(-ln 2^-24), -ln(-ln(1 - 2^-24))] = [-2.81, 16.64]
+    # (the uniform map never returns 0 or 1).  A gap in base-2 units or untempered would fall outside.
+    V, r, N = 64, 8, 3
+    g = np.random.default_rng(int(T * 10))
+    base = g.normal(0, 1, size=(1, N, V)).astype(np.float32)
+    base[0, :, 5] += 1000.0
+    w1 = np.zeros((V, r), np.uint16)
+    w2 = synth.bf16_bits(g.normal(size=(V, r)).astype(np.float32))
+    out = stages.markov_sample(base, w1, w2, None, [0], [T], [3], seed=11)
+    gmax, gmin = -math.log(-math.log(1 - 2.0 ** -24)), -math.log(-math.log(2.0 ** -24))
+    for i in range(N):
+        second = np.sort(base[0, i].astype(np.float64))[-2]
+        margin = (base[0, i, 5] - second) / T
+        assert out["tokens"][0, i] == 5
+        assert margin - (gmax - gmin) <= out["gap"][0, i] <= margin + (gmax - gmin)
+
+
+def test_markov_teacher_forcing():
+    c = _small(V=12, r=4, N=5, B=2, std=0.8, seed=3)
+    T = np.array([1.0, 0.7], np.float32)
+    rid = np.array([4, 9], np.uint32)
+    free = stages.markov_sample(c["base"], c["w1"], c["w2"], None, c["anchor"], T, rid, seed=5)
+    # the sampler's own tokens as the teacher: identical outputs, zero deficit
+    own = stages.markov_sample(c["base"], c["w1"], c["w2"], None, c["anchor"], T, rid, seed=5,
+                               teacher=free["tokens"])
+    for k in ("processed", "tokens", "logZ", "gap"):
+        assert np.array_equal(own[k], free[k])
+    assert (own["teacher_deficit"] == 0).all()
+    # another chain: step i's bias is the explicit bigram row of the teacher's token i-1
+    other = (free["tokens"] + 5) % 12
+    tf = stages.markov_sample(c["base"], c["w1"], c["w2"], None, c["anchor"], T, rid, seed=5, teacher=other)
+    table = stages.bf16_decode(c["w1"]) @ stages.bf16_decode(c["w2"]).T      # [V, Vd] bigram table
+    for b in range(2):
+        for i in range(5):
+            prev = c["anchor"][b] if i == 0 else other[b, i - 1]
+            want = (c["base"][b, i].astype(np.float64) + table[prev]).astype(np.float32)
+            assert np.allclose(tf["processed"][b, i], want, rtol=0, atol=1e-6)
+            d = tf["teacher_deficit"][b, i]
+            assert d >= 0 and ((d == 0) == (tf["tokens"][b, i] == other[b, i]) or tf["gap"][b, i] == 0)
+    assert np.array_equal(tf["processed"][:, 0], free["processed"][:, 0])     # step 0 starts at the anchor
+
+
+def test_probs_from_logits_closed_forms():
+    # two logits T*ln(3) apart: p = (1/4, 3/4) at every temperature (a dropped or inverted
+    # temperature would give 1/(1 + 3^T) or 1/(1 + 3^(1/T^2)))
+    for T in (0.5, 0.7, 1.0, 2.0):
+        p = stages.probs_from_logits(np.array([0.0, T * math.log(3.0)], np.float32), T)
+        assert p.dtype == np.float32 and np.allclose(p, [0.25, 0.75], rtol=1e-6)
+    # shift invariance and the uniform row
+    assert np.allclose(stages.probs_from_logits(np.full(8, 123.0, np.float32), 0.9), 1.0 / 8)
+    # T = 0: the point mass on the first maximum
+    assert stages.probs_from_logits(np.array([1.0, 5.0, 5.0, 2.0], np.float32), 0.0).tolist() == [0, 1, 0, 0]
+    # the draft distribution at T = 0 is the point mass on the drafted entry, whatever the logits
+    assert stages.draft_probs(np.array([9.0, 1.0, 0.0], np.float32), 0.0, 2).tolist() == [0, 0, 1]
