@@ -6,11 +6,14 @@ One step = one round of the whole hot path over one batch of synthetic input:
 HBM before the timed region; the target logits are the step's own base logits
 plus seeded noise, made once before timing.
 
-Metric: draft+verify positions per second (B * N per step), plus the roofline
-of the dominant kernel (the draft-logit GEMM: HBM-bound when the batch is a few
-positions, MFMA-bound for large batches) measured with HIP events on the stream
-the kernels run on, and the CPU oracle timed on a bounded sample of the same
-workload.
+Metric: draft+verify positions per second (B * N per step).  The default
+workload is the largest single-GPU one at V = 151936: B = 256 requests, N = 16
+draft positions, rank 256, K = 1024 admitted.  Beside it: the roofline of the
+dominant kernel (the draft-logit GEMM, MFMA-bound at that size) and the HBM
+fractions of the Markov loop and of verify, each from HIP events recorded on the
+stream the kernels run on inside the timed steps; the same stages timed cold
+(a 1 GiB read-write scrub before each stage evicts the 256 MB last-level cache);
+and the CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--graph]
 """
@@ -38,13 +41,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="qwen3_8b_single",
+    p.add_argument("--workload", default="admission",
                    help="tiny | qwen3_8b_single | batched | admission | reduced_vocab")
     p.add_argument("--graph", action="store_true", help="replay each step as one captured HIP graph")
-    p.add_argument("--overlap", action="store_true",
-                   help="run the verify statistics and the admission on a second stream beside stages 1-2. "
-                        "Not the default: it assumes the target logits exist before the draft does, "
-                        "which a draft-then-verify loop does not have (the target scores the draft)")
     p.add_argument("--verify", default="rejection", choices=("rejection", "coupled"),
                    help="stage 3 rule: rejection sampling on p_t, p_d (default) or Gumbel-coupled verification")
     p.add_argument("--round", default="path", choices=("path", "full"),
@@ -52,6 +51,7 @@ def parse():
                         "full: also the confidence head (its output feeds admission) and the throughput-optimal "
                         "K, computed from this round's survival and used two rounds later")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cold", action="store_true", help="skip the cold-cache stage timings")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB five times (reference for the "
@@ -66,13 +66,10 @@ def src_hash(path: str) -> str:
 class Path:
     """Device buffers and the four C-ABI calls of one round."""
 
-    def __init__(self, w, torch, dsl, synth, verify_mode="rejection", full_round=False, overlap=False):
+    def __init__(self, w, torch, dsl, synth, verify_mode="rejection", full_round=False):
         self.w, self.torch, self.dsl = w, torch, dsl
         self.coupled = verify_mode == "coupled"
         self.full = full_round
-        # overlap: the target-row statistics and the admission (which need neither stage 1
-        # nor stage 2 when the confidence is an input) run on a second stream beside them
-        self.overlap = overlap and not self.coupled and not full_round
         dev = torch.device("cuda:0")
         rp = synth.request_params(w)
 
@@ -141,11 +138,6 @@ class Path:
             self.K_used = []
         torch.cuda.synchronize()
         self.setup_s = time.time() - t0
-        self.ev = None
-        if self.overlap:
-            self.side = torch.cuda.Stream()               # (default priority)
-            self.ev_side, self.ev_main = torch.cuda.Event(), torch.cuda.Event()
-            self.ev_main.record()
 
     def budget(self):
         """K for this round: fixed, or (full round) the K chosen two rounds ago."""
@@ -155,67 +147,75 @@ class Path:
         self.k_ready[slot].synchronize()        # long done: the GPU is at most a round behind
         return int(self.k_host[slot])
 
-    def step(self, events=None):
-        """One round.  events: optional list of 5 (7 for a full round) torch.cuda.Event
-        bracketing the stages."""
+    def step(self, timer=None, scrub=None):
+        """One round.  timer: optional StageTimer that brackets each stage with HIP
+        events on the launch stream.  scrub: optional callable run before each stage,
+        outside its events (cold-cache timing)."""
         w, dsl = self.w, self.dsl
-        if self.overlap and not events:
-            self.step_overlapped()
-            return
-        rec = (lambda i: events[i].record()) if events else (lambda i: None)
-        rec(0)
-        dsl.draft_logits(self.hidden, self.lm_head, out=self.logits.view(w.M, w.Vd))
-        rec(1)
-        dsl.markov_sample(self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, self.seed,
-                          draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov)
-        rec(2)
+
+        def stage(name, fn):
+            if scrub is not None:
+                scrub()
+            if timer is not None:
+                timer.begin(name)
+            fn()
+            if timer is not None:
+                timer.end(name)
+
+        stage("draft_logits", lambda: dsl.draft_logits(self.hidden, self.lm_head, out=self.logits.view(w.M, w.Vd)))
+        stage("markov_sample", lambda: dsl.markov_sample(
+            self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, self.seed,
+            draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov))
         conf = self.conf
         if self.full:
-            dsl.confidence(self.hidden, self.w1, self.tokens, self.anchor, self.wconf, self.cbias, self.tau,
-                           c_out=self.c_model)
+            stage("confidence", lambda: dsl.confidence(self.hidden, self.w1, self.tokens, self.anchor, self.wconf,
+                                                       self.cbias, self.tau, c_out=self.c_model))
             conf = self.c_model
-            rec(5)
         K = self.budget()
         if self.full:
             self.K_used.append(K)
-        dsl.admit(conf, K, survival=self.survival, admit_len=self.admit_len)
-        rec(3)
+        stage("admit", lambda: dsl.admit(conf, K, survival=self.survival, admit_len=self.admit_len))
         if self.coupled:
-            dsl.verify_coupled(self.target, self.tokens, self.inv, self.admit_len, self.temp, self.rid, self.seed,
-                               Vd=w.Vd, accepted=self.accepted, out_tokens=self.out_tokens,
-                               workspace=self.ws_verify)
+            stage("verify", lambda: dsl.verify_coupled(
+                self.target, self.tokens, self.inv, self.admit_len, self.temp, self.rid, self.seed, Vd=w.Vd,
+                accepted=self.accepted, out_tokens=self.out_tokens, workspace=self.ws_verify))
         else:
-            dsl.verify(dsl.INPUT_LOGITS, self.target, self.logits, self.logz, self.tokens, self.inv,
-                       self.admit_len, self.temp, self.rid, self.seed, accepted=self.accepted,
-                       out_tokens=self.out_tokens, workspace=self.ws_verify)
-        rec(4)
+            stage("verify", lambda: dsl.verify(
+                dsl.INPUT_LOGITS, self.target, self.logits, self.logz, self.tokens, self.inv, self.admit_len,
+                self.temp, self.rid, self.seed, accepted=self.accepted, out_tokens=self.out_tokens,
+                workspace=self.ws_verify))
         if self.full:
-            # the budget of two rounds ahead, from this round's survival
-            dsl.choose_k(self.survival, self.sps, k_out=self.k_dev, objective_out=self.k_obj)
-            slot = self.round % 3
-            self.k_host[slot:slot + 1].copy_(self.k_dev, non_blocking=True)
-            self.k_ready[slot].record()
+            def budget_ahead():
+                # the budget of two rounds ahead, from this round's survival
+                dsl.choose_k(self.survival, self.sps, k_out=self.k_dev, objective_out=self.k_obj)
+                slot = self.round % 3
+                self.k_host[slot:slot + 1].copy_(self.k_dev, non_blocking=True)
+                self.k_ready[slot].record()
+            stage("choose_k", budget_ahead)
             self.round += 1
-            rec(6)
 
 
-    def step_overlapped(self):
-        """One round with the statistics pass and the admission on the side stream."""
-        w, dsl, torch = self.w, self.dsl, self.torch
-        main = torch.cuda.current_stream()
-        self.side.wait_event(self.ev_main)   # the previous round's verify has read both outputs
-        with torch.cuda.stream(self.side):
-            dsl.verify_stats(self.target, self.temp, self.ws_verify, w.N)
-            dsl.admit(self.conf, self.budget(), survival=self.survival, admit_len=self.admit_len)
-            self.ev_side.record(self.side)
-        dsl.draft_logits(self.hidden, self.lm_head, out=self.logits.view(w.M, w.Vd))
-        dsl.markov_sample(self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, self.seed,
-                          draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov)
-        main.wait_event(self.ev_side)
-        dsl.verify(dsl.INPUT_LOGITS, self.target, self.logits, self.logz, self.tokens, self.inv,
-                   self.admit_len, self.temp, self.rid, self.seed, accepted=self.accepted,
-                   out_tokens=self.out_tokens, workspace=self.ws_verify, stats_done=True)
-        self.ev_main.record(main)
+class StageTimer:
+    """HIP event pairs around each stage, recorded on torch's current stream (the
+    stream the binding launches on); durations are read after a synchronisation."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+        self.open = {}
+
+    def begin(self, name):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.open[name] = e
+
+    def end(self, name):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.setdefault(name, []).append((self.open.pop(name), e))
+
+    def mean_ms(self):
+        return {k: float(np.mean([b.elapsed_time(e) for b, e in v])) for k, v in self.pairs.items()}
 
 
 def stage_bytes(w, admit_len, coupled):
@@ -254,24 +254,37 @@ def k1_roofline(w, k1_ms):
     else:
         roof["kernel"] = ("draft_logits (k1_skinny)" if w.M <= 64 else
                           "draft_logits (k1_big)" if w.H % 64 == 0 else "draft_logits (k1_tiled)")
-    roof["traffic"] = measured_traffic(w)
+    roof["traffic"] = measured_traffic("draft_logits", w)
     return roof
 
 
-def measured_traffic(w):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else null."""
-    path = os.path.join(PROFILES, f"draft_logits_{w.name}_traffic.json")
+def measured_traffic(stage, w):
+    """HBM bytes (FETCH + WRITE, calibrated) per call of a stage from the committed
+    rocprofv3 counter summary profiles/<stage>_<workload>_traffic.json, if it was
+    taken on the current source of the kernel file it names; else null."""
+    path = os.path.join(PROFILES, f"{stage}_{w.name}_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         d = json.load(open(path))
-        if d.get("source_sha256_16") != src_hash(os.path.join(ROOT, "draft_sampling_lossless_amd", "csrc",
-                                                              "gemm.hip")):
+        src = os.path.join(ROOT, d["source_file"])
+        if d.get("source_sha256_16") != src_hash(src):
             return None
-        return d.get("bytes_per_launch")
+        return d.get("bytes_per_call")
     except Exception:
         return None
+
+
+def hbm_roofline(name, bytes_, ms, w, cold_ms=None):
+    ach = bytes_ / (ms * 1e-3) / 1e9
+    out = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(bytes_),
+           "traffic": measured_traffic(name.split(" ")[0], w)}
+    if cold_ms:
+        cold = bytes_ / (cold_ms * 1e-3) / 1e9
+        out["achieved_cold"] = round(cold, 1)
+        out["frac_cold"] = round(cold / HBM_PEAK_GBS, 4)
+    return out
 
 
 def cpu_baseline(w, budget_s):
@@ -349,9 +362,22 @@ def main():
                                    "replayed as one captured graph"}))
         sys.exit(2)
     w = synth.get(args.workload)
-    overlap = args.overlap and not args.graph
-    path = Path(w, torch, dsl, synth, args.verify, args.round == "full", overlap=overlap)
+    path = Path(w, torch, dsl, synth, args.verify, args.round == "full")
+    result = run(args, w, path, torch)
+    # release the graph and every device buffer, synchronised, before the interpreter
+    # (and any profiler attached to it) tears the HIP runtime down
+    torch.cuda.synchronize()
+    del path
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
 
+
+def run(args, w, path, torch):
     graph = None
     if args.graph:
         for _ in range(2):
@@ -362,51 +388,55 @@ def main():
             path.step()
         torch.cuda.synchronize()
 
-    def run_step(events=None):
-        if graph is not None:
-            if events:
-                events[0].record()
-            graph.replay()
-            if events:
-                for e in events[1:]:
-                    e.record()
-        else:
-            path.step(events)
-
     for _ in range(args.warmup):
-        run_step()
+        if graph is not None:
+            graph.replay()
+        else:
+            path.step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, no per-stage events (they would add work)
+    # timed region: K steps; eager steps carry HIP event pairs around every stage
+    timer = StageTimer(torch) if graph is None else None
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        run_step()
+        if graph is not None:
+            graph.replay()
+        else:
+            path.step(timer)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    if timer is None:       # graph replay: stage times from eager rounds after the timed region
+        timer = StageTimer(torch)
+        for _ in range(max(5, min(args.steps, 50))):
+            path.step(timer)
+        torch.cuda.synchronize()
+    stage_ms = timer.mean_ms()
 
-    # per-stage durations with HIP events on the launch stream (eager steps)
-    stage_ms = np.zeros(4)
-    extra_ms = np.zeros(2)
-    nrep = max(5, min(args.steps, 50))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(nrep)]
-    for e in evs:
-        path.step(e)
-    torch.cuda.synchronize()
-    for e in evs:
-        if path.full:   # order: 0 K1 1 K2 2 confidence 5 admit 3 verify 4 choose_k 6
-            stage_ms += [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[5].elapsed_time(e[3]),
-                         e[3].elapsed_time(e[4])]
-            extra_ms += [e[2].elapsed_time(e[5]), e[4].elapsed_time(e[6])]
-        else:
-            stage_ms += [e[i].elapsed_time(e[i + 1]) for i in range(4)]
-    stage_ms /= nrep
-    extra_ms /= nrep
+    cold_ms = None
+    if not args.no_cold:
+        # a 1 GiB read-modify-write before each stage: 2 GiB of traffic evicts the 256 MB MALL
+        scrub_buf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+        cold = StageTimer(torch)
+        for _ in range(5):
+            path.step(cold, scrub=lambda: scrub_buf.add_(1.0))
+        torch.cuda.synchronize()
+        cold_ms = cold.mean_ms()
+        del scrub_buf
 
     positions = w.B * w.N
     value = positions / (ms_per_step * 1e-3)
     k2_bytes, k3_bytes = stage_bytes(w, path.admit_len.cpu().numpy(), path.coupled)
-    roof = k1_roofline(w, stage_ms[0])
+    roof = k1_roofline(w, stage_ms["draft_logits"])
+    if cold_ms:
+        _, flops = k1_work(w)
+        roof["frac_cold"] = round(flops / (cold_ms["draft_logits"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4) \
+            if roof["bound"] == "mfma" else round(k1_work(w)[0] / (cold_ms["draft_logits"] * 1e-3) / 1e9
+                                                  / HBM_PEAK_GBS, 4)
+    roof["stages"] = [
+        hbm_roofline("markov_sample", k2_bytes, stage_ms["markov_sample"], w, cold_ms and cold_ms["markov_sample"]),
+        hbm_roofline("verify", k3_bytes, stage_ms["verify"], w, cold_ms and cold_ms["verify"]),
+    ]
     result = {
         "metric": "draft+verify positions/sec (B*N) and achieved HBM GB/s at V=151936",
         "value": round(value, 1),
@@ -421,26 +451,21 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "V": w.V, "Vd": w.Vd, "r": w.r,
-                   "K": w.budget, "graph": bool(args.graph),
-                   "side_stream": "verify statistics + admission" if path.overlap else None},
-        "stage_ms": {"draft_logits": round(stage_ms[0], 4), "markov_sample": round(stage_ms[1], 4),
-                     "admit": round(stage_ms[2], 4), "verify": round(stage_ms[3], 4)},
-        "stage_hbm_gbs": {"markov_sample": round(k2_bytes / (stage_ms[1] * 1e-3) / 1e9, 1),
-                          "verify": round(k3_bytes / (stage_ms[3] * 1e-3) / 1e9, 1),
-                          "markov_bytes": k2_bytes, "verify_bytes": k3_bytes},
+                   "K": w.budget, "graph": graph is not None},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": roof,
     }
+    if cold_ms:
+        result["stage_ms_cold"] = {k: round(v, 4) for k, v in cold_ms.items()}
     if path.coupled:
         result["config"]["verify"] = "coupled"
     if path.full:
         result["config"]["round"] = "full"
-        result["stage_ms"]["confidence"] = round(extra_ms[0], 4)
-        result["stage_ms"]["choose_k"] = round(extra_ms[1], 4)
         result["budget_K"] = {"first": path.K_used[2] if len(path.K_used) > 2 else None,
                               "last": path.K_used[-1], "of": w.B * w.N}
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    if graph is not None:
+        del graph
+    return result
 
 
 if __name__ == "__main__":

@@ -49,9 +49,6 @@ _SIGS = {
     "dspark_verify_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
     "dspark_verify": (_c_int, [_c_int] + [_c_void_p] * 8 + [_c_u64, _c_void_p, _c_void_p, _c_void_p] + [_c_int] * 4
                       + [_c_void_p, _c_size, _c_void_p]),
-    "dspark_verify_stats": (_c_int, [_c_void_p, _c_void_p] + [_c_int] * 3 + [_c_void_p, _c_size, _c_void_p]),
-    "dspark_verify_finish": (_c_int, [_c_int] + [_c_void_p] * 8 + [_c_u64, _c_void_p, _c_void_p, _c_void_p]
-                             + [_c_int] * 4 + [_c_void_p, _c_size, _c_void_p]),
     "dspark_verify_coupled_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
     "dspark_verify_coupled": (_c_int, [_c_void_p] * 6 + [_c_u64, _c_void_p, _c_void_p] + [_c_int] * 4
                               + [_c_void_p, _c_size, _c_void_p]),
@@ -216,10 +213,9 @@ def verify(input_kind: int, target: torch.Tensor, draft: torch.Tensor, draft_log
            temperature: Optional[torch.Tensor], request_id: torch.Tensor, seed: int,
            accepted: Optional[torch.Tensor] = None, out_tokens: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, accept_prob: Optional[torch.Tensor] = None,
-           with_accept_prob: bool = False, stats_done: bool = False):
+           with_accept_prob: bool = False):
     """Stage 3.  target [B, N+1, V], draft [B, N, Vd].  Returns (accepted [B], out_tokens [B, N+1]),
-    plus accept_prob [B, N] (NaN past verify_len) when it is passed or with_accept_prob is set.
-    stats_done: the workspace holds verify_stats's output for this target (dspark_verify_finish)."""
+    plus accept_prob [B, N] (NaN past verify_len) when it is passed or with_accept_prob is set."""
     B, N, Vd = draft.shape
     V = target.shape[2]
     dev = target.device
@@ -230,10 +226,7 @@ def verify(input_kind: int, target: torch.Tensor, draft: torch.Tensor, draft_log
     if accept_prob is None and with_accept_prob:
         accept_prob = torch.empty((B, N), dtype=torch.float32, device=dev)
     ws = _workspace(workspace, verify_workspace_size(B, N, V), dev)
-    if stats_done and workspace is None:
-        raise ValueError("stats_done needs the workspace verify_stats filled")
-    name = "dspark_verify_finish" if stats_done else "dspark_verify"
-    _check(name, getattr(load(), name)(
+    _check("dspark_verify", load().dspark_verify(
         input_kind, _ptr(target, "target", _F32, dev, (B, N + 1, V)), _ptr(draft, "draft", _F32, dev),
         _ptr(draft_log_z, "draft_log_z", _F32, dev, (B, N)),
         _ptr(draft_tokens, "draft_tokens", _I32, dev, (B, N)), _ptr(inv_map, "inv_map", _I32, dev, (V,)),
@@ -245,16 +238,6 @@ def verify(input_kind: int, target: torch.Tensor, draft: torch.Tensor, draft_log
     if accept_prob is not None:
         return accepted, out_tokens, accept_prob
     return accepted, out_tokens
-
-
-def verify_stats(target: torch.Tensor, temperature: torch.Tensor, workspace: torch.Tensor, N: int) -> None:
-    """Statistics of every target row k <= N into workspace (then verify(..., stats_done=True))."""
-    B, V = target.shape[0], target.shape[2]
-    dev = target.device
-    ws = _workspace(workspace, verify_workspace_size(B, N, V), dev)
-    _check("dspark_verify_stats", load().dspark_verify_stats(
-        _ptr(target, "target", _F32, dev, (B, N + 1, V)), _ptr(temperature, "temperature", _F32, dev, (B,)),
-        B, N, V, ws.data_ptr(), ws.numel(), _stream(target)))
 
 
 def verify_coupled_workspace_size(B: int, N: int, V: int) -> int:

@@ -142,14 +142,14 @@ size_t dspark_verify_workspace_size(int B, int N, int V) {
   return dspark::plan_verify(B, N, V).total_bytes;
 }
 
+}  // extern "C"
+
 namespace {
-// dspark_verify and dspark_verify_finish: the same checks; stats_done skips the
-// statistics pass (the workspace holds dspark_verify_stats's output)
-dspark_status verify_checked(int input_kind, const float* target, const float* draft, const float* draft_log_z,
-                             const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
-                             const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
-                             int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
-                             size_t workspace_bytes, void* stream, bool stats_done) {
+// the argument checks of dspark_verify (everything but the workspace)
+dspark_status verify_args(int input_kind, const float* target, const float* draft, const float* draft_log_z,
+                          const int32_t* draft_tokens, const int32_t* inv_map, const float* temperature,
+                          const uint32_t* request_id, const int32_t* accepted, const int32_t* out_tokens, int B, int N,
+                          int V, int Vd) {
   REQUIRE(input_kind == DSPARK_INPUT_LOGITS || input_kind == DSPARK_INPUT_PROBS, DSPARK_ERR_INVALID,
           "input_kind must be DSPARK_INPUT_LOGITS or DSPARK_INPUT_PROBS (got %d)", input_kind);
   REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);
@@ -171,6 +171,20 @@ dspark_status verify_checked(int input_kind, const float* target, const float* d
     REQUIRE_PTR(temperature, "temperature (required for logits input)");
     REQUIRE_PTR(draft_log_z, "draft_log_z (required for logits input)");
   }
+  return ok();
+}
+}  // namespace
+
+extern "C" {
+
+dspark_status dspark_verify(int input_kind, const float* target, const float* draft, const float* draft_log_z,
+                            const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
+                            const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
+                            int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const dspark_status st = verify_args(input_kind, target, draft, draft_log_z, draft_tokens, inv_map, temperature,
+                                       request_id, accepted, out_tokens, B, N, V, Vd);
+  if (st != DSPARK_OK) return st;
   const size_t need = dspark_verify_workspace_size(B, N, V);
   REQUIRE(workspace != nullptr, DSPARK_ERR_WORKSPACE, "workspace must not be NULL (%zu bytes needed)", need);
   REQUIRE(aligned16(workspace), DSPARK_ERR_INVALID, "workspace must be 16-byte aligned");
@@ -178,48 +192,8 @@ dspark_status verify_checked(int input_kind, const float* target, const float* d
           need);
   return hip_status(dspark::launch_verify(input_kind, target, draft, draft_log_z, draft_tokens, inv_map, verify_len,
                                           temperature, request_id, seed, accepted, out_tokens, accept_prob, B, N,
-                                          V, Vd, workspace, (hipStream_t)stream, stats_done),
+                                          V, Vd, workspace, (hipStream_t)stream),
                     "verify");
-}
-}  // namespace
-
-dspark_status dspark_verify(int input_kind, const float* target, const float* draft, const float* draft_log_z,
-                            const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
-                            const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
-                            int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
-                            size_t workspace_bytes, void* stream) {
-  return verify_checked(input_kind, target, draft, draft_log_z, draft_tokens, inv_map, verify_len, temperature,
-                        request_id, seed, accepted, out_tokens, accept_prob, B, N, V, Vd, workspace, workspace_bytes,
-                        stream, false);
-}
-
-dspark_status dspark_verify_stats(const float* target, const float* temperature, int B, int N, int V,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
-  REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);
-  REQUIRE(B <= DSPARK_MAX_B, DSPARK_ERR_UNSUPPORTED, "B must be <= %d (got %d)", DSPARK_MAX_B, B);
-  REQUIRE(N >= 1, DSPARK_ERR_INVALID, "N must be >= 1 (got %d)", N);
-  REQUIRE(N <= DSPARK_MAX_N, DSPARK_ERR_UNSUPPORTED, "N must be <= %d (got %d)", DSPARK_MAX_N, N);
-  REQUIRE(V > 0 && V % 4 == 0, DSPARK_ERR_INVALID, "V must be a positive multiple of 4 (got %d)", V);
-  REQUIRE((int64_t)B * (N + 1) * V < ((int64_t)1 << 40), DSPARK_ERR_UNSUPPORTED, "B * (N+1) * V too large");
-  REQUIRE_PTR16(target, "target");
-  REQUIRE_PTR(temperature, "temperature");
-  const size_t need = dspark_verify_workspace_size(B, N, V);
-  REQUIRE(workspace != nullptr, DSPARK_ERR_WORKSPACE, "workspace must not be NULL (%zu bytes needed)", need);
-  REQUIRE(aligned16(workspace), DSPARK_ERR_INVALID, "workspace must be 16-byte aligned");
-  REQUIRE(workspace_bytes >= need, DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
-          need);
-  return hip_status(dspark::launch_verify_stats(target, temperature, B, N, V, workspace, (hipStream_t)stream),
-                    "verify_stats");
-}
-
-dspark_status dspark_verify_finish(int input_kind, const float* target, const float* draft, const float* draft_log_z,
-                                   const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
-                                   const float* temperature, const uint32_t* request_id, uint64_t seed,
-                                   int32_t* accepted, int32_t* out_tokens, float* accept_prob, int B, int N, int V,
-                                   int Vd, void* workspace, size_t workspace_bytes, void* stream) {
-  return verify_checked(input_kind, target, draft, draft_log_z, draft_tokens, inv_map, verify_len, temperature,
-                        request_id, seed, accepted, out_tokens, accept_prob, B, N, V, Vd, workspace, workspace_bytes,
-                        stream, true);
 }
 
 size_t dspark_verify_coupled_workspace_size(int B, int N, int V) {

@@ -65,10 +65,7 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
                          const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
                          const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
                          int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
-                         hipStream_t stream, bool stats_done = false);
-// the statistics pass alone, for every target row k <= N (the workspace of launch_verify)
-hipError_t launch_verify_stats(const float* target, const float* temperature, int B, int N, int V, void* workspace,
-                               hipStream_t stream);
+                         hipStream_t stream);
 
 // ---- Gumbel-coupled verification
 size_t coupled_workspace_bytes(int B, int N, int V);

@@ -709,7 +709,7 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
                          const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
                          const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
                          int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
-                         hipStream_t stream, bool stats_done) {
+                         hipStream_t stream) {
   const VerifyPlan p = plan_verify(B, N, V);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t rows = (size_t)B * (N + 1);
@@ -728,7 +728,7 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
   const uint32_t k0 = (uint32_t)(seed & 0xFFFFFFFFu), k1 = (uint32_t)(seed >> 32);
   const bool probs = input_kind == DSPARK_INPUT_PROBS;
   const unsigned stat_grid = (unsigned)((long)B * (N + 1) * p.stat_chunks);
-  if (!probs && !stats_done && B <= kFusedMaxB) {
+  if (!probs && B <= kFusedMaxB) {
     // statistics and acceptance in one launch, with this launch's ticket set
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
@@ -749,7 +749,7 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
                        tickets, accepted, out_tokens, accept_prob, st, N, V, Vd, p.stat_chunks, p.stat_chunk,
                        p.sample_chunks);
   } else {
-    if (!probs && !stats_done)
+    if (!probs)
       hipLaunchKernelGGL(verify_rowstats, dim3(stat_grid), dim3(256), 0, stream, target, verify_len, temperature,
                          stats, B, N, V, p.stat_chunks, p.stat_chunk);
     hipLaunchKernelGGL(verify_accept, dim3(B), dim3(256), 0, stream, input_kind, target, draft, draft_log_z,
@@ -761,15 +761,6 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
                      input_kind, target, draft, draft_log_z, inv_map, temperature, request_id, k0, k1, jobs, rstat,
                      race, apart, tickets, accepted, out_tokens, accept_prob, B, N, V, Vd, R, p.sample_chunks,
                      p.sample_chunk);
-  return hipGetLastError();
-}
-
-hipError_t launch_verify_stats(const float* target, const float* temperature, int B, int N, int V, void* workspace,
-                               hipStream_t stream) {
-  const VerifyPlan p = plan_verify(B, N, V);
-  RowStat* stats = static_cast<RowStat*>(workspace);  // (the region launch_verify reads them from)
-  hipLaunchKernelGGL(verify_rowstats, dim3((unsigned)((long)B * (N + 1) * p.stat_chunks)), dim3(256), 0, stream,
-                     target, nullptr, temperature, stats, B, N, V, p.stat_chunks, p.stat_chunk);
   return hipGetLastError();
 }
 

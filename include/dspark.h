@@ -11,7 +11,6 @@
  *   dspark_markov_sample  stage 2: N-step low-rank Markov Gumbel-max loop [P1 §2.2, §3, §5; P2 §4]
  *   dspark_admit          stage 4: survival by chain rule, pooled top-K    [P2 §6, §7]
  *   dspark_verify         stage 3: lossless rejection-sampling verify      [P2 §2; P3 §2]
- *   dspark_verify_stats / dspark_verify_finish   the same in two calls
  *
  * Conventions shared by every call
  *   Memory     Every pointer argument is device memory (HBM) unless stated otherwise.
@@ -59,7 +58,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 2
+#define DSPARK_ABI_VERSION 3
 
 typedef enum dspark_status {
   DSPARK_OK = 0,
@@ -205,28 +204,6 @@ dspark_status dspark_verify(int input_kind, const float* target, const float* dr
                             int32_t* accepted, int32_t* out_tokens, float* accept_prob,
                             int B, int N, int V, int Vd,
                             void* workspace, size_t workspace_bytes, void* stream);
-
-/* Stage 3 in two calls.  The statistics of the target rows (base-2 log-sum-exp of
- * l_t / T, or the argmax at T == 0) need only the target logits and temperatures,
- * so they can run before stages 1 and 2 finish, e.g. on another stream.
- *   dspark_verify_stats: those statistics for every row k <= N of every request
- *     (verify_len is not known yet) into the workspace.  target [B, N+1, V] float32
- *     logits, temperature [B] float32, device; the limits of dspark_verify apply.
- *   dspark_verify_finish: the same arguments, checks and results as dspark_verify
- *     (logits or probabilities), without the statistics pass: in logits mode the
- *     workspace must hold dspark_verify_stats's output for the same target,
- *     temperature, B, N and V, with no other call on it in between (undefined
- *     results otherwise; nothing on the device checks it).
- * Both return DSPARK_ERR_INVALID / _UNSUPPORTED / _WORKSPACE as dspark_verify does. */
-dspark_status dspark_verify_stats(const float* target, const float* temperature, int B, int N, int V,
-                                  void* workspace, size_t workspace_bytes, void* stream);
-dspark_status dspark_verify_finish(int input_kind, const float* target, const float* draft,
-                                   const float* draft_log_z, const int32_t* draft_tokens,
-                                   const int32_t* inv_map, const int32_t* verify_len,
-                                   const float* temperature, const uint32_t* request_id, uint64_t seed,
-                                   int32_t* accepted, int32_t* out_tokens, float* accept_prob,
-                                   int B, int N, int V, int Vd,
-                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- stage 3, coupled
  * Gumbel-coupled verification [P1 §5: the target verifies with the same Gumbel seed

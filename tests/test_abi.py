@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(dspark_lib):
 
 
 def test_abi_version(dspark_lib):
-    assert dsl.abi_version() == 2
+    assert dsl.abi_version() == 3
 
 
 def _err():
@@ -92,30 +92,6 @@ def test_verify_validation(dspark_lib):
     need = dsl.verify_workspace_size(2, 8, 1024)
     assert need > 0
     assert _verify(workspace_bytes=need - 1) == WORKSPACE
-
-
-def test_verify_two_call_validation(dspark_lib):
-    L = dsl.load()
-    need = dsl.verify_workspace_size(2, 8, 1024)
-    # statistics pass
-    assert L.dspark_verify_stats(FAKE, FAKE, 0, 8, 1024, FAKE, need, None) == INVALID
-    assert L.dspark_verify_stats(FAKE, FAKE, 2, 65, 1024, FAKE, need, None) == UNSUPPORTED
-    assert L.dspark_verify_stats(FAKE, FAKE, 2, 8, 1026, FAKE, need, None) == INVALID
-    assert L.dspark_verify_stats(FAKE_ODD, FAKE, 2, 8, 1024, FAKE, need, None) == INVALID and "target" in _err()
-    assert L.dspark_verify_stats(FAKE, None, 2, 8, 1024, FAKE, need, None) == INVALID and "temperature" in _err()
-    assert L.dspark_verify_stats(FAKE, FAKE, 2, 8, 1024, None, need, None) == WORKSPACE
-    assert L.dspark_verify_stats(FAKE, FAKE, 2, 8, 1024, FAKE, need - 1, None) == WORKSPACE
-    # the rest: the checks of dspark_verify
-    a = [0, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 0, FAKE, FAKE, None, 2, 8, 1024, 1024, FAKE, 1 << 30, None]
-    bad = list(a)
-    bad[0] = 7
-    assert L.dspark_verify_finish(*bad) == INVALID
-    bad = list(a)
-    bad[3] = None    # draft_log_z, logits input
-    assert L.dspark_verify_finish(*bad) == INVALID and "draft_log_z" in _err()
-    bad = list(a)
-    bad[18] = need - 1
-    assert L.dspark_verify_finish(*bad) == WORKSPACE
 
 
 def test_draft_logits_and_rng_validation(dspark_lib):

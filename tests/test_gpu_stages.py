@@ -316,7 +316,10 @@ def test_verify_probs_bit_exact(B, N, V, Vd, reduced):
                                                     (4, 64, 512, 512, (0.0, 1.0), False),
                                                     # more than 256 requests: statistics and acceptance
                                                     # in separate launches
-                                                    (300, 2, 256, 256, (0.0, 1.0), False)])
+                                                    (300, 2, 256, 256, (0.0, 1.0), False),
+                                                    # one full-vocabulary request; a few with mixed temperatures
+                                                    (1, 8, 151936, 151936, (1.0,), False),
+                                                    (37, 5, 4096, 4096, (0.0, 0.7, 1.0), False)])
 def test_verify_logits_parity(B, N, V, Vd, temps, reduced):
     say(f"verify logits B={B} N={N} V={V} Vd={Vd} T={temps}")
     c = _verify_inputs(B, N, V, Vd, temps, seed=B * N + 1, reduced=reduced)
@@ -335,37 +338,6 @@ def test_verify_logits_parity(B, N, V, Vd, temps, reduced):
     near = compare_verify(host(acc), host(out), ref, exact=False)
     say(f"  {near} near-tie requests of {B}")
     assert near <= max(1, B // 50)
-
-
-@pytest.mark.parametrize("B,N,V,Vd,temps,reduced", [(1, 8, 151936, 151936, (1.0,), False),
-                                                    (37, 5, 4096, 4096, (0.0, 0.7, 1.0), False),
-                                                    (12, 8, 2048, 1000, (0.0, 1.0), True)])
-def test_verify_in_two_calls(B, N, V, Vd, temps, reduced):
-    """verify_stats then verify(stats_done=True) gives exactly the one-call result, with and
-    without accept_prob (the statistics then cover every row, not only rows k <= L)."""
-    say(f"verify in two calls B={B} N={N} V={V} Vd={Vd} T={temps}")
-    c = _verify_inputs(B, N, V, Vd, temps, seed=B * 5 + N, reduced=reduced)
-    logz = np.empty((B, N), np.float32)
-    for b in range(B):
-        for k in range(N):
-            T = float(c["temp"][b])
-            y = c["proc"][b, k].astype(np.float64)
-            logz[b, k] = (np.log(np.exp(y / T - (y / T).max()).sum()) + (y / T).max()) if T > 0 else y.max()
-    inv = None if c["inv"] is None else dev(c["inv"])
-    tgt, temp = dev(c["tgt"]), dev(c["temp"])
-    args = (dsl.INPUT_LOGITS, tgt, dev(c["proc"]), dev(logz), dev(c["tok"]), inv, dev(c["L"]), temp,
-            dev(c["rid"]), 4242)
-    ws = torch.zeros(dsl.verify_workspace_size(B, N, V), dtype=torch.uint8, device="cuda")
-    for alpha in (False, True):
-        one = dsl.verify(*args, with_accept_prob=alpha)
-        dsl.verify_stats(tgt, temp, ws, N)
-        two = dsl.verify(*args, workspace=ws, with_accept_prob=alpha, stats_done=True)
-        for x, y in zip(one, two):
-            assert np.array_equal(host(x), host(y), equal_nan=True), "two-call verify differs"
-    ref = stages.verify("logits", c["tgt"], c["proc"], c["tok"], c["inv"], c["L"], c["temp"], c["rid"], 4242)
-    near = compare_verify(host(two[0]), host(two[1]), ref, exact=False)
-    assert near <= max(1, B // 50)
-    say(f"  identical to one call; {near} near-tie requests against the oracle")
 
 
 def _alpha_ref(p_t, p_d, inv, L):
