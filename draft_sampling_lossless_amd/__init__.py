@@ -26,7 +26,7 @@ import torch
 __all__ = [
     "LIB_PATH", "load", "abi_version", "INPUT_LOGITS", "INPUT_PROBS", "DSparkError",
     "philox_blocks", "race_exponentials", "draft_logits", "markov_sample",
-    "markov_workspace_size", "build_inverse_map", "verify", "verify_workspace_size", "admit",
+    "markov_workspace_size", "build_inverse_map", "verify", "verify_workspace_size", "verify_noalloc", "admit",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.so")
@@ -49,6 +49,9 @@ _SIGS = {
     "dspark_verify_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
     "dspark_verify": (_c_int, [_c_int] + [_c_void_p] * 8 + [_c_u64, _c_void_p, _c_void_p, _c_void_p] + [_c_int] * 4
                       + [_c_void_p, _c_size, _c_void_p]),
+    "dspark_verify_noalloc_max_bytes": (_c_size, []),
+    "dspark_verify_noalloc": (_c_int, [_c_int] + [_c_void_p] * 8 + [_c_u64, _c_void_p, _c_void_p, _c_void_p]
+                              + [_c_int] * 4 + [_c_void_p]),
     "dspark_verify_coupled_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
     "dspark_verify_coupled": (_c_int, [_c_void_p] * 6 + [_c_u64, _c_void_p, _c_void_p] + [_c_int] * 4
                               + [_c_void_p, _c_size, _c_void_p]),
@@ -238,6 +241,25 @@ def verify(input_kind: int, target: torch.Tensor, draft: torch.Tensor, draft_log
     if accept_prob is not None:
         return accepted, out_tokens, accept_prob
     return accepted, out_tokens
+
+
+def verify_noalloc(input_kind: int, target: torch.Tensor, draft: torch.Tensor, draft_log_z: Optional[torch.Tensor],
+                   draft_tokens: torch.Tensor, inv_map: Optional[torch.Tensor], verify_len: Optional[torch.Tensor],
+                   temperature: Optional[torch.Tensor], request_id: torch.Tensor, seed: int,
+                   accepted: torch.Tensor, out_tokens: torch.Tensor, accept_prob: Optional[torch.Tensor] = None):
+    """verify() on the library's static scratch (dspark_verify_noalloc): the outputs must be
+    passed in, nothing is allocated.  Calls that overlap on one device race."""
+    B, N, Vd = draft.shape
+    V = target.shape[2]
+    dev = target.device
+    _check("dspark_verify_noalloc", load().dspark_verify_noalloc(
+        input_kind, _ptr(target, "target", _F32, dev, (B, N + 1, V)), _ptr(draft, "draft", _F32, dev),
+        _ptr(draft_log_z, "draft_log_z", _F32, dev, (B, N)),
+        _ptr(draft_tokens, "draft_tokens", _I32, dev, (B, N)), _ptr(inv_map, "inv_map", _I32, dev, (V,)),
+        _ptr(verify_len, "verify_len", _I32, dev, (B,)), _ptr(temperature, "temperature", _F32, dev, (B,)),
+        _ptr(request_id, "request_id", _U32, dev, (B,)), seed,
+        _ptr(accepted, "accepted", _I32, dev, (B,)), _ptr(out_tokens, "out_tokens", _I32, dev, (B, N + 1)),
+        _ptr(accept_prob, "accept_prob", _F32, dev, (B, N)), B, N, V, Vd, _stream(target)))
 
 
 def verify_coupled_workspace_size(B: int, N: int, V: int) -> int:

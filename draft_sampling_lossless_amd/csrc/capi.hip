@@ -145,7 +145,7 @@ size_t dspark_verify_workspace_size(int B, int N, int V) {
 }  // extern "C"
 
 namespace {
-// the argument checks of dspark_verify (everything but the workspace)
+// the argument checks of dspark_verify and dspark_verify_noalloc (everything but the workspace)
 dspark_status verify_args(int input_kind, const float* target, const float* draft, const float* draft_log_z,
                           const int32_t* draft_tokens, const int32_t* inv_map, const float* temperature,
                           const uint32_t* request_id, const int32_t* accepted, const int32_t* out_tokens, int B, int N,
@@ -194,6 +194,26 @@ dspark_status dspark_verify(int input_kind, const float* target, const float* dr
                                           temperature, request_id, seed, accepted, out_tokens, accept_prob, B, N,
                                           V, Vd, workspace, (hipStream_t)stream),
                     "verify");
+}
+
+size_t dspark_verify_noalloc_max_bytes(void) { return dspark::kVerifyScratchBytes; }
+
+dspark_status dspark_verify_noalloc(int input_kind, const float* target, const float* draft,
+                                    const float* draft_log_z, const int32_t* draft_tokens, const int32_t* inv_map,
+                                    const int32_t* verify_len, const float* temperature, const uint32_t* request_id,
+                                    uint64_t seed, int32_t* accepted, int32_t* out_tokens, float* accept_prob, int B,
+                                    int N, int V, int Vd, void* stream) {
+  const dspark_status st = verify_args(input_kind, target, draft, draft_log_z, draft_tokens, inv_map, temperature,
+                                       request_id, accepted, out_tokens, B, N, V, Vd);
+  if (st != DSPARK_OK) return st;
+  const size_t need = dspark_verify_workspace_size(B, N, V);
+  REQUIRE(need <= dspark::kVerifyScratchBytes, DSPARK_ERR_UNSUPPORTED,
+          "verify_noalloc: this shape needs %zu bytes of scratch, above the static %zu (use dspark_verify with a "
+          "workspace)", need, dspark::kVerifyScratchBytes);
+  return hip_status(dspark::launch_verify_noalloc(input_kind, target, draft, draft_log_z, draft_tokens, inv_map,
+                                                  verify_len, temperature, request_id, seed, accepted, out_tokens,
+                                                  accept_prob, B, N, V, Vd, (hipStream_t)stream),
+                    "verify_noalloc");
 }
 
 size_t dspark_verify_coupled_workspace_size(int B, int N, int V) {

@@ -66,6 +66,13 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
                          const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
                          int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
                          hipStream_t stream);
+// launch_verify with the library's static per-device scratch array as workspace
+constexpr size_t kVerifyScratchBytes = (size_t)4 << 20;
+hipError_t launch_verify_noalloc(int input_kind, const float* target, const float* draft, const float* draft_log_z,
+                                 const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
+                                 const float* temperature, const uint32_t* request_id, uint64_t seed,
+                                 int32_t* accepted, int32_t* out_tokens, float* accept_prob, int B, int N, int V,
+                                 int Vd, hipStream_t stream);
 
 // ---- Gumbel-coupled verification
 size_t coupled_workspace_bytes(int B, int N, int V);

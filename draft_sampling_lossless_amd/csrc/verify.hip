@@ -764,4 +764,30 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- no-allocation variant
+// The workspace of launch_verify as a file-scope device array, for callers that cannot
+// allocate.  Each device holds its own copy at its own address; host code uses the
+// address hipGetSymbolAddress returns for the current device, never the array's name.
+// Every call on a device shares that device's copy, so calls that overlap on one
+// device race.  launch_verify needs no initialised workspace content.
+__device__ __attribute__((aligned(256))) char scratch[kVerifyScratchBytes];
+
+hipError_t launch_verify_noalloc(int input_kind, const float* target, const float* draft, const float* draft_log_z,
+                                 const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
+                                 const float* temperature, const uint32_t* request_id, uint64_t seed,
+                                 int32_t* accepted, int32_t* out_tokens, float* accept_prob, int B, int N, int V,
+                                 int Vd, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  static std::atomic<void*> ptr_of[64];
+  void* ptr = ptr_of[dev].load(std::memory_order_acquire);
+  if (!ptr) {  // first call on this device, with the device current (concurrent first calls store the same address)
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr_of[dev].store(ptr, std::memory_order_release);
+  }
+  return launch_verify(input_kind, target, draft, draft_log_z, draft_tokens, inv_map, verify_len, temperature,
+                       request_id, seed, accepted, out_tokens, accept_prob, B, N, V, Vd, ptr, stream);
+}
+
 }  // namespace dspark

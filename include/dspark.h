@@ -205,6 +205,24 @@ dspark_status dspark_verify(int input_kind, const float* target, const float* dr
                             int B, int N, int V, int Vd,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* dspark_verify without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments (minus workspace), checks, kernels and results as
+ * dspark_verify.  The scratch is a static device array of the library,
+ * dspark_verify_noalloc_max_bytes() bytes (4 MiB) per device, held until the process
+ * ends; a shape whose dspark_verify_workspace_size(B, N, V) exceeds it returns
+ * DSPARK_ERR_UNSUPPORTED and enqueues nothing.  The call allocates nothing.  Every
+ * call on one device shares that device's array, so two calls that overlap on one
+ * device (two streams, or two host threads) race and give undefined results; calls
+ * on different devices do not interact. */
+size_t dspark_verify_noalloc_max_bytes(void);
+dspark_status dspark_verify_noalloc(int input_kind, const float* target, const float* draft,
+                                    const float* draft_log_z, const int32_t* draft_tokens,
+                                    const int32_t* inv_map, const int32_t* verify_len,
+                                    const float* temperature, const uint32_t* request_id, uint64_t seed,
+                                    int32_t* accepted, int32_t* out_tokens, float* accept_prob,
+                                    int B, int N, int V, int Vd, void* stream);
+
 /* ---------------------------------------------------------------- stage 3, coupled
  * Gumbel-coupled verification [P1 §5: the target verifies with the same Gumbel seed
  * the draft sampled with, so the output distribution is unchanged].  No draft
