@@ -45,6 +45,8 @@ _SIGS = {
     "dspark_markov_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "dspark_markov_sample": (_c_int, [_c_void_p] * 7 + [_c_u64, _c_void_p, _c_void_p] + [_c_int] * 5
                              + [_c_void_p, _c_size, _c_void_p]),
+    "dspark_markov_check": (_c_int, [_c_void_p]),
+    "dspark_markov_test_mode": (_c_int, [_c_int]),
     "dspark_build_inverse_map": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_void_p]),
     "dspark_verify_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
     "dspark_verify": (_c_int, [_c_int] + [_c_void_p] * 8 + [_c_u64, _c_void_p, _c_void_p, _c_void_p] + [_c_int] * 4
@@ -193,6 +195,17 @@ def markov_sample(logits: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, d2t:
         _ptr(draft_tokens, "draft_tokens", _I32, dev, (B, N)), _ptr(log_z, "log_z", _F32, dev, (B, N)),
         B, N, V, Vd, r, ws.data_ptr(), ws.numel(), _stream(logits)))
     return draft_tokens, log_z
+
+
+def markov_check() -> None:
+    """Synchronise the current stream and raise DSparkError if a few-request Markov
+    launch since the last check gave up on a grid barrier (its outputs are -1 / NaN)."""
+    _check("dspark_markov_check", load().dspark_markov_check(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+
+
+def markov_test_mode(mode: int) -> None:
+    """Test hook: 0 normal, 1 single-workgroup few-request kernel, 2 forced barrier give-up."""
+    _check("dspark_markov_test_mode", load().dspark_markov_test_mode(int(mode)))
 
 
 def build_inverse_map(d2t: torch.Tensor, V: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:

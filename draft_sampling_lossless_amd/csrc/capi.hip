@@ -129,6 +129,24 @@ dspark_status dspark_markov_sample(float* logits, const uint16_t* w1, const uint
                     "markov_sample");
 }
 
+dspark_status dspark_markov_check(void* stream) {
+  bool gave_up = false;
+  const hipError_t e = dspark::markov_check((hipStream_t)stream, &gave_up);
+  if (e != hipSuccess) return hip_status(e, "markov_check");
+  if (gave_up)
+    return fail(DSPARK_ERR_HIP,
+                "markov_sample: a grid barrier of the few-request kernel gave up waiting (not every workgroup "
+                "became resident); the draft tokens and log Z of the launches since the previous check are "
+                "invalid (-1 / NaN)");
+  return ok();
+}
+
+dspark_status dspark_markov_test_mode(int mode) {
+  REQUIRE(mode >= 0 && mode <= 2, DSPARK_ERR_INVALID, "mode must be 0, 1 or 2 (got %d)", mode);
+  dspark::set_markov_test_mode(mode);
+  return ok();
+}
+
 dspark_status dspark_build_inverse_map(const int64_t* d2t, int Vd, int V, int32_t* inv_map, void* stream) {
   REQUIRE(Vd > 0 && V > 0 && Vd <= V, DSPARK_ERR_INVALID, "need 0 < Vd <= V (got Vd=%d, V=%d)", Vd, V);
   REQUIRE_PTR(d2t, "d2t");

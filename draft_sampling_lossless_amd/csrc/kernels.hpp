@@ -50,6 +50,11 @@ hipError_t launch_markov_sample(float* logits, const uint16_t* w1, const uint16_
                                 const int32_t* anchor, const float* temperature, const uint32_t* request_id,
                                 uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,
                                 int r, void* workspace, hipStream_t stream);
+// few-request kernel: test hooks (0 normal, 1 single workgroup, 2 forced barrier give-up)
+// and the host-side check of the device's sticky give-up word (synchronises `stream`;
+// on a give-up also resets the counter sets)
+void set_markov_test_mode(int mode);
+hipError_t markov_check(hipStream_t stream, bool* gave_up);
 hipError_t launch_build_inverse_map(const int64_t* d2t, int Vd, int V, int32_t* inv_map, hipStream_t stream);
 
 // ---- stage 3

@@ -110,7 +110,7 @@ constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0) (gfx9 encoding)
 // misc layout (ints)
 constexpr int kMsCnt = 0, kMsInc = 64, kMsOff = 128, kMsSel = 192, kMsPre = 256;  // [64] each ([65] for kMsPre)
 constexpr int kMsFs = 336, kMsFit = 337, kMsPairs = 338, kMsTot = 339, kMsRole = 340, kMsTicket = 341;
-constexpr int kMsLastOut = 342, kMsRows = 343;
+constexpr int kMsLastOut = 342, kMsRows = 343, kMsBarrierOk = 344;
 constexpr int kMsRoff = 448;  // [64] first (previous survivor) row of each step in phase C
 constexpr int kMsPrev = 352, kMsFst = 368;  // [16] each (per-step pass)
 constexpr int kMsN1 = 384;                  // [16] floats: largest recorded W1 norm per request (phase B)
@@ -156,6 +156,8 @@ struct FewArgs {
   FewWs ws;
   uint32_t key0, key1;
   int B, N, V, Vd, r, CH, cap, force_solo;
+  unsigned* status;       // the device's sticky error word (bit 0: a grid barrier gave up)
+  int force_give_up;      // test mode: every grid barrier reports a give-up after it completes
 };
 
 // layout of the phase-C region of LDS (also used by the host plan)
@@ -201,6 +203,9 @@ __device__ __forceinline__ int req_anchor(const Lds& L, int b) { return L.misc[k
 
 // every launch's counter sets, kCtrWords words each (zero-initialised when loaded)
 __device__ __attribute__((aligned(256))) unsigned g_few_counters[kCtrSets * kCtrWords];
+// sticky error word of this device: set when a grid barrier's bounded wait gives up;
+// read and cleared by the host (dspark_markov_check)
+__device__ __attribute__((aligned(256))) unsigned g_few_status[64];
 
 // half-width of a full key's interval around the bias-free key, per unit of W2
 // row norm, and an absolute slack: room for the float rounding of norms, dots
@@ -1172,11 +1177,23 @@ __device__ __forceinline__ bool barrier_done(unsigned* ctr, unsigned round, int 
 }
 
 // The wait is bounded (about 0.1 s) so that a broken launch can never hang the device.
-__device__ __forceinline__ void grid_barrier(unsigned* ctr, unsigned round, int G) {
-  barrier_arrive(ctr, round, G);
-  if (threadIdx.x == 0)
-    for (int spin = 0; spin < (1 << 22) && !barrier_done(ctr, round, G); ++spin) __builtin_amdgcn_s_sleep(1);
+// Returns false (the whole workgroup) when the bound ran out before every workgroup
+// arrived; the sticky status word then records it, and the caller consumes nothing
+// that other workgroups were to publish before this barrier.  (force_give_up: the
+// test mode reports a give-up after a barrier that did complete.)
+__device__ __forceinline__ bool grid_barrier(const FewArgs& a, unsigned round, int G, int* misc) {
+  barrier_arrive(a.ws.ctr, round, G);
+  if (threadIdx.x == 0) {
+    bool done = false;
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+      if ((done = barrier_done(a.ws.ctr, round, G))) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (!done || a.force_give_up) __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    misc[kMsBarrierOk] = done && !a.force_give_up;
+  }
   __syncthreads();
+  return misc[kMsBarrierOk] != 0;
 }
 
 // Role of this workgroup at the first barrier: 0 return at once, 1 go on with its
@@ -1213,16 +1230,23 @@ __device__ __forceinline__ int first_barrier_role(const FewArgs& a, int G, bool 
         __builtin_amdgcn_s_sleep(1);
       }
     } else {
-      // the first workgroup settles it within its window; the bound only guards a broken launch
+      // the first workgroup settles it within its window; the bound only guards a broken
+      // launch, and running out of it is recorded in the sticky status word
+      bool settled = false;
       for (int spin = 0; spin < (1 << 22); ++spin) {
         const unsigned v = ld_u(ctr);
-        if (v & kClosed) break;
+        if (v & kClosed) {
+          settled = true;
+          break;
+        }
         if (v >= target) {
           role = 1;
+          settled = true;
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
+      if (!settled) __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     misc[kMsRole] = role;
   }
@@ -1330,18 +1354,23 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
   else
     for (int b = solo ? 0 : wg; b < B; b += solo ? 1 : G) phase_c(a, L, b, G, true);
   const bool rows_in_lds = redundant && L.misc[kMsFs] == N && L.misc[kMsFit] != 0;
-  if (!solo && !rows_in_lds) grid_barrier(a.ws.ctr, ++round, G);
+  // A grid barrier whose bounded wait gave up leaves this workgroup "broken": it reads
+  // nothing more that other workgroups publish and goes straight to the final count
+  // (every later barrier of the others then gives up too), and the last workgroup
+  // replaces the outputs by -1 tokens and NaN log Z.
+  bool broken = false;
+  if (!solo && !rows_in_lds) broken = !grid_barrier(a, ++round, G, L.misc);
 
   // per-step pass from the first incomplete step of any request
   int* prevs = L.misc + kMsPrev;
   int* fstl = L.misc + kMsFst;
-  if (tid < B) fstl[tid] = rows_in_lds ? N : ld_i(a.ws.fstep + tid);
+  if (tid < B) fstl[tid] = (rows_in_lds || broken) ? N : ld_i(a.ws.fstep + tid);
   __syncthreads();
   int fmin = N;
   for (int b = 0; b < B; ++b) fmin = min(fmin, fstl[b]);
   const bool writer = solo || wg == 0;
   if (__builtin_expect(fmin < N, 0)) {
-    for (int s = fmin; s < N; ++s) {
+    for (int s = fmin; s < N && !broken; ++s) {
       step_prevs(a, G, s, fstl, prevs, writer);
       bf16x8 efrag[kMaxKSteps];
       load_efrag(a.w1, (n < B) ? prevs[n] : 0, n < B && fstl[n] <= s, a.V, r, ksteps, g, efrag);
@@ -1350,14 +1379,16 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
         if (solo) load_slice<false>(a, L, sl);
         step_partial(a, L, sl, vwg, G, s, fstl, efrag);
       }
-      if (!solo) grid_barrier(a.ws.ctr, ++round, G);
+      if (!solo) broken = !grid_barrier(a, ++round, G, L.misc);
     }
-    // tokens of the last step (s == N: nothing is published)
-    step_prevs(a, G, N, fstl, prevs, writer);
-    if (!solo) grid_barrier(a.ws.ctr, ++round, G);
+    if (!broken) {
+      // tokens of the last step (s == N: nothing is published)
+      step_prevs(a, G, N, fstl, prevs, writer);
+      if (!solo) broken = !grid_barrier(a, ++round, G, L.misc);
+    }
   }
 
-  for (int vwg = v0; vwg < v1; ++vwg) {
+  for (int vwg = v0; vwg < v1 && !broken; ++vwg) {
     const Slice sl = slice_of(a, vwg);
     if (__builtin_expect(solo, 0)) {
       load_slice<false>(a, L, sl);
@@ -1375,9 +1406,20 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
   else
     clear_counters(a.ws.ctr, merge);
   if (merge) {
-    for (int row = wave; row < rows; row += 4) {
-      const MarkovPartial q = wave_merge(a.ws.partD + (size_t)row * G, G, lane);
-      if (lane == 0) a.log_z[row] = log_z_of(q, req_temperature(L, row / N));
+    // a grid barrier of this launch (or of an earlier one not yet checked) gave up:
+    // no output is trustworthy, so none is left looking valid
+    if (tid == 0) L.misc[kMsBarrierOk] = ld_u(a.status) == 0u;
+    __syncthreads();
+    if (L.misc[kMsBarrierOk]) {
+      for (int row = wave; row < rows; row += 4) {
+        const MarkovPartial q = wave_merge(a.ws.partD + (size_t)row * G, G, lane);
+        if (lane == 0) a.log_z[row] = log_z_of(q, req_temperature(L, row / N));
+      }
+    } else {
+      for (int row = tid; row < rows; row += blockDim.x) {
+        st_i(a.draft_tokens + row, -1);
+        a.log_z[row] = __builtin_nanf("");
+      }
     }
   }
 }
@@ -1385,6 +1427,10 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
+
+// test hooks (dspark_markov_test_mode): 1 every slice in one workgroup, 2 every grid
+// barrier reports a give-up after it completes
+std::atomic<int> g_markov_test_mode{0};
 
 FewPlan plan_markov_few(int B, int N, int Vd, int r, int cus) {
   FewPlan p{};
@@ -1471,6 +1517,16 @@ hipError_t launch_markov_few(const FewPlan& p, float* logits, const uint16_t* w1
     ctr_base[dev].store(base, std::memory_order_relaxed);
   }
   a.ws.ctr = base + (size_t)(next_set[dev].fetch_add(1u, std::memory_order_relaxed) % kCtrSets) * kCtrWords;
+  static std::atomic<unsigned*> status_of[64];
+  unsigned* status = status_of[dev].load(std::memory_order_relaxed);
+  if (!status) {
+    void* sym = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&sym, HIP_SYMBOL(g_few_status));
+    if (e != hipSuccess) return e;
+    status = static_cast<unsigned*>(sym);
+    status_of[dev].store(status, std::memory_order_relaxed);
+  }
+  a.status = status;
   a.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
   a.key1 = (uint32_t)(seed >> 32);
   a.B = B;
@@ -1480,11 +1536,31 @@ hipError_t launch_markov_few(const FewPlan& p, float* logits, const uint16_t* w1
   a.r = r;
   a.CH = p.ch;
   a.cap = p.cap;
-  // test hook: DSPARK_MARKOV_SOLO=1 runs every slice in one workgroup
-  const char* solo = getenv("DSPARK_MARKOV_SOLO");
-  a.force_solo = (solo && solo[0] == '1') ? 1 : 0;
+  const int mode = g_markov_test_mode.load(std::memory_order_relaxed);
+  a.force_solo = mode == 1;
+  a.force_give_up = mode == 2;
   hipLaunchKernelGGL(markov_few, dim3(p.grid), dim3(256), p.lds, stream, a);
   return hipGetLastError();
+}
+
+void set_markov_test_mode(int mode) { g_markov_test_mode.store(mode, std::memory_order_relaxed); }
+
+hipError_t markov_check(hipStream_t stream, bool* gave_up) {
+  *gave_up = false;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return e;
+  void* sym = nullptr;
+  if ((e = hipGetSymbolAddress(&sym, HIP_SYMBOL(g_few_status))) != hipSuccess) return e;
+  unsigned v = 0;
+  if ((e = hipMemcpy(&v, sym, sizeof(v), hipMemcpyDeviceToHost)) != hipSuccess) return e;
+  if (v == 0u) return hipSuccess;
+  *gave_up = true;
+  // a launch that gave up may have left its counter set uncleared: reset every set
+  void* ctr = nullptr;
+  if ((e = hipGetSymbolAddress(&ctr, HIP_SYMBOL(g_few_counters))) != hipSuccess) return e;
+  if ((e = hipMemset(ctr, 0, sizeof(unsigned) * kCtrSets * kCtrWords)) != hipSuccess) return e;
+  if ((e = hipMemset(sym, 0, sizeof(unsigned))) != hipSuccess) return e;
+  return hipDeviceSynchronize();
 }
 
 }  // namespace dspark

@@ -149,6 +149,25 @@ dspark_status dspark_markov_sample(float* logits, const uint16_t* w1, const uint
                                    int B, int N, int V, int Vd, int r,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Give-up check of the few-request kernel (B <= 16).  That kernel synchronises its
+ * workgroups with grid barriers whose waits are bounded (about 0.1 s), so a launch
+ * whose workgroups cannot all become resident never hangs the device.  A wait that
+ * runs out sets a sticky per-device error word; the launch then stops consuming
+ * data of other workgroups and writes draft_tokens = -1 and log_z = NaN for every
+ * position, as does every later launch until the word is cleared.
+ * dspark_markov_check synchronises `stream`, reads the word, and if it is set
+ * clears it (and the library's barrier counters) and returns DSPARK_ERR_HIP with a
+ * message; otherwise DSPARK_OK.  It is the one call that waits and reads device
+ * memory on the host. */
+dspark_status dspark_markov_check(void* stream);
+
+/* Test hooks of the few-request kernel (process-wide; not for production use):
+ *   0 normal; 1 every vocabulary slice is run by a single workgroup (the fallback
+ *   when not every workgroup becomes resident); 2 every grid barrier reports a
+ *   give-up after it has completed (exercises the error path without ever reading
+ *   data that was not published).  Other values: DSPARK_ERR_INVALID. */
+dspark_status dspark_markov_test_mode(int mode);
+
 /* Inverse of the reduced-vocabulary map [P3 §3.2 (d2t)]: inv_map[v] = j if
  * v == j + d2t[j], else -1.
  *   d2t [Vd] int64, device (injective into [0, V), not checked on the device);

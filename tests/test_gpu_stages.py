@@ -193,13 +193,17 @@ def test_markov_unstaged_chain():
     (2, 5, 8192, 8192, 64, (1.0,), 0.02),   # survivors: the staged chain
     (3, 4, 4096, 4096, 64, (0.0, 1.0), 1.0),  # the per-step pass
 ])
-def test_markov_few_solo(B, N, V, Vd, r, temps, wstd, monkeypatch):
+def test_markov_few_solo(B, N, V, Vd, r, temps, wstd):
     # the few-request kernel with every slice run by one workgroup (what it does when
     # not all of its workgroups become resident): same results as the oracle
-    monkeypatch.setenv("DSPARK_MARKOV_SOLO", "1")
     say(f"markov few solo B={B} N={N} V={V} r={r} std={wstd}")
     c = _markov_case(B, N, V, Vd, r, temps, seed=0x51, wstd=wstd)
-    tok, proc, logz = _run_markov_gpu(c)
+    dsl.markov_test_mode(1)
+    try:
+        tok, proc, logz = _run_markov_gpu(c)
+    finally:
+        dsl.markov_test_mode(0)
+    dsl.markov_check()
     ref = stages.markov_sample(c["base"], c["w1"], c["w2"], None, c["anchor"], c["temp"], c["rid"], c["seed"],
                                teacher=tok)
     checked, near = compare_markov(tok, proc, logz, ref, label=f"few solo B={B} std={wstd}")
@@ -217,7 +221,7 @@ def test_markov_deterministic():
                                   y.view(np.uint32) if y.dtype == np.float32 else y)
 
 
-def test_markov_few_counter_sets_reused(monkeypatch):
+def test_markov_few_counter_sets_reused():
     """The few-request kernel's barrier counters live in a ring of counter sets that each
     launch leaves cleared.  Well over two rounds of the ring, alternating normal and
     single-workgroup launches (which clear the counters on different paths), give the
@@ -226,14 +230,40 @@ def test_markov_few_counter_sets_reused(monkeypatch):
     say("markov few: 150 launches over the counter sets")
     ref = _run_markov_gpu(c)
     for i in range(150):
-        if i % 3 == 2:
-            monkeypatch.setenv("DSPARK_MARKOV_SOLO", "1")
-        else:
-            monkeypatch.delenv("DSPARK_MARKOV_SOLO", raising=False)
-        got = _run_markov_gpu(c)
+        dsl.markov_test_mode(1 if i % 3 == 2 else 0)
+        try:
+            got = _run_markov_gpu(c)
+        finally:
+            dsl.markov_test_mode(0)
         for x, y in zip(ref, got):
             assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
                                   y.view(np.uint32) if y.dtype == np.float32 else y), f"launch {i}"
+
+
+@pytest.mark.parametrize("B,N,V,r,wstd,temps", [
+    (2, 5, 8192, 64, 0.02, (0.0, 1.0)),   # several requests: a barrier after phase C
+    (3, 4, 4096, 64, 1.0, (0.0, 1.0)),    # the per-step pass: a barrier per step
+    (1, 6, 4096, 64, 1.0, (1.0,))])       # one request, margin too wide: the per-step pass from step 0
+def test_markov_few_barrier_give_up_is_reported(B, N, V, r, wstd, temps):
+    """A grid barrier that gives up (forced from the host: every barrier reports a give-up
+    after completing) never leaves valid-looking outputs: every token is -1, log Z is NaN,
+    and the check raises.  After the check the next launch is correct again."""
+    c = _markov_case(B, N, V, V, r, temps, seed=0x61, wstd=wstd)
+    say(f"markov few forced give-up B={B} N={N} V={V} std={wstd}")
+    dsl.markov_check()                                   # nothing pending
+    dsl.markov_test_mode(2)
+    try:
+        tok, _, logz = _run_markov_gpu(c)
+    finally:
+        dsl.markov_test_mode(0)
+    with pytest.raises(dsl.DSparkError, match="gave up"):
+        dsl.markov_check()
+    assert (tok == -1).all() and np.isnan(logz).all()
+    tok, proc, logz = _run_markov_gpu(c)
+    dsl.markov_check()
+    ref = stages.markov_sample(c["base"], c["w1"], c["w2"], None, c["anchor"], c["temp"], c["rid"], c["seed"],
+                               teacher=tok)
+    compare_markov(tok, proc, logz, ref, label=f"after give-up B={B}")
 
 
 @pytest.mark.parametrize("name,nsample", [("qwen3_8b_single", 1), ("batched", 4), ("admission", 3),
