@@ -50,6 +50,10 @@ def parse():
                    help="path: stages 1-4 with the workload's synthetic confidences and fixed K (default); "
                         "full: also the confidence head (its output feeds admission) and the throughput-optimal "
                         "K, computed from this round's survival and used two rounds later")
+    p.add_argument("--rounds", type=int, default=8,
+                   help="multi-round driver: R consecutive rounds (each drafting from the previous round's last "
+                        "emitted token, with its own seed) captured in one HIP graph and replayed; reports tau and "
+                        "the time per emitted token (0: skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache stage timings")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
@@ -125,7 +129,9 @@ class Path:
             # confidence head weights (random, like every weight here): w ~ N(0, 1/(H + r)),
             # bias 1.5 and per-position temperatures; an SPS table of the target engine
             g = np.random.default_rng([w.seed, 91])
-            self.wconf = up(synth.bf16_bits(g.normal(0, 1.0 / np.sqrt(w.H + w.r), size=w.H + w.r).astype(np.float32)))
+            wconf = synth.bf16_bits(g.normal(0, 1.0 / np.sqrt(w.H + w.r), size=w.H + w.r).astype(np.float32))
+            self.w_h, self.w_e = up(wconf[:w.H].copy()), up(wconf[w.H:].copy())
+            self.h_dot = torch.empty(w.M, dtype=torch.float32, device=dev)
             self.cbias = 1.5
             self.tau = up(np.linspace(1.0, 1.6, w.N).astype(np.float32))
             self.sps = up(synth.sps_table(w.B * w.N + w.B + 64, seed=w.seed, tile=64, knee=max(64, w.B * 4)))
@@ -136,6 +142,10 @@ class Path:
             self.k_ready = [torch.cuda.Event() for _ in range(3)]
             self.round = 0
             self.K_used = []
+        # multi-round driving (off by default): anchor <- last emitted token, emitted count
+        self.advance = False
+        self.round_seed = 0
+        self.emitted = torch.zeros(w.B, dtype=torch.int64, device=dev)
         torch.cuda.synchronize()
         self.setup_s = time.time() - t0
 
@@ -162,28 +172,39 @@ class Path:
             if timer is not None:
                 timer.end(name)
 
-        stage("draft_logits", lambda: dsl.draft_logits(self.hidden, self.lm_head, out=self.logits.view(w.M, w.Vd)))
-        stage("markov_sample", lambda: dsl.markov_sample(
-            self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, self.seed,
-            draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov))
-        conf = self.conf
+        seed = self.seed + self.round_seed
         if self.full:
-            stage("confidence", lambda: dsl.confidence(self.hidden, self.w1, self.tokens, self.anchor, self.wconf,
-                                                       self.cbias, self.tau, c_out=self.c_model))
+            # the confidence head rides along: w_h as one more LM-head row, the rest in stage 2
+            stage("draft_logits", lambda: dsl.draft_logits(self.hidden, self.lm_head, out=self.logits.view(w.M, w.Vd),
+                                                           w_h=self.w_h, h_dot=self.h_dot))
+            stage("markov_sample", lambda: dsl.markov_sample(
+                self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, seed,
+                draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov,
+                conf=(self.h_dot, self.w_e, self.cbias, self.tau, self.c_model)))
             conf = self.c_model
+        else:
+            stage("draft_logits", lambda: dsl.draft_logits(self.hidden, self.lm_head,
+                                                           out=self.logits.view(w.M, w.Vd)))
+            stage("markov_sample", lambda: dsl.markov_sample(
+                self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, seed,
+                draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov))
+            conf = self.conf
         K = self.budget()
         if self.full:
             self.K_used.append(K)
         stage("admit", lambda: dsl.admit(conf, K, survival=self.survival, admit_len=self.admit_len))
         if self.coupled:
             stage("verify", lambda: dsl.verify_coupled(
-                self.target, self.tokens, self.inv, self.admit_len, self.temp, self.rid, self.seed, Vd=w.Vd,
+                self.target, self.tokens, self.inv, self.admit_len, self.temp, self.rid, seed, Vd=w.Vd,
                 accepted=self.accepted, out_tokens=self.out_tokens, workspace=self.ws_verify))
         else:
             stage("verify", lambda: dsl.verify(
                 dsl.INPUT_LOGITS, self.target, self.logits, self.logz, self.tokens, self.inv, self.admit_len,
-                self.temp, self.rid, self.seed, accepted=self.accepted, out_tokens=self.out_tokens,
+                self.temp, self.rid, seed, accepted=self.accepted, out_tokens=self.out_tokens,
                 workspace=self.ws_verify))
+        if self.advance:
+            # the next round drafts from this round's last emitted token
+            stage("advance", lambda: dsl.advance(self.accepted, self.out_tokens, self.anchor, self.emitted))
         if self.full:
             def budget_ahead():
                 # the budget of two rounds ahead, from this round's survival
@@ -377,6 +398,47 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def multi_round(w, path, torch, R, reps=5):
+    """R consecutive rounds captured in one HIP graph: round q drafts from the previous
+    round's last emitted token (dspark_advance) with seed base + q.  The hidden states
+    and target logits stay those of the synthetic batch (no backbone or target model
+    runs here).  tau = tokens emitted per request per round; time per emitted token =
+    round time / tau, i.e. (T_draft + T_verify) / tau."""
+    anchor0 = path.anchor.clone()
+    path.advance = True
+    for q in range(R):                      # warm-up of the same rounds, eager
+        path.round_seed = q + 1
+        path.step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for q in range(R):
+            path.round_seed = q + 1        # (each captured launch keeps its own seed)
+            path.step()
+    path.round_seed = 0
+    times = []
+    for _ in range(reps):
+        path.anchor.copy_(anchor0)
+        path.emitted.zero_()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    emitted = int(path.emitted.sum().item())
+    ms = float(np.median(times))
+    tau = emitted / (w.B * R)
+    path.advance = False
+    path.anchor.copy_(anchor0)
+    del graph
+    return {"rounds": R, "graph": True, "tau": round(tau, 4), "ms_per_round": round(ms / R, 4),
+            "round_ms_per_token": round(ms / R / tau, 4), "emitted_tokens_per_s": round(emitted / (ms * 1e-3), 1),
+            "note": "tau = tokens emitted per request per round (accepted drafts + 1); round_ms_per_token = "
+                    "(T_draft + T_verify) / tau"}
+
+
 def run(args, w, path, torch):
     graph = None
     if args.graph:
@@ -465,6 +527,8 @@ def run(args, w, path, torch):
                               "last": path.K_used[-1], "of": w.B * w.N}
     if graph is not None:
         del graph
+    if args.rounds > 0 and not path.full:
+        result["multi_round"] = multi_round(w, path, torch, args.rounds)
     return result
 
 

@@ -57,7 +57,10 @@ _SIGS = {
     "dspark_verify_coupled_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
     "dspark_verify_coupled": (_c_int, [_c_void_p] * 6 + [_c_u64, _c_void_p, _c_void_p] + [_c_int] * 4
                               + [_c_void_p, _c_size, _c_void_p]),
-    "dspark_confidence": (_c_int, [_c_void_p] * 5 + [ctypes.c_float] + [_c_void_p] * 2 + [_c_int] * 5 + [_c_void_p]),
+    "dspark_draft_logits_conf": (_c_int, [_c_void_p] * 5 + [_c_int] * 3 + [_c_void_p]),
+    "dspark_markov_sample_conf": (_c_int, [_c_void_p] * 7 + [_c_u64] + [_c_void_p] * 4 + [ctypes.c_float]
+                                  + [_c_void_p] * 2 + [_c_int] * 5 + [_c_void_p, _c_size, _c_void_p]),
+    "dspark_advance": (_c_int, [_c_void_p] * 4 + [_c_int] * 2 + [_c_void_p]),
     "dspark_choose_k": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "dspark_admit": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
 }
@@ -155,17 +158,28 @@ def race_exponentials(seed: int, position: int, request_id: int, tag: int, n: in
 # ---------------------------------------------------------------- stage 1
 
 def draft_logits(hidden: torch.Tensor, lm_head: torch.Tensor,
-                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """logits[m, j] = sum_h hidden[m, h] * lm_head[j, h]; hidden [M, H], lm_head [Vd, H] bf16."""
+                 out: Optional[torch.Tensor] = None, w_h: Optional[torch.Tensor] = None,
+                 h_dot: Optional[torch.Tensor] = None):
+    """logits[m, j] = sum_h hidden[m, h] * lm_head[j, h]; hidden [M, H], lm_head [Vd, H] bf16.
+    With w_h [H] bf16 (the confidence head's hidden-state weights, dspark_draft_logits_conf)
+    also h_dot[m] = w_h . hidden[m]; returns (logits, h_dot) then."""
     M, H = hidden.shape
     Vd = lm_head.shape[0]
     dev = hidden.device
     if out is None:
         out = torch.empty((M, Vd), dtype=torch.float32, device=dev)
-    _check("dspark_draft_logits", load().dspark_draft_logits(
+    if w_h is None:
+        _check("dspark_draft_logits", load().dspark_draft_logits(
+            _ptr(hidden, "hidden", _BF16, dev), _ptr(lm_head, "lm_head", _BF16, dev, (Vd, H)),
+            _ptr(out, "out", _F32, dev, (M, Vd)), M, H, Vd, _stream(hidden)))
+        return out
+    if h_dot is None:
+        h_dot = torch.empty(M, dtype=torch.float32, device=dev)
+    _check("dspark_draft_logits_conf", load().dspark_draft_logits_conf(
         _ptr(hidden, "hidden", _BF16, dev), _ptr(lm_head, "lm_head", _BF16, dev, (Vd, H)),
-        _ptr(out, "out", _F32, dev, (M, Vd)), M, H, Vd, _stream(hidden)))
-    return out
+        _ptr(w_h, "w_h", _BF16, dev, (H,)), _ptr(out, "out", _F32, dev, (M, Vd)),
+        _ptr(h_dot, "h_dot", _F32, dev, (M,)), M, H, Vd, _stream(hidden)))
+    return out, h_dot
 
 
 # ---------------------------------------------------------------- stage 2
@@ -177,8 +191,10 @@ def markov_workspace_size(B: int, N: int, Vd: int, r: int) -> int:
 def markov_sample(logits: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, d2t: Optional[torch.Tensor],
                   anchor: torch.Tensor, temperature: torch.Tensor, request_id: torch.Tensor, seed: int,
                   draft_tokens: Optional[torch.Tensor] = None, log_z: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Stage 2 on logits [B, N, Vd] (base in, processed out, in place).  Returns (tokens, log_z)."""
+                  workspace: Optional[torch.Tensor] = None, conf=None):
+    """Stage 2 on logits [B, N, Vd] (base in, processed out, in place).  Returns (tokens, log_z).
+    conf = (h_dot [B*N], w_e [r] bf16, bias, tau [N], c_out [B, N] or None): the fused
+    confidence head (dspark_markov_sample_conf); returns (tokens, log_z, c) then."""
     B, N, Vd = logits.shape
     V, r = w1.shape
     dev = logits.device
@@ -187,6 +203,20 @@ def markov_sample(logits: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, d2t:
     if log_z is None:
         log_z = torch.empty((B, N), dtype=torch.float32, device=dev)
     ws = _workspace(workspace, markov_workspace_size(B, N, Vd, r), dev)
+    if conf is not None:
+        h_dot, w_e, cbias, tau, c_out = conf
+        if c_out is None:
+            c_out = torch.empty((B, N), dtype=torch.float32, device=dev)
+        _check("dspark_markov_sample_conf", load().dspark_markov_sample_conf(
+            _ptr(logits, "logits", _F32, dev), _ptr(w1, "w1", _BF16, dev),
+            _ptr(w2, "w2", _BF16, dev, (Vd, r)), _ptr(d2t, "d2t", _I64, dev, (Vd,)),
+            _ptr(anchor, "anchor", _I32, dev, (B,)), _ptr(temperature, "temperature", _F32, dev, (B,)),
+            _ptr(request_id, "request_id", _U32, dev, (B,)), seed,
+            _ptr(draft_tokens, "draft_tokens", _I32, dev, (B, N)), _ptr(log_z, "log_z", _F32, dev, (B, N)),
+            _ptr(h_dot, "h_dot", _F32, dev, (B * N,)), _ptr(w_e, "w_e", _BF16, dev, (r,)), float(cbias),
+            _ptr(tau, "tau", _F32, dev, (N,)), _ptr(c_out, "c_out", _F32, dev, (B, N)),
+            B, N, V, Vd, r, ws.data_ptr(), ws.numel(), _stream(logits)))
+        return draft_tokens, log_z, c_out
     _check("dspark_markov_sample", load().dspark_markov_sample(
         _ptr(logits, "logits", _F32, dev), _ptr(w1, "w1", _BF16, dev),
         _ptr(w2, "w2", _BF16, dev, (Vd, r)), _ptr(d2t, "d2t", _I64, dev, (Vd,)),
@@ -303,21 +333,15 @@ def verify_coupled(target: torch.Tensor, draft_tokens: torch.Tensor, inv_map: Op
     return accepted, out_tokens
 
 
-def confidence(hidden: torch.Tensor, w1: torch.Tensor, draft_tokens: torch.Tensor, anchor: torch.Tensor,
-               w: torch.Tensor, bias: float, tau: torch.Tensor, c_out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Confidence head.  hidden [B*N, H] bf16, w1 [V, r] bf16, w [H + r] bf16, tau [N].  Returns c [B, N]."""
-    B, N = draft_tokens.shape
-    H = hidden.shape[1]
-    V, r = w1.shape
-    dev = hidden.device
-    if c_out is None:
-        c_out = torch.empty((B, N), dtype=torch.float32, device=dev)
-    _check("dspark_confidence", load().dspark_confidence(
-        _ptr(hidden, "hidden", _BF16, dev, (B * N, H)), _ptr(w1, "w1", _BF16, dev, (V, r)),
-        _ptr(draft_tokens, "draft_tokens", _I32, dev, (B, N)), _ptr(anchor, "anchor", _I32, dev, (B,)),
-        _ptr(w, "w", _BF16, dev, (H + r,)), float(bias), _ptr(tau, "tau", _F32, dev, (N,)),
-        _ptr(c_out, "c_out", _F32, dev, (B, N)), B, N, H, V, r, _stream(hidden)))
-    return c_out
+def advance(accepted: torch.Tensor, out_tokens: torch.Tensor, anchor: torch.Tensor,
+            emitted: Optional[torch.Tensor] = None) -> None:
+    """End of a round: anchor[b] = out_tokens[b, accepted[b]]; emitted[b] += accepted[b] + 1."""
+    B, N1 = out_tokens.shape
+    dev = out_tokens.device
+    _check("dspark_advance", load().dspark_advance(
+        _ptr(accepted, "accepted", _I32, dev, (B,)), _ptr(out_tokens, "out_tokens", _I32, dev, (B, N1)),
+        _ptr(anchor, "anchor", _I32, dev, (B,)), _ptr(emitted, "emitted", (torch.int64,), dev, (B,)),
+        B, N1 - 1, _stream(out_tokens)))
 
 
 def choose_k(survival: torch.Tensor, sps: torch.Tensor, k_out: Optional[torch.Tensor] = None,

@@ -86,8 +86,25 @@ dspark_status dspark_draft_logits(const uint16_t* hidden, const uint16_t* lm_hea
   REQUIRE_PTR16(hidden, "hidden");
   REQUIRE_PTR16(lm_head, "lm_head");
   REQUIRE_PTR(logits, "logits");
-  return hip_status(dspark::launch_draft_logits(hidden, lm_head, logits, M, H, Vd, (hipStream_t)stream),
+  return hip_status(dspark::launch_draft_logits(hidden, lm_head, logits, M, H, Vd, nullptr, nullptr,
+                                                (hipStream_t)stream),
                     "draft_logits");
+}
+
+dspark_status dspark_draft_logits_conf(const uint16_t* hidden, const uint16_t* lm_head, const uint16_t* w_h,
+                                       float* logits, float* h_dot, int M, int H, int Vd, void* stream) {
+  REQUIRE(M >= 0, DSPARK_ERR_INVALID, "M must be >= 0 (got %d)", M);
+  REQUIRE(H > 0 && H % 8 == 0, DSPARK_ERR_INVALID, "H must be a positive multiple of 8 (got %d)", H);
+  REQUIRE(Vd > 0, DSPARK_ERR_INVALID, "Vd must be > 0 (got %d)", Vd);
+  if (M == 0) return ok();
+  REQUIRE((int64_t)M * (Vd + 1) < ((int64_t)1 << 40), DSPARK_ERR_UNSUPPORTED, "M * Vd too large");
+  REQUIRE_PTR16(hidden, "hidden");
+  REQUIRE_PTR16(lm_head, "lm_head");
+  REQUIRE_PTR16(w_h, "w_h");
+  REQUIRE_PTR(logits, "logits");
+  REQUIRE_PTR(h_dot, "h_dot");
+  return hip_status(dspark::launch_draft_logits(hidden, lm_head, logits, M, H, Vd, w_h, h_dot, (hipStream_t)stream),
+                    "draft_logits_conf");
 }
 
 size_t dspark_markov_workspace_size(int B, int N, int Vd, int r) {
@@ -95,10 +112,13 @@ size_t dspark_markov_workspace_size(int B, int N, int Vd, int r) {
   return dspark::plan_markov(B, N, Vd, r, 0).partial_bytes;
 }
 
-dspark_status dspark_markov_sample(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
-                                   const int32_t* anchor, const float* temperature, const uint32_t* request_id,
-                                   uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,
-                                   int r, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+dspark_status markov_checked(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
+                             const int32_t* anchor, const float* temperature, const uint32_t* request_id,
+                             uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd, int r,
+                             void* workspace, size_t workspace_bytes, const dspark::ConfArgs& conf, void* stream) {
   REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);
   REQUIRE(B <= DSPARK_MAX_B, DSPARK_ERR_UNSUPPORTED, "B must be <= %d (got %d)", DSPARK_MAX_B, B);
   REQUIRE(N >= 1, DSPARK_ERR_INVALID, "N must be >= 1 (got %d)", N);
@@ -125,8 +145,41 @@ dspark_status dspark_markov_sample(float* logits, const uint16_t* w1, const uint
   REQUIRE(workspace_bytes >= need, DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
           need);
   return hip_status(dspark::launch_markov_sample(logits, w1, w2, d2t, anchor, temperature, request_id, seed,
-                                                 draft_tokens, log_z, B, N, V, Vd, r, workspace, (hipStream_t)stream),
-                    "markov_sample");
+                                                 draft_tokens, log_z, B, N, V, Vd, r, workspace, conf,
+                                                 (hipStream_t)stream),
+                    conf.out ? "markov_sample_conf" : "markov_sample");
+}
+}  // namespace
+
+extern "C" {
+
+dspark_status dspark_markov_sample(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
+                                   const int32_t* anchor, const float* temperature, const uint32_t* request_id,
+                                   uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,
+                                   int r, void* workspace, size_t workspace_bytes, void* stream) {
+  return markov_checked(logits, w1, w2, d2t, anchor, temperature, request_id, seed, draft_tokens, log_z, B, N, V, Vd,
+                        r, workspace, workspace_bytes, dspark::ConfArgs{}, stream);
+}
+
+dspark_status dspark_markov_sample_conf(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
+                                        const int32_t* anchor, const float* temperature,
+                                        const uint32_t* request_id, uint64_t seed, int32_t* draft_tokens,
+                                        float* log_z, const float* h_dot, const uint16_t* w_e, float conf_bias,
+                                        const float* tau, float* c_out, int B, int N, int V, int Vd, int r,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE_PTR(h_dot, "h_dot");
+  REQUIRE_PTR16(w_e, "w_e");
+  REQUIRE_PTR(tau, "tau");
+  REQUIRE_PTR(c_out, "c_out");
+  REQUIRE(std::isfinite(conf_bias), DSPARK_ERR_INVALID, "conf_bias must be finite");
+  dspark::ConfArgs conf;
+  conf.hdot = h_dot;
+  conf.we = w_e;
+  conf.bias = conf_bias;
+  conf.tau = tau;
+  conf.out = c_out;
+  return markov_checked(logits, w1, w2, d2t, anchor, temperature, request_id, seed, draft_tokens, log_z, B, N, V, Vd,
+                        r, workspace, workspace_bytes, conf, stream);
 }
 
 dspark_status dspark_markov_check(void* stream) {
@@ -283,26 +336,17 @@ dspark_status dspark_admit(const float* cond_accept, int B, int N, int K, float*
   return hip_status(dspark::launch_admit(cond_accept, B, N, K, survival, admit_len, (hipStream_t)stream), "admit");
 }
 
-dspark_status dspark_confidence(const uint16_t* hidden, const uint16_t* w1, const int32_t* draft_tokens,
-                                const int32_t* anchor, const uint16_t* w, float bias, const float* tau,
-                                float* c_out, int B, int N, int H, int V, int r, void* stream) {
+dspark_status dspark_advance(const int32_t* accepted, const int32_t* out_tokens, int32_t* anchor, int64_t* emitted,
+                             int B, int N, void* stream) {
   REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);
   REQUIRE(B <= DSPARK_MAX_B, DSPARK_ERR_UNSUPPORTED, "B must be <= %d (got %d)", DSPARK_MAX_B, B);
-  REQUIRE(N >= 1 && N <= DSPARK_MAX_N, DSPARK_ERR_INVALID, "N must be in [1, %d] (got %d)", DSPARK_MAX_N, N);
-  REQUIRE(H > 0 && H % 8 == 0, DSPARK_ERR_INVALID, "H must be a positive multiple of 8 (got %d)", H);
-  REQUIRE(r >= 8 && r % 8 == 0, DSPARK_ERR_INVALID, "r must be a positive multiple of 8 (got %d)", r);
-  REQUIRE(V > 0, DSPARK_ERR_INVALID, "V must be positive (got %d)", V);
-  REQUIRE(std::isfinite(bias), DSPARK_ERR_INVALID, "bias must be finite");
-  REQUIRE_PTR16(hidden, "hidden");
-  REQUIRE_PTR16(w1, "w1");
-  REQUIRE_PTR(draft_tokens, "draft_tokens");
+  REQUIRE(N >= 1, DSPARK_ERR_INVALID, "N must be >= 1 (got %d)", N);
+  REQUIRE(N <= DSPARK_MAX_N, DSPARK_ERR_UNSUPPORTED, "N must be <= %d (got %d)", DSPARK_MAX_N, N);
+  REQUIRE_PTR(accepted, "accepted");
+  REQUIRE_PTR(out_tokens, "out_tokens");
   REQUIRE_PTR(anchor, "anchor");
-  REQUIRE_PTR16(w, "w");
-  REQUIRE_PTR(tau, "tau");
-  REQUIRE_PTR(c_out, "c_out");
-  return hip_status(dspark::launch_confidence(hidden, w1, draft_tokens, anchor, w, bias, tau, c_out, B, N, H, V, r,
-                                              (hipStream_t)stream),
-                    "confidence");
+  return hip_status(dspark::launch_advance(accepted, out_tokens, anchor, emitted, B, N, (hipStream_t)stream),
+                    "advance");
 }
 
 dspark_status dspark_choose_k(const float* survival, int B, int N, const float* sps, int S, int32_t* k_out,

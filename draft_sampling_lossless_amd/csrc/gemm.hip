@@ -21,6 +21,10 @@
 //    fragments.  Both MFMA tilings take a grouped tile order (8 row tiles at a
 //    time), XCD by XCD.
 //
+// Optional extra row (the confidence head's hidden-state weights): with `wx` set, the
+// LM head is read as Vd + 1 rows, row Vd being wx, and output column Vd goes to
+// xout[m] instead of the logits.  Every tiling handles it as one more vocabulary row.
+//
 // MFMA 16x16x32 fragment layout (64 lanes, lane = 16 * g + n):
 //   A: lane holds 8 consecutive k of row n;  B: 8 consecutive k of column n;
 //   the k block of a lane is 8 * g within each 32-wide k step (the same mapping
@@ -39,16 +43,29 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
 
+// row j of the LM head extended by the extra row: j < Vd: lm_head row j; j == Vd: wx
+__device__ __forceinline__ const uint16_t* head_row(const uint16_t* W, const uint16_t* wx, int j, int Vd, int H) {
+  return j < Vd ? W + (size_t)j * H : wx;
+}
+
+// output column j of row m: the logits, or the extra row's output
+__device__ __forceinline__ void put_out(float* C, float* xout, int m, int j, int Vd, float v) {
+  if (j < Vd) C[(size_t)m * Vd + j] = v;
+  else xout[m] = v;
+}
+
 // ------------------------------------------------------------------ skinny
 
 template <int FR, int MT>
 __global__ __launch_bounds__(256) void k1_skinny(const uint16_t* __restrict__ A,
                                                  const uint16_t* __restrict__ W,
-                                                 float* __restrict__ C, int M, int H, int Vd) {
+                                                 float* __restrict__ C, int M, int H, int Vd,
+                                                 const uint16_t* __restrict__ wx, float* __restrict__ xout) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int Vt = Vd + (wx ? 1 : 0);
   const int j0 = wave * (16 * FR);
-  if (j0 >= Vd) return;  // whole wave
+  if (j0 >= Vt) return;  // whole wave
   const int n = lane & 15, g = lane >> 4;
 
   const uint16_t* wrow[FR];
@@ -56,8 +73,8 @@ __global__ __launch_bounds__(256) void k1_skinny(const uint16_t* __restrict__ A,
 #pragma unroll
   for (int f = 0; f < FR; ++f) {
     const int j = j0 + 16 * f + n;
-    wok[f] = j < Vd;
-    wrow[f] = W + (size_t)(wok[f] ? j : 0) * H;
+    wok[f] = j < Vt;
+    wrow[f] = head_row(W, wx, wok[f] ? j : 0, Vd, H);
   }
   const uint16_t* arow[MT];
   bool aok[MT];
@@ -101,11 +118,11 @@ __global__ __launch_bounds__(256) void k1_skinny(const uint16_t* __restrict__ A,
 #pragma unroll
     for (int f = 0; f < FR; ++f) {
       const int j = j0 + 16 * f + n;
-      if (j >= Vd) continue;
+      if (j >= Vt) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * t + 4 * g + i;
-        if (m < M) C[(size_t)m * Vd + j] = acc[t][f][i];
+        if (m < M) put_out(C, xout, m, j, Vd, acc[t][f][i]);
       }
     }
 }
@@ -120,7 +137,8 @@ constexpr int SFIXED = SNS * SSTAGE + 2 * SRED * 4;  // ring + two partial-sum b
 constexpr int SOUT_MAX = 96 * 1024;           // bytes of outputs a workgroup may hold in LDS
 
 __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-                                                 float* __restrict__ C, int M, int H, int Vd) {
+                                                 float* __restrict__ C, int M, int H, int Vd,
+                                                 const uint16_t* __restrict__ wx, float* __restrict__ xout) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* ring = smem;
   float* red = reinterpret_cast<float*>(smem + SNS * SSTAGE);  // [2][SRED], by block parity
@@ -142,8 +160,9 @@ __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A,
   // A contiguous run of LM-head rows per workgroup (the row counts differ by at most
   // one, so no workgroup streams a whole block more than another), in 16-row blocks
   // from its first row; the last block may be partial.
-  const int r0 = (int)((long)Vd * blockIdx.x / gridDim.x);
-  const int r1 = (int)((long)Vd * (blockIdx.x + 1) / gridDim.x);
+  const int Vt = Vd + (wx ? 1 : 0);  // rows, with the extra one
+  const int r0 = (int)((long)Vt * blockIdx.x / gridDim.x);
+  const int r1 = (int)((long)Vt * (blockIdx.x + 1) / gridDim.x);
   const int nb = (r1 - r0 + 15) / 16, L = 16 * nb;
   const int T = nb * spb;  // stages this workgroup consumes
   // stage t: block t / spb, k range (t % spb) * 512 .. +512; wave w loads rows
@@ -157,7 +176,7 @@ __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A,
     for (int q = 0; q < 4; ++q) {
       const int row = wave + 4 * q;
       const int j = min(r0 + blk * 16 + row, r1 - 1);
-      __builtin_amdgcn_global_load_lds(W + (size_t)j * H + kst * 512 + lane * 8, base + row * SROW, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(head_row(W, wx, j, Vd, H) + kst * 512 + lane * 8, base + row * SROW, 16, 0, 0);
     }
   };
   // a finished block: wave w adds the four waves' partial sums of output rows
@@ -208,7 +227,7 @@ __global__ __launch_bounds__(256) void k1_stream(const uint16_t* __restrict__ A,
   // the outputs leave only after the whole stream: a contiguous run of each output
   // row (writes interleaved with the stream cost it several percent)
   for (int m = 0; m < M; ++m)
-    for (int x = tid; x < r1 - r0; x += 256) C[(size_t)m * Vd + r0 + x] = outl[m * L + x];
+    for (int x = tid; x < r1 - r0; x += 256) put_out(C, xout, m, r0 + x, Vd, outl[m * L + x]);
 }
 
 size_t k1_stream_lds(int M, int Vd, int grid) {
@@ -234,15 +253,18 @@ int cu_count() {
 constexpr int TBM = 128, TBN = 128, TBK = 64;
 constexpr int TLDS_ROW = TBK * 2 + 16;  // bytes per LDS row (16-byte pad)
 
+// rows row0 .. row0+127 of a matrix of nrows rows: row gr < nsrc from src, row nsrc
+// (when nrows > nsrc) from the extra row wx
 __device__ __forceinline__ void tile_global_load(uint4 (&regs)[4], const uint16_t* __restrict__ src,
-                                                 int row0, int nrows, int k0, int H, int tid) {
+                                                 const uint16_t* __restrict__ wx, int row0, int nsrc, int nrows,
+                                                 int k0, int H, int tid) {
   // 128 rows x 64 bf16 = 1024 chunks of 16 bytes; thread takes chunks tid + 256 * p
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int c = tid + 256 * p;
     const int row = c >> 3, col = (c & 7) * 8;
     const int gr = row0 + row, gk = k0 + col;
-    regs[p] = (gr < nrows && gk < H) ? *reinterpret_cast<const uint4*>(src + (size_t)gr * H + gk)
+    regs[p] = (gr < nrows && gk < H) ? *reinterpret_cast<const uint4*>(head_row(src, wx, gr, nsrc, H) + gk)
                                      : make_uint4(0, 0, 0, 0);
   }
 }
@@ -258,7 +280,8 @@ __device__ __forceinline__ void tile_lds_store(char* lds, const uint4 (&regs)[4]
 
 __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                 float* __restrict__ C, int M, int H, int Vd, int mtiles,
-                                                int ntiles) {
+                                                int ntiles, const uint16_t* __restrict__ wx,
+                                                float* __restrict__ xout) {
   __shared__ __attribute__((aligned(16))) char lds[2][2][TBM * TLDS_ROW];  // [buf][A|W]
   // XCD-aware, grouped order: blocks are dispatched round-robin over 8 XCDs; each
   // XCD takes a contiguous run of the linear tile order, and that order walks groups
@@ -287,9 +310,10 @@ __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, 
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int ksteps = (H + TBK - 1) / TBK;
+  const int Vt = Vd + (wx ? 1 : 0);
   uint4 ra[4], rw[4];
-  tile_global_load(ra, A, m0, M, 0, H, tid);
-  tile_global_load(rw, W, n0, Vd, 0, H, tid);
+  tile_global_load(ra, A, nullptr, m0, M, M, 0, H, tid);
+  tile_global_load(rw, W, wx, n0, Vd, Vt, 0, H, tid);
   tile_lds_store(lds[0][0], ra, tid);
   tile_lds_store(lds[0][1], rw, tid);
   __syncthreads();
@@ -298,8 +322,8 @@ __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, 
     const int cur = ks & 1;
     const bool more = ks + 1 < ksteps;
     if (more) {
-      tile_global_load(ra, A, m0, M, (ks + 1) * TBK, H, tid);
-      tile_global_load(rw, W, n0, Vd, (ks + 1) * TBK, H, tid);
+      tile_global_load(ra, A, nullptr, m0, M, M, (ks + 1) * TBK, H, tid);
+      tile_global_load(rw, W, wx, n0, Vd, Vt, (ks + 1) * TBK, H, tid);
     }
     const char* la = lds[cur][0];
     const char* lw = lds[cur][1];
@@ -331,11 +355,11 @@ __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + wn * 64 + 16 * j + n;
-      if (col >= Vd) continue;
+      if (col >= Vt) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = m0 + wm * 64 + 16 * i + 4 * g + q;
-        if (row < M) C[(size_t)row * Vd + col] = acc[i][j][q];
+        if (row < M) put_out(C, xout, row, col, Vd, acc[i][j][q]);
       }
     }
 }
@@ -359,7 +383,8 @@ __device__ __forceinline__ void dma16_g(const uint16_t* src, char* lds_base) {
 
 __global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                               float* __restrict__ C, int M, int H, int Vd, int mtiles,
-                                              int ntiles) {
+                                              int ntiles, const uint16_t* __restrict__ wx,
+                                              float* __restrict__ xout) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int kGroupM = 4;
   const int total = mtiles * ntiles;
@@ -386,7 +411,7 @@ __global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, co
     const int r = wave * 64 + 8 * u + (lane >> 3);
     const int lg = (lane & 7) ^ ((r >> 1) & 7);
     asrc[u] = A + (size_t)min(m0 + r, M - 1) * H + lg * 8;   // rows past M: a valid row, never stored
-    wsrc[u] = W + (size_t)min(n0 + r, Vd - 1) * H + lg * 8;  // rows past Vd: likewise
+    wsrc[u] = head_row(W, wx, min(n0 + r, Vd + (wx ? 1 : 0) - 1), Vd, H) + lg * 8;  // rows past the last: likewise
   }
   auto issue = [&](int kt) {
     char* st = smem + (kt % BNS) * BSTAGE;
@@ -435,16 +460,17 @@ __global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, co
     }
   }
 
+  const int Vt = Vd + (wx ? 1 : 0);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int col = n0 + wn * 128 + 16 * j + n;
-    if (col >= Vd) continue;
+    if (col >= Vt) continue;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = m0 + wm * 128 + 16 * i + 4 * g + q;
-        if (row < M) C[(size_t)row * Vd + col] = acc[i][j][q];
+        if (row < M) put_out(C, xout, row, col, Vd, acc[i][j][q]);
       }
   }
 }
@@ -452,12 +478,13 @@ __global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, co
 }  // namespace
 
 hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, float* logits, int M, int H,
-                               int Vd, hipStream_t stream) {
+                               int Vd, const uint16_t* wx, float* xout, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  const int sgrid = min(cu_count(), (Vd + 15) / 16);
+  const int Vt = Vd + (wx ? 1 : 0);  // LM-head rows including the extra one
+  const int sgrid = min(cu_count(), (Vt + 15) / 16);
   // (at least half of a CU's 160 KB: one stream workgroup per CU, also when another
   // stream's kernels fill the chip at the same time; two on one CU would halve both)
-  const size_t slds = std::max(k1_stream_lds(M, Vd, sgrid), (size_t)(81 * 1024));
+  const size_t slds = std::max(k1_stream_lds(M, Vt, sgrid), (size_t)(81 * 1024));
   if (M <= 16 && H % 512 == 0 && H <= 4096 && slds <= SFIXED + SOUT_MAX) {
     static bool attr_set[64] = {false};
     int dev = 0;
@@ -468,17 +495,18 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
       if (e != hipSuccess) return e;
       attr_set[dev] = true;
     }
-    hipLaunchKernelGGL(k1_stream, dim3(sgrid), dim3(256), slds, stream, hidden, lm_head, logits, M, H, Vd);
+    hipLaunchKernelGGL(k1_stream, dim3(sgrid), dim3(256), slds, stream, hidden, lm_head, logits, M, H, Vd, wx,
+                       xout);
   } else if (M <= 64) {
     constexpr int FR = 2;
-    const int waves = (Vd + 16 * FR - 1) / (16 * FR);
+    const int waves = (Vt + 16 * FR - 1) / (16 * FR);
     const dim3 grid((waves + 3) / 4), block(256);
     if (M <= 16)
-      hipLaunchKernelGGL((k1_skinny<FR, 1>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd);
+      hipLaunchKernelGGL((k1_skinny<FR, 1>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd, wx, xout);
     else if (M <= 32)
-      hipLaunchKernelGGL((k1_skinny<FR, 2>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd);
+      hipLaunchKernelGGL((k1_skinny<FR, 2>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd, wx, xout);
     else
-      hipLaunchKernelGGL((k1_skinny<FR, 4>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd);
+      hipLaunchKernelGGL((k1_skinny<FR, 4>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd, wx, xout);
   } else if (H % BBK == 0) {
     static bool attr_set[64] = {false};
     int dev = 0;
@@ -489,16 +517,17 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
       if (e != hipSuccess) return e;
       attr_set[dev] = true;
     }
-    const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vd + BBN - 1) / BBN;
+    const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vt + BBN - 1) / BBN;
     const int per_xcd = (mtiles * ntiles + 7) / 8;
     hipLaunchKernelGGL(k1_big, dim3(per_xcd * 8), dim3(256), BLDS, stream, hidden, lm_head, logits, M, H, Vd, mtiles,
-                       ntiles);
+                       ntiles, wx, xout);
   } else {
-    const int mtiles = (M + TBM - 1) / TBM, ntiles = (Vd + TBN - 1) / TBN;
+    const int mtiles = (M + TBM - 1) / TBM, ntiles = (Vt + TBN - 1) / TBN;
     const int total = mtiles * ntiles;
     const int per_xcd = (total + 7) / 8;
     const dim3 grid(per_xcd * 8), block(256);
-    hipLaunchKernelGGL(k1_tiled, grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd, mtiles, ntiles);
+    hipLaunchKernelGGL(k1_tiled, grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd, mtiles, ntiles, wx,
+                       xout);
   }
   return hipGetLastError();
 }

@@ -16,10 +16,21 @@ hipError_t launch_race_exponentials(uint64_t seed, uint32_t position, uint32_t r
                                     float* out, int64_t n, hipStream_t stream);
 
 // ---- stage 1
+// wx (optional, [H] bf16): one more LM-head row; its output column goes to xout [M]
 hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, float* logits, int M, int H,
-                               int Vd, hipStream_t stream);
+                               int Vd, const uint16_t* wx, float* xout, hipStream_t stream);
 
 // ---- stage 2
+// Confidence head fused into the Markov loop (all null/unused when out == nullptr):
+// c[b, k] = sigmoid((hdot[b*N + k] + we . W1[x_{k-1}] + bias) / tau[k]), x_{-1} = anchor
+struct ConfArgs {
+  const float* hdot = nullptr;    // [B*N] w_h . hidden (the draft-logit product's extra column)
+  const uint16_t* we = nullptr;   // [r] bf16
+  float bias = 0.0f;
+  const float* tau = nullptr;     // [N]
+  float* out = nullptr;           // [B, N]
+};
+
 // Few requests: one cooperative launch (markov_few.hip).
 struct FewPlan {
   bool use;            // B <= 16 and the per-workgroup W2 slice fits in LDS
@@ -33,7 +44,7 @@ FewPlan plan_markov_few(int B, int N, int Vd, int r, int cus);
 hipError_t launch_markov_few(const FewPlan& p, float* logits, const uint16_t* w1, const uint16_t* w2,
                              const int64_t* d2t, const int32_t* anchor, const float* temperature,
                              const uint32_t* request_id, uint64_t seed, int32_t* draft_tokens, float* log_z, int B,
-                             int N, int V, int Vd, int r, void* workspace, hipStream_t stream);
+                             int N, int V, int Vd, int r, void* workspace, const ConfArgs& conf, hipStream_t stream);
 
 struct MarkovPlan {
   int chunks_per_wg;   // 64-wide vocabulary chunks per workgroup, at most (per-step path)
@@ -49,7 +60,7 @@ MarkovPlan plan_markov(int B, int N, int Vd, int r, int cus);
 hipError_t launch_markov_sample(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
                                 const int32_t* anchor, const float* temperature, const uint32_t* request_id,
                                 uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,
-                                int r, void* workspace, hipStream_t stream);
+                                int r, void* workspace, const ConfArgs& conf, hipStream_t stream);
 // few-request kernel: test hooks (0 normal, 1 single workgroup, 2 forced barrier give-up)
 // and the host-side check of the device's sticky give-up word (synchronises `stream`;
 // on a give-up also resets the counter sets)
@@ -86,10 +97,9 @@ hipError_t launch_verify_coupled(const float* target, const int32_t* draft_token
                                  uint64_t seed, int32_t* accepted, int32_t* out_tokens, int B, int N, int V,
                                  void* workspace, hipStream_t stream);
 
-// ---- confidence head
-hipError_t launch_confidence(const uint16_t* hidden, const uint16_t* w1, const int32_t* draft_tokens,
-                             const int32_t* anchor, const uint16_t* w, float bias, const float* tau, float* c_out,
-                             int B, int N, int H, int V, int r, hipStream_t stream);
+// ---- end of a round: next anchors, emitted-token counts
+hipError_t launch_advance(const int32_t* accepted, const int32_t* out_tokens, int32_t* anchor, int64_t* emitted,
+                          int B, int N, hipStream_t stream);
 
 // ---- verification budget
 hipError_t launch_choose_k(const float* survival, int B, int N, const float* sps, int S, int32_t* k_out,

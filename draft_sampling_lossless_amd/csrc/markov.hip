@@ -126,7 +126,8 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
                                                    int prev_stride, const float* __restrict__ temperature,
                                                    const uint32_t* __restrict__ request_id, uint32_t key0,
                                                    uint32_t key1, MarkovPartial* __restrict__ partial, int step,
-                                                   int B, int N, int V, int Vd, int r, int nvs, int nbt) {
+                                                   int B, int N, int V, int Vd, int r, int nvs, int nbt,
+                                                   ConfArgs conf) {
   constexpr int P = 4 * KS;
   using Lay = ChunkLds<P>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -191,6 +192,22 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
       const int k = s * 32 + 8 * g;
       const uint4 v = *reinterpret_cast<const uint4*>(er + min(k, r - 8));
       efrag[s] = __builtin_bit_cast(bf16x8, k < r ? v : make_uint4(0, 0, 0, 0));
+    }
+  }
+  // confidence head of this step (first workgroup of each request tile): the embedding
+  // part w_e . W1[prev] from the fragments above, the four lanes of a request summed
+  if (conf.out != nullptr && vs == 0) {
+    float d = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int k = s * 32 + 8 * g;
+      if (k < r) d += dot_bf16x8(__builtin_bit_cast(uint4, efrag[s]), *reinterpret_cast<const uint4*>(conf.we + k));
+    }
+    d += __shfl_xor(d, 16);
+    d += __shfl_xor(d, 32);
+    if (g == 0 && lane_ok) {
+      const size_t row = (size_t)b * N + step;
+      conf.out[row] = conf_prob(conf.hdot[row], d, conf.bias, conf.tau[step]);
     }
   }
 
@@ -481,7 +498,7 @@ template <int KS, bool kReduced>
 hipError_t launch_steps(float* logits, const uint16_t* w1, const uint16_t* w2, const int32_t* tgt,
                         float* spill, const int32_t* anchor, const float* temperature, const uint32_t* request_id, uint32_t k0,
                         uint32_t k1, MarkovPartial* partial, int32_t* draft_tokens, float* log_z, int B, int N, int V,
-                        int Vd, int r, int nbt, int max_slices, hipStream_t stream) {
+                        int Vd, int r, int nbt, int max_slices, const ConfArgs& conf, hipStream_t stream) {
   const size_t lds = ChunkLds<4 * KS>::kBytes;
   const int chunks = (Vd + kChunk - 1) / kChunk;
   const int slots = std::min(kMaxSlots, resident_per_cu<KS, kReduced>(lds) * cu_count_markov());
@@ -491,7 +508,8 @@ hipError_t launch_steps(float* logits, const uint16_t* w1, const uint16_t* w2, c
     const int32_t* prev = (i == 0) ? anchor : draft_tokens + (i - 1);
     const int stride = (i == 0) ? 1 : N;
     hipLaunchKernelGGL(HIP_KERNEL_NAME(markov_step<KS, kReduced>), grid, dim3(256), lds, stream, logits, w1, w2, tgt,
-                       spill, prev, stride, temperature, request_id, k0, k1, partial, i, B, N, V, Vd, r, nvs, nbt);
+                       spill, prev, stride, temperature, request_id, k0, k1, partial, i, B, N, V, Vd, r, nvs, nbt,
+                       conf);
     hipLaunchKernelGGL(markov_merge, dim3((B + 3) / 4), dim3(256), 0, stream, partial, temperature, draft_tokens,
                        log_z, i, B, N, nvs);
   }
@@ -502,11 +520,11 @@ template <int KS>
 hipError_t launch_ks(bool reduced, float* logits, const uint16_t* w1, const uint16_t* w2, const int32_t* tgt,
                      float* spill, const int32_t* anchor, const float* temperature, const uint32_t* request_id, uint32_t k0,
                      uint32_t k1, MarkovPartial* partial, int32_t* draft_tokens, float* log_z, int B, int N, int V,
-                     int Vd, int r, int nbt, int max_slices, hipStream_t stream) {
+                     int Vd, int r, int nbt, int max_slices, const ConfArgs& conf, hipStream_t stream) {
   return reduced ? launch_steps<KS, true>(logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                                          draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, stream)
+                                          draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, conf, stream)
                  : launch_steps<KS, false>(logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                                           draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, stream);
+                                           draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, conf, stream);
 }
 
 }  // namespace
@@ -534,11 +552,11 @@ MarkovPlan plan_markov(int B, int N, int Vd, int r, int cus) {
 hipError_t launch_markov_sample(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
                                 const int32_t* anchor, const float* temperature, const uint32_t* request_id,
                                 uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,
-                                int r, void* workspace, hipStream_t stream) {
+                                int r, void* workspace, const ConfArgs& conf, hipStream_t stream) {
   const MarkovPlan p = plan_markov(B, N, Vd, r, cu_count_markov());
   if (p.few.use)
     return launch_markov_few(p.few, logits, w1, w2, d2t, anchor, temperature, request_id, seed, draft_tokens, log_z,
-                             B, N, V, Vd, r, workspace, stream);
+                             B, N, V, Vd, r, workspace, conf, stream);
   MarkovPartial* partial = static_cast<MarkovPartial*>(workspace);
   int32_t* tgt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.tgt_offset);
   float* spill = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.spill_offset);
@@ -548,16 +566,16 @@ hipError_t launch_markov_sample(float* logits, const uint16_t* w1, const uint16_
   switch (ksteps_of(r)) {
     case 1:
       return launch_ks<1>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, stream);
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, stream);
     case 2:
       return launch_ks<2>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, stream);
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, stream);
     case 4:
       return launch_ks<4>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, stream);
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, stream);
     default:
       return launch_ks<8>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, stream);
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, stream);
   }
 }
 

@@ -172,5 +172,22 @@ __device__ __forceinline__ float log_z_of(const MarkovPartial& q, float T) {
 }
 
 
+// sum of the products of eight bf16 pairs (two 16-byte pieces)
+__device__ __forceinline__ float dot_bf16x8(const uint4& a, const uint4& b) {
+  const uint32_t x[4] = {a.x, a.y, a.z, a.w}, y[4] = {b.x, b.y, b.z, b.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    s += __uint_as_float(x[q] << 16) * __uint_as_float(y[q] << 16);
+    s += __uint_as_float(x[q] & 0xFFFF0000u) * __uint_as_float(y[q] & 0xFFFF0000u);
+  }
+  return s;
+}
+
+// the confidence head's probability from its logit parts
+__device__ __forceinline__ float conf_prob(float hdot, float edot, float bias, float tau) {
+  return 1.0f / (1.0f + expf(-(hdot + edot + bias) / tau));
+}
+
 }  // namespace mk
 }  // namespace dspark

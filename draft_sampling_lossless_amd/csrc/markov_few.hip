@@ -156,6 +156,7 @@ struct FewArgs {
   FewWs ws;
   uint32_t key0, key1;
   int B, N, V, Vd, r, CH, cap, force_solo;
+  ConfArgs conf;          // fused confidence head (conf.out == nullptr: none)
   unsigned* status;       // the device's sticky error word (bit 0: a grid barrier gave up)
   int force_give_up;      // test mode: every grid barrier reports a give-up after it completes
 };
@@ -1415,10 +1416,24 @@ __global__ __launch_bounds__(256) void markov_few(FewArgs a) {
         const MarkovPartial q = wave_merge(a.ws.partD + (size_t)row * G, G, lane);
         if (lane == 0) a.log_z[row] = log_z_of(q, req_temperature(L, row / N));
       }
+      // confidence head of every position, now that the chains are final: one wave per
+      // row, w_e . W1[previous token] over 16-byte pieces
+      if (a.conf.out != nullptr)
+        for (int row = wave; row < rows; row += 4) {
+          const int b = row / N, k = row - b * N;
+          const int prev = (k == 0) ? req_anchor(L, b) : ld_i(a.draft_tokens + row - 1);
+          const uint4* er = reinterpret_cast<const uint4*>(a.w1 + (size_t)min(max(prev, 0), a.V - 1) * r);
+          const uint4* we = reinterpret_cast<const uint4*>(a.conf.we);
+          float d = 0.0f;
+          for (int p = lane; p < r / 8; p += 64) d += dot_bf16x8(er[p], we[p]);
+          d = group_sum(d, 64);
+          if (lane == 0) a.conf.out[row] = conf_prob(a.conf.hdot[row], d, a.conf.bias, a.conf.tau[k]);
+        }
     } else {
       for (int row = tid; row < rows; row += blockDim.x) {
         st_i(a.draft_tokens + row, -1);
         a.log_z[row] = __builtin_nanf("");
+        if (a.conf.out != nullptr) a.conf.out[row] = __builtin_nanf("");
       }
     }
   }
@@ -1476,7 +1491,7 @@ FewPlan plan_markov_few(int B, int N, int Vd, int r, int cus) {
 hipError_t launch_markov_few(const FewPlan& p, float* logits, const uint16_t* w1, const uint16_t* w2,
                              const int64_t* d2t, const int32_t* anchor, const float* temperature,
                              const uint32_t* request_id, uint64_t seed, int32_t* draft_tokens, float* log_z, int B,
-                             int N, int V, int Vd, int r, void* workspace, hipStream_t stream) {
+                             int N, int V, int Vd, int r, void* workspace, const ConfArgs& conf, hipStream_t stream) {
   static bool attr_set[64] = {false};
   int dev = 0;
   (void)hipGetDevice(&dev);
@@ -1497,6 +1512,7 @@ hipError_t launch_markov_few(const FewPlan& p, float* logits, const uint16_t* w1
   a.request_id = request_id;
   a.draft_tokens = draft_tokens;
   a.log_z = log_z;
+  a.conf = conf;
   a.ws.norms = reinterpret_cast<float*>(w + p.off_norms);
   a.ws.n1 = reinterpret_cast<float*>(w + p.off_n1);
   a.ws.rec = reinterpret_cast<uint64_t*>(w + p.off_rec);

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 3
+#define DSPARK_ABI_VERSION 4
 
 typedef enum dspark_status {
   DSPARK_OK = 0,
@@ -287,21 +287,46 @@ dspark_status dspark_verify_coupled(const float* target_logits, const int32_t* d
 dspark_status dspark_admit(const float* cond_accept, int B, int N, int K, float* survival,
                            int32_t* admit_len, void* stream);
 
-/* ---------------------------------------------------------------- confidence head
+/* ---------------------------------------------------------------- confidence head, fused
  * Conditional acceptance probability of each draft position [P2 §6: a linear
  * projection of the backbone hidden state plus the Markov embedding, calibrated by
  * temperature scaling per position]:
- *   c[b, k] = 1 / (1 + exp(-(w[0:H] . h[b*N + k] + w[H:H+r] . W1[x_{k-1}] + bias) / tau[k]))
- * with x_{-1} = anchor[b] (the token stage 2 starts from).  Float32 arithmetic.
- * Its output is dspark_admit's cond_accept.
- *   hidden [B*N, H] bf16 (the stage-1 input), w1 [V, r] bf16, w [H + r] bf16: device,
- *            16-byte aligned; draft_tokens [B, N] int32, anchor [B] int32,
- *            tau [N] float32 > 0, c_out [B, N] float32 out: device.
- *   H % 8 == 0, r % 8 == 0, bias finite.  Previous tokens are clamped into [0, V).
- */
-dspark_status dspark_confidence(const uint16_t* hidden, const uint16_t* w1, const int32_t* draft_tokens,
-                                const int32_t* anchor, const uint16_t* w, float bias, const float* tau,
-                                float* c_out, int B, int N, int H, int V, int r, void* stream);
+ *   c[b, k] = 1 / (1 + exp(-(w_h . h[b*N + k] + w_e . W1[x_{k-1}] + conf_bias) / tau[k]))
+ * with x_{-1} = anchor[b] (the token stage 2 starts from); its output is
+ * dspark_admit's cond_accept.  It runs inside the two stages that already read its
+ * inputs, with no launch of its own:
+ *   dspark_draft_logits_conf   stage 1 with w_h as one more LM-head row: logits as
+ *              dspark_draft_logits, plus h_dot[m] = w_h . hidden[m] (fp32 accumulation).
+ *              w_h [H] bf16, device, 16-byte aligned; h_dot [M] float32 out, device.
+ *   dspark_markov_sample_conf  stage 2 as dspark_markov_sample, plus c_out [B, N]:
+ *              each step forms w_e . W1[previous token] from the W1 row it gathers.
+ *              h_dot [B*N] float32 (from dspark_draft_logits_conf), w_e [r] bf16
+ *              (16-byte aligned), conf_bias finite, tau [N] float32 > 0, c_out [B, N]
+ *              float32 out; all device.  On a barrier give-up (dspark_markov_check)
+ *              c_out is NaN like log_z.
+ * Float32 arithmetic.  Other arguments, limits and errors as the plain calls. */
+dspark_status dspark_draft_logits_conf(const uint16_t* hidden, const uint16_t* lm_head, const uint16_t* w_h,
+                                       float* logits, float* h_dot, int M, int H, int Vd, void* stream);
+dspark_status dspark_markov_sample_conf(float* logits, const uint16_t* w1, const uint16_t* w2,
+                                        const int64_t* d2t, const int32_t* anchor,
+                                        const float* temperature, const uint32_t* request_id,
+                                        uint64_t seed, int32_t* draft_tokens, float* log_z,
+                                        const float* h_dot, const uint16_t* w_e, float conf_bias,
+                                        const float* tau, float* c_out,
+                                        int B, int N, int V, int Vd, int r,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- end of a round
+ * The next round's anchors ["DSpark 的实现和测评" §2.1: the anchor of a request is the
+ * token its previous step verified]: anchor[b] = out_tokens[b, accepted[b]], the
+ * correction or bonus token dspark_verify / dspark_verify_coupled emitted last, and,
+ * when emitted is not NULL, emitted[b] += accepted[b] + 1 (tokens emitted this round),
+ * for a multi-round driver that measures tokens per round.
+ *   accepted [B] int32 in [0, N] (clamped), out_tokens [B, N+1] int32, anchor [B]
+ *   int32 out, emitted [B] int64 in/out or NULL; device.  1 <= B <= DSPARK_MAX_B,
+ *   1 <= N <= DSPARK_MAX_N. */
+dspark_status dspark_advance(const int32_t* accepted, const int32_t* out_tokens, int32_t* anchor,
+                             int64_t* emitted, int B, int N, void* stream);
 
 /* ---------------------------------------------------------------- verification budget
  * Throughput-optimal budget K [P2 §6 (maximise expected tokens per batch times SPS at

@@ -447,6 +447,23 @@ def admit(cond_accept, K: int) -> Dict[str, np.ndarray]:
     return {"survival": s, "admit_len": admit_len, "admitted": admitted.reshape(B, N)}
 
 
+# ---------------------------------------------------------------- end of a round
+
+def advance(accepted, out_tokens, anchor, emitted=None):
+    """The next round's anchors [P1 §2.1: the anchor of a request is the token its
+    previous step verified]: anchor[b] = out_tokens[b, accepted[b]] (the correction or
+    bonus token verify emitted last); emitted[b] += accepted[b] + 1.  Returns the new
+    (anchor, emitted) arrays.
+    Pins: a hand-worked round (a rejection and a full acceptance); chaining verify's
+    greedy outputs reproduces the greedy decode of the target argmaxes.
+    """
+    acc = np.asarray(accepted, dtype=np.int64)
+    out = np.asarray(out_tokens, dtype=np.int64)
+    new_anchor = out[np.arange(acc.size), acc].astype(np.int32)
+    new_emitted = None if emitted is None else (np.asarray(emitted, dtype=np.int64) + acc + 1)
+    return new_anchor, new_emitted
+
+
 # ---------------------------------------------------------------- next rows: budget K
 
 def choose_k(survival, sps, B: Optional[int] = None) -> Dict[str, object]:

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(dspark_lib):
 
 
 def test_abi_version(dspark_lib):
-    assert dsl.abi_version() == 3
+    assert dsl.abi_version() == 4
 
 
 def _err():

@@ -543,22 +543,104 @@ def test_choose_k_scans_past_a_local_maximum_on_gpu():
 
 # ---------------------------------------------------------------- next rows: confidence head
 
-@pytest.mark.parametrize("B,N,H,V,r", [(1, 8, 4096, 151936, 64), (64, 8, 4096, 32000, 256), (5, 3, 264, 100, 8),
-                                       (256, 16, 4096, 4096, 64)])
-def test_confidence_parity(B, N, H, V, r):
-    say(f"confidence B={B} N={N} H={H} V={V} r={r}")
-    g = np.random.default_rng(B + N + H)
+@pytest.mark.parametrize("B,N,H,V,Vd,r", [
+    (1, 8, 4096, 151936, 151936, 64),    # one request: the stream GEMM, the few-request Markov kernel
+    (64, 8, 4096, 32000, 32000, 256),    # the big-tile GEMM, the per-step Markov kernel
+    (5, 3, 264, 100, 100, 8),            # H not a multiple of 64: the tiled GEMM
+    (256, 16, 4096, 4096, 4096, 64),     # Vd a multiple of 256: the extra row opens a new column tile
+    (40, 4, 512, 8192, 2048, 32),        # reduced vocabulary, skinny GEMM
+    (12, 2, 4096, 1024, 1024, 16)])      # several requests in the few-request kernel
+def test_confidence_fused_parity(B, N, H, V, Vd, r):
+    """The confidence head inside stages 1 and 2: w_h as one more LM-head row (h_dot), the
+    embedding part and the sigmoid inside the Markov loop.  Against the oracle's head on the
+    GPU's own draft tokens; the logits, tokens and log Z equal the plain calls' bit for bit."""
+    say(f"confidence fused B={B} N={N} H={H} V={V} Vd={Vd} r={r}")
+    g = np.random.default_rng(B + N + H + Vd)
     hid = synth.bf16_bits(g.normal(size=(B * N, H)).astype(np.float32))
-    w1 = synth.bf16_bits(g.normal(0, 0.5, size=(V, r)).astype(np.float32))
-    w = synth.bf16_bits(g.normal(0, 1.0 / math.sqrt(H + r), size=H + r).astype(np.float32))
-    tok = g.integers(0, V, size=(B, N)).astype(np.int32)
+    W = synth.bf16_bits(g.normal(0, 0.02, size=(Vd, H)).astype(np.float32))
+    w1 = synth.bf16_bits(g.normal(0, 0.3, size=(V, r)).astype(np.float32))
+    w2 = synth.bf16_bits(g.normal(0, 0.3, size=(Vd, r)).astype(np.float32))
+    wconf = synth.bf16_bits(g.normal(0, 1.0 / math.sqrt(H + r), size=H + r).astype(np.float32))
+    d2t = None if Vd == V else (g.permutation(V)[:Vd] - np.arange(Vd)).astype(np.int64)
     anc = g.integers(0, V, size=B).astype(np.int32)
+    temp = np.asarray([0.0, 0.7, 1.0], np.float32)[g.integers(0, 3, size=B)]
+    rid = np.arange(B, dtype=np.uint32)
     tau = g.uniform(0.7, 1.5, size=N).astype(np.float32)
-    c = host(dsl.confidence(dev(hid), dev(w1), dev(tok), dev(anc), dev(w), 0.3, dev(tau)))
-    ref = stages.confidence_head(hid, w1, tok, anc, w, 0.3, tau)
-    err = np.abs(c.astype(np.float64) - ref).max()
-    say(f"  max abs err {err:.2e}, c in [{ref.min():.3f}, {ref.max():.3f}]")
+    args = (dev(w1), dev(w2), None if d2t is None else dev(d2t), dev(anc), dev(temp), dev(rid), 99)
+    plain = dsl.draft_logits(dev(hid), dev(W))
+    logits, h_dot = dsl.draft_logits(dev(hid), dev(W), w_h=dev(wconf[:H].copy()))
+    assert torch.equal(plain, logits), "the extra LM-head row changed the logits"
+    plain = plain.view(B, N, Vd)
+    tok0, lz0 = dsl.markov_sample(plain, *args)
+    tok, lz, c = dsl.markov_sample(logits.view(B, N, Vd), *args,
+                                   conf=(h_dot, dev(wconf[H:].copy()), 0.3, dev(tau), None))
+    assert torch.equal(tok0, tok) and torch.equal(lz0, lz) and torch.equal(plain, logits.view(B, N, Vd))
+    dsl.markov_check()
+    ref = stages.confidence_head(hid, w1, host(tok), anc, wconf, 0.3, tau)
+    err = np.abs(host(c).astype(np.float64) - ref).max()
+    hd_ref = stages.bf16_decode(hid) @ stages.bf16_decode(wconf[:H])
+    hd_err = np.abs(host(h_dot).astype(np.float64) - hd_ref).max()
+    say(f"  c max abs err {err:.2e} (h_dot {hd_err:.2e}), c in [{ref.min():.3f}, {ref.max():.3f}]")
+    assert hd_err <= 2e-2
     assert err <= 1e-6
+
+
+# ---------------------------------------------------------------- end of a round
+
+def test_advance_parity():
+    B, N = 300, 7
+    g = np.random.default_rng(17)
+    acc = g.integers(0, N + 1, size=B).astype(np.int32)
+    out = g.integers(0, 151936, size=(B, N + 1)).astype(np.int32)
+    anchor = np.zeros(B, np.int32)
+    emitted = g.integers(0, 1000, size=B).astype(np.int64)
+    a_d, e_d = dev(anchor), dev(emitted)
+    dsl.advance(dev(acc), dev(out), a_d, e_d)
+    ra, re = stages.advance(acc, out, anchor, emitted)
+    assert np.array_equal(host(a_d), ra) and np.array_equal(host(e_d), re)
+
+
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("batched", dict(B=24, H=512, V=4096, Vd=4096, r=32))])
+def test_multi_round_graph(name, over):
+    """R rounds chained by advance (each drafting from the last emitted token, its own seed),
+    captured in one HIP graph: every replay equals the same rounds run eagerly, bit for bit
+    (each stage's parity against the oracle is tested on its own); every round's anchor is the
+    previous round's last emitted token; tau lies in [1, N + 1]."""
+    import bench
+    w = synth.get(name, **over)
+    R = 4
+    path = bench.Path(w, torch, dsl, synth, "rejection", False)
+    anchor0 = path.anchor.clone()
+    path.advance = True
+    eager = []
+    for q in range(R):
+        path.round_seed = q + 1
+        path.step()
+        eager.append((path.tokens.clone(), path.accepted.clone(), path.out_tokens.clone(), path.anchor.clone()))
+    em_eager = path.emitted.clone()
+    graph = torch.cuda.CUDAGraph()
+    path.anchor.copy_(anchor0)
+    path.emitted.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for q in range(R):
+            path.round_seed = q + 1
+            path.step()
+    for rep in range(2):
+        path.anchor.copy_(anchor0)
+        path.emitted.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(path.anchor, eager[-1][3]) and torch.equal(path.emitted, em_eager), f"replay {rep}"
+        assert torch.equal(path.out_tokens, eager[-1][2]) and torch.equal(path.accepted, eager[-1][1])
+    # the anchors follow the verified tokens: each round's anchor is the previous round's last emitted token
+    for q in range(1, R):
+        prev_acc, prev_out = host(eager[q - 1][1]), host(eager[q - 1][2])
+        assert np.array_equal(host(eager[q - 1][3]), prev_out[np.arange(w.B), prev_acc])
+    tau = host(em_eager).sum() / (w.B * R)
+    say(f"  tau {tau:.3f} over {R} rounds")
+    assert 1.0 <= tau <= w.N + 1
 
 
 # ------------------------------------------------------------------ whole round in a HIP graph

@@ -642,3 +642,30 @@ def test_probs_from_logits_closed_forms():
     assert stages.probs_from_logits(np.array([1.0, 5.0, 5.0, 2.0], np.float32), 0.0).tolist() == [0, 1, 0, 0]
     # the draft distribution at T = 0 is the point mass on the drafted entry, whatever the logits
     assert stages.draft_probs(np.array([9.0, 1.0, 0.0], np.float32), 0.0, 2).tolist() == [0, 0, 1]
+
+
+# ---------------------------------------------------------------- end of a round
+
+def test_advance_hand_worked():
+    # request 0 rejected at position 2 (correction 77); request 1 accepted all 3 (bonus 9)
+    accepted = np.array([2, 3])
+    out = np.array([[5, 6, 77, -1], [1, 2, 3, 9]])
+    anchor, emitted = stages.advance(accepted, out, np.array([0, 0]), np.array([10, 0]))
+    assert anchor.tolist() == [77, 9] and emitted.tolist() == [13, 4]
+
+
+def test_advance_chains_greedy_decode():
+    # at T = 0 with draft = target rows, chaining verify and advance emits exactly the target's
+    # greedy decode: every round accepts all N drafts and adds the bonus argmax
+    V, N, R = 16, 3, 4
+    g = np.random.default_rng(3)
+    tgt = g.normal(size=(R, N + 1, V)).astype(np.float32)
+    anchor, emitted, decoded = np.array([0]), np.array([0]), []
+    for rnd in range(R):
+        drafts = tgt[rnd, :N].argmax(axis=1)[None].astype(np.int32)
+        res = stages.verify("logits", tgt[rnd][None], tgt[rnd, :N][None], drafts, None, None, [0.0], [0], seed=rnd)
+        decoded += res["out_tokens"][0, :res["accepted"][0] + 1].tolist()
+        anchor, emitted = stages.advance(res["accepted"], res["out_tokens"], anchor, emitted)
+        assert anchor[0] == tgt[rnd, N].argmax()
+    assert decoded == [int(t) for rnd in range(R) for t in tgt[rnd].argmax(axis=1)]
+    assert emitted[0] == R * (N + 1)
