@@ -220,17 +220,22 @@ class StageTimer:
     """HIP event pairs around each stage, recorded on torch's current stream (the
     stream the binding launches on); durations are read after a synchronisation."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, only=None):
         self.torch = torch
+        self.only = only        # stage names to time (None: every stage)
         self.pairs = {}
         self.open = {}
 
     def begin(self, name):
+        if self.only is not None and name not in self.only:
+            return
         e = self.torch.cuda.Event(enable_timing=True)
         e.record()
         self.open[name] = e
 
     def end(self, name):
+        if name not in self.open:
+            return
         e = self.torch.cuda.Event(enable_timing=True)
         e.record()
         self.pairs.setdefault(name, []).append((self.open.pop(name), e))
@@ -457,23 +462,27 @@ def run(args, w, path, torch):
             path.step()
     torch.cuda.synchronize()
 
-    # timed region: K steps; eager steps carry HIP event pairs around every stage
-    timer = StageTimer(torch) if graph is None else None
+    # timed region: K steps; eager steps carry one HIP event pair, around the dominant
+    # kernel (the draft-logit product) -- events around every stage would add their own
+    # cost to a round that lasts a fraction of a millisecond
+    live = StageTimer(torch, only={"draft_logits"}) if graph is None else None
     t0 = time.perf_counter()
     for _ in range(args.steps):
         if graph is not None:
             graph.replay()
         else:
-            path.step(timer)
+            path.step(live)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    if timer is None:       # graph replay: stage times from eager rounds after the timed region
-        timer = StageTimer(torch)
-        for _ in range(max(5, min(args.steps, 50))):
-            path.step(timer)
-        torch.cuda.synchronize()
+    # every stage's time from eager rounds after the timed region
+    timer = StageTimer(torch)
+    for _ in range(max(5, min(args.steps, 50))):
+        path.step(timer)
+    torch.cuda.synchronize()
     stage_ms = timer.mean_ms()
+    if live is not None:
+        stage_ms["draft_logits_live"] = live.mean_ms()["draft_logits"]
 
     cold_ms = None
     if not args.no_cold:
@@ -489,7 +498,7 @@ def run(args, w, path, torch):
     positions = w.B * w.N
     value = positions / (ms_per_step * 1e-3)
     k2_bytes, k3_bytes = stage_bytes(w, path.admit_len.cpu().numpy(), path.coupled)
-    roof = k1_roofline(w, stage_ms["draft_logits"])
+    roof = k1_roofline(w, stage_ms.get("draft_logits_live", stage_ms["draft_logits"]))
     if cold_ms:
         _, flops = k1_work(w)
         roof["frac_cold"] = round(flops / (cold_ms["draft_logits"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4) \
