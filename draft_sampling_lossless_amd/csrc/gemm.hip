@@ -372,7 +372,14 @@ __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, 
 // fragments for 128 MFMAs, half the LDS bytes per MFMA of 64 x 64 wave tiles, and one
 // barrier covers 128 MFMAs.  LDS row = 64 k = eight 16-byte pieces; logical piece q
 // of row r sits at piece q ^ ((r >> 1) & 7), so the 16 rows one fragment reads at a k
-// offset fall into 16 distinct bank groups.  Requires H % 64 == 0.
+// offset fall into 16 distinct bank groups.  Within a half step the eight LM-head
+// fragments are read first and the hidden-row fragments stream two ahead of the MFMAs
+// that use them.  The LM-head fragment is the MFMA's first operand, so a lane's four
+// accumulators are four adjacent output columns of one row.  The epilogue stages each
+// wave's 128 x 128 fp32 block through the (then idle) operand ring in two halves and
+// stores whole 512-byte row pieces: storing 16-lane 64-byte pieces straight from the
+// accumulators left the output write exposed for ~12% of the launch at the admission
+// shape.  Requires H % 64 == 0.
 constexpr int BBM = 256, BBN = 256, BBK = 64, BNS = 2;
 constexpr int BSTAGE = (BBM + BBN) * BBK * 2;  // 64 KB
 constexpr int BLDS = BNS * BSTAGE;             // 128 KB
@@ -443,35 +450,61 @@ __global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, co
     const char* st = smem + (kt % BNS) * BSTAGE;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      // all 16 fragment reads of the half step first (one LDS latency per half step)
       const int pc = ((4 * s + g) ^ swz) * 16;
-      bf16x8 af[8], bf[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + arow + i * 16 * 128 + pc));
+      auto afrag = [&](int i) {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + arow + i * 16 * 128 + pc));
+      };
+      bf16x8 bf[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + brow + j * 16 * 128 + pc));
+      bf16x8 acur = afrag(0), anext = afrag(1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i) {
+        // fragment i + 2 goes out before the eight MFMAs of fragment i
+        bf16x8 afar = anext;
+        if (i < 6) afar = afrag(i + 2);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], acur, acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        acur = anext;
+        anext = afar;
+      }
     }
   }
 
+  // acc[i][j][q] = C[row 16 i + n][column 16 j + 4 g + q] of the wave's block.  Every
+  // wave has finished reading the ring; each takes 32 KB of it (64 rows x 512 B, piece
+  // p of row r at p ^ (r & 7)) and writes its block in two halves of 64 rows.
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  char* stage = smem + wave * 32768;
   const int Vt = Vd + (wx ? 1 : 0);
+  // whole float4 stores need 16-byte aligned rows
+  const bool vec = (Vd % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int col = n0 + wn * 128 + 16 * j + n;
-    if (col >= Vt) continue;
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = m0 + wm * 128 + 16 * i + 4 * g + q;
-        if (row < M) put_out(C, xout, row, col, Vd, acc[i][j][q]);
+      for (int j = 0; j < 8; ++j) {
+        const int r = 16 * i + n, p = 4 * j + g;
+        *reinterpret_cast<floatx4*>(stage + r * 512 + ((p ^ (r & 7)) * 16)) = acc[4 * h + i][j];
       }
+#pragma unroll 4
+    for (int t = 0; t < 32; ++t) {
+      const int r = 2 * t + (lane >> 5), p = lane & 31;
+      const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * 512 + ((p ^ (r & 7)) * 16));
+      const int row = m0 + wm * 128 + 64 * h + r, col = n0 + wn * 128 + 4 * p;
+      if (row >= M || col >= Vt) continue;
+      if (vec && col + 3 < Vd) {
+        *reinterpret_cast<floatx4*>(C + (size_t)row * Vd + col) = v;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (col + q < Vt) put_out(C, xout, row, col + q, Vd, v[q]);
+      }
+    }
   }
 }
 

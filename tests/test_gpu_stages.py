@@ -60,7 +60,10 @@ def test_race_exponentials_bit_exact(n, pos, req, tag):
                                     (8, 4096, 20000), (3, 4096, 20004), (16, 4096, 12300),
                                     # the stream kernel's LDS output buffer exactly full (96 KB per
                                     # workgroup at 256 CUs), and one size past it (the skinny kernel)
-                                    (16, 512, 393216), (16, 512, 400000)])
+                                    (16, 512, 393216), (16, 512, 400000),
+                                    # big tiles with Vd % 4 = 1, 2, 3: rows of the output not
+                                    # 16-byte aligned, the epilogue's scalar stores
+                                    (130, 128, 1001), (260, 256, 1002), (333, 192, 771)])
 def test_draft_logits_small(M, H, Vd):
     say(f"draft_logits M={M} H={H} Vd={Vd}")
     g = np.random.default_rng(M * 7 + H)
