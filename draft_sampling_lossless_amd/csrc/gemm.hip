@@ -367,18 +367,17 @@ __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, 
 // ------------------------------------------------------------------ big tiles
 
 // 256 x 256 output tiles, BK = 64, a two-stage LDS ring filled by global->LDS DMA
-// (every load instruction moves 8 rows x 128 B), four waves of 128 x 128 (8 x 8
-// fragments of 16x16, accumulators in AGPRs).  Per 64-k step a wave reads 32 KB of
-// fragments for 128 MFMAs, half the LDS bytes per MFMA of 64 x 64 wave tiles, and one
-// barrier covers 128 MFMAs.  LDS row = 64 k = eight 16-byte pieces; logical piece q
-// of row r sits at piece q ^ ((r >> 1) & 7), so the 16 rows one fragment reads at a k
-// offset fall into 16 distinct bank groups.  Within a half step the eight LM-head
-// fragments are read first and the hidden-row fragments stream two ahead of the MFMAs
-// that use them.  The LM-head fragment is the MFMA's first operand, so a lane's four
-// accumulators are four adjacent output columns of one row.  The epilogue stages each
-// wave's 128 x 128 fp32 block through the (then idle) operand ring in two halves and
-// stores whole 512-byte row pieces: storing 16-lane 64-byte pieces straight from the
-// accumulators left the output write exposed for ~12% of the launch at the admission
+// (every load instruction moves 8 rows x 128 B).  Eight waves, two per SIMD, each
+// computing 128 hidden rows x 64 LM-head rows (8 x 4 fragments of 16x16, 128
+// accumulators): while one wave of a SIMD waits on its fragment reads or the barrier,
+// the other's MFMAs run.  LDS row = 64 k = eight 16-byte pieces; logical piece q of row
+// r sits at piece q ^ ((r >> 1) & 7), so the 16 rows one fragment reads at a k offset
+// fall into 16 distinct bank groups.  The LM-head fragment is the MFMA's first
+// operand, so a lane's four accumulators are four adjacent output columns of one row,
+// and the MFMAs of a half step run at raised wave priority.  The epilogue stages each
+// wave's 128 x 64 fp32 block through the (then idle) operand ring in two halves and
+// stores whole 256-byte row pieces: storing 16-lane 64-byte pieces straight from the
+// accumulators left the output write exposed for ~12% of a launch at the admission
 // shape.  Requires H % 64 == 0.
 constexpr int BBM = 256, BBN = 256, BBK = 64, BNS = 2;
 constexpr int BSTAGE = (BBM + BBN) * BBK * 2;  // 64 KB
@@ -388,7 +387,7 @@ __device__ __forceinline__ void dma16_g(const uint16_t* src, char* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
 }
 
-__global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+__global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                               float* __restrict__ C, int M, int H, int Vd, int mtiles,
                                               int ntiles, const uint16_t* __restrict__ wx,
                                               float* __restrict__ xout) {
@@ -405,44 +404,45 @@ __global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, co
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave & 1, wn = wave >> 1;  // hidden-row half, LM-head-row quarter
   const int n = lane & 15, g = lane >> 4;
+  const int Vt = Vd + (wx ? 1 : 0);         // LM-head rows including the extra one
 
-  // DMA: instruction u (0..7) of this wave fills A rows (and W rows) 64 wave + 8 u .. +7;
-  // lane L takes row 8 u + L / 8 of the wave's 64, physical piece L % 8, which holds
-  // logical piece (L % 8) ^ ((row >> 1) & 7), row = 64 wave + 8 u + L / 8
-  const uint16_t* asrc[8];
-  const uint16_t* wsrc[8];
+  // DMA: instruction u (0..3) of this wave fills A rows (and W rows) 32 wave + 8 u .. +7;
+  // lane L takes row 8 u + L / 8 of the wave's 32, physical piece L % 8, which holds
+  // logical piece (L % 8) ^ ((row >> 1) & 7)
+  const uint16_t* asrc[4];
+  const uint16_t* wsrc[4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int r = wave * 64 + 8 * u + (lane >> 3);
+  for (int u = 0; u < 4; ++u) {
+    const int r = wave * 32 + 8 * u + (lane >> 3);
     const int lg = (lane & 7) ^ ((r >> 1) & 7);
-    asrc[u] = A + (size_t)min(m0 + r, M - 1) * H + lg * 8;   // rows past M: a valid row, never stored
-    wsrc[u] = head_row(W, wx, min(n0 + r, Vd + (wx ? 1 : 0) - 1), Vd, H) + lg * 8;  // rows past the last: likewise
+    asrc[u] = A + (size_t)min(m0 + r, M - 1) * H + lg * 8;               // rows past M: a valid row, never stored
+    wsrc[u] = head_row(W, wx, min(n0 + r, Vt - 1), Vd, H) + lg * 8;      // rows past the last: likewise
   }
   auto issue = [&](int kt) {
     char* st = smem + (kt % BNS) * BSTAGE;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      dma16_g(asrc[u] + kt * BBK, st + (wave * 64 + 8 * u) * 128);
-      dma16_g(wsrc[u] + kt * BBK, st + BBM * 128 + (wave * 64 + 8 * u) * 128);
+    for (int u = 0; u < 4; ++u) {
+      dma16_g(asrc[u] + kt * BBK, st + (wave * 32 + 8 * u) * 128);
+      dma16_g(wsrc[u] + kt * BBK, st + BBM * 128 + (wave * 32 + 8 * u) * 128);
     }
   };
 
-  floatx4 acc[8][8];
+  floatx4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // fragment reads: row (16 i + n) of the wave's 128 rows, logical piece 4 s + g
+  // fragment reads: row (16 i + n) of the wave's rows, logical piece 4 s + g
   const int swz = (n >> 1) & 7;
-  const int arow = (wm * 128 + n) * 128, brow = BBM * 128 + (wn * 128 + n) * 128;
+  const int arow = (wm * 128 + n) * 128, brow = BBM * 128 + (wn * 64 + n) * 128;
 
   const int KT = H / BBK;
   issue(0);
   for (int kt = 0; kt < KT; ++kt) {
-    // this wave's 16 DMA instructions of stage kt are done; after the barrier every
+    // this wave's 8 DMA instructions of stage kt are done; after the barrier every
     // wave's are, and every wave has finished reading stage kt - 1, whose buffer
     // stage kt + 1 reuses
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -451,35 +451,29 @@ __global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, co
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int pc = ((4 * s + g) ^ swz) * 16;
-      auto afrag = [&](int i) {
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + arow + i * 16 * 128 + pc));
-      };
-      bf16x8 bf[8];
+      bf16x8 af[8], bf[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 4; ++j)
         bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + brow + j * 16 * 128 + pc));
-      bf16x8 acur = afrag(0), anext = afrag(1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + arow + i * 16 * 128 + pc));
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // fragment i + 2 goes out before the eight MFMAs of fragment i
-        bf16x8 afar = anext;
-        if (i < 6) afar = afrag(i + 2);
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], acur, acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        acur = anext;
-        anext = afar;
-      }
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // acc[i][j][q] = C[row 16 i + n][column 16 j + 4 g + q] of the wave's block.  Every
-  // wave has finished reading the ring; each takes 32 KB of it (64 rows x 512 B, piece
+  // wave has finished reading the ring; each takes 16 KB of it (64 rows x 256 B, piece
   // p of row r at p ^ (r & 7)) and writes its block in two halves of 64 rows.
   asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  char* stage = smem + wave * 32768;
-  const int Vt = Vd + (wx ? 1 : 0);
+  char* stage = smem + wave * 16384;
   // whole float4 stores need 16-byte aligned rows
   const bool vec = (Vd % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
 #pragma unroll
@@ -487,15 +481,15 @@ __global__ __launch_bounds__(256) void k1_big(const uint16_t* __restrict__ A, co
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         const int r = 16 * i + n, p = 4 * j + g;
-        *reinterpret_cast<floatx4*>(stage + r * 512 + ((p ^ (r & 7)) * 16)) = acc[4 * h + i][j];
+        *reinterpret_cast<floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16)) = acc[4 * h + i][j];
       }
 #pragma unroll 4
-    for (int t = 0; t < 32; ++t) {
-      const int r = 2 * t + (lane >> 5), p = lane & 31;
-      const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * 512 + ((p ^ (r & 7)) * 16));
-      const int row = m0 + wm * 128 + 64 * h + r, col = n0 + wn * 128 + 4 * p;
+    for (int t = 0; t < 16; ++t) {
+      const int r = 4 * t + (lane >> 4), p = lane & 15;
+      const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16));
+      const int row = m0 + wm * 128 + 64 * h + r, col = n0 + wn * 64 + 4 * p;
       if (row >= M || col >= Vt) continue;
       if (vec && col + 3 < Vd) {
         *reinterpret_cast<floatx4*>(C + (size_t)row * Vd + col) = v;
@@ -552,7 +546,7 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
     }
     const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vt + BBN - 1) / BBN;
     const int per_xcd = (mtiles * ntiles + 7) / 8;
-    hipLaunchKernelGGL(k1_big, dim3(per_xcd * 8), dim3(256), BLDS, stream, hidden, lm_head, logits, M, H, Vd, mtiles,
+    hipLaunchKernelGGL(k1_big, dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits, M, H, Vd, mtiles,
                        ntiles, wx, xout);
   } else {
     const int mtiles = (M + TBM - 1) / TBM, ntiles = (Vt + TBN - 1) / TBN;
