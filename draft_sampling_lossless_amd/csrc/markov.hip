@@ -15,6 +15,8 @@
 //                 (n, g) holds request n, entries 16 f + 4 g .. +3: one float4 of
 //                 base logits and one Philox block per fragment, and the four lanes
 //                 of a request read 64 contiguous bytes per load instruction.  The
+//                 processed logits go back through a per-wave LDS block and out
+//                 by rows (256 contiguous bytes per request per instruction).  The
 //                 next chunk's W2 and base logits are requested before this chunk's
 //                 epilogue runs; every lane issues the same memory operations, so
 //                 nothing waits on them until the next chunk.  Per lane a running
@@ -119,6 +121,7 @@ __device__ __forceinline__ void dma16(const uint16_t* src, char* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
 }
 
+constexpr int kTurnRow = 272, kTurnBytes = 16 * kTurnRow;  // per wave: 16 requests x 64 entries
 template <int KS, bool kReduced>
 __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, const uint16_t* __restrict__ w1,
                                                    const uint16_t* __restrict__ w2, const int32_t* __restrict__ tgt_of,
@@ -237,8 +240,18 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   // stores and the vector-memory counter stays exact.
   const int vd4 = Vd / 4;
   float4* const row4 = reinterpret_cast<float4*>(logits + ((size_t)b * N + step) * Vd);
-  float4* const st4 = lane_ok ? row4 : reinterpret_cast<float4*>(spill_row);
   float4* const spill4 = reinterpret_cast<float4*>(spill_row);
+  // stores go out by rows: store instruction k of a chunk writes requests 4 k .. 4 k + 3
+  // of the wave, lane L entries 4 (L % 16) .. +3 of request 4 k + L / 16 (256 contiguous
+  // bytes per request); the chunk's logits are turned around in this wave's LDS block
+  // (16 rows of 272 bytes: the 16 rows one fragment writes fall into 16 bank groups)
+  char* const turn = lds + Lay::kBytes + wave * kTurnBytes;
+  float4* srow[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int bq = rq0 + 4 * k + (lane >> 4);
+    srow[k] = bq < B ? reinterpret_cast<float4*>(logits + ((size_t)bq * N + step) * Vd) : nullptr;
+  }
   auto load_base = [&](int c, float4 (&bv)[4]) {
     const int j4 = c * (kChunk / 4) + g;
 #pragma unroll
@@ -301,8 +314,14 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
       l[f][1] = cb[f].y + acc[f][1];
       l[f][2] = cb[f].z + acc[f][2];
       l[f][3] = cb[f].w + acc[f][3];
-      float4* dst = (j4 + 4 * f < vd4) ? st4 + (j4 + 4 * f) : spill4 + (j4 + 4 * f);
-      *dst = make_float4(l[f][0], l[f][1], l[f][2], l[f][3]);
+      *reinterpret_cast<float4*>(turn + n * kTurnRow + (16 * f + 4 * g) * 4) = make_float4(l[f][0], l[f][1], l[f][2], l[f][3]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = lane & 15, jj4 = jc / 4 + e;
+      const float4 v = *reinterpret_cast<const float4*>(turn + (4 * k + (lane >> 4)) * kTurnRow + e * 16);
+      float4* dst = (srow[k] != nullptr && jj4 < vd4) ? srow[k] + jj4 : spill4 + jj4;
+      *dst = v;
     }
     if (jc + kChunk > Vd) {  // the last, partial chunk: entries past Vd never win nor count
 #pragma unroll
@@ -499,7 +518,7 @@ hipError_t launch_steps(float* logits, const uint16_t* w1, const uint16_t* w2, c
                         float* spill, const int32_t* anchor, const float* temperature, const uint32_t* request_id, uint32_t k0,
                         uint32_t k1, MarkovPartial* partial, int32_t* draft_tokens, float* log_z, int B, int N, int V,
                         int Vd, int r, int nbt, int max_slices, const ConfArgs& conf, hipStream_t stream) {
-  const size_t lds = ChunkLds<4 * KS>::kBytes;
+  const size_t lds = ChunkLds<4 * KS>::kBytes + 4 * kTurnBytes;
   const int chunks = (Vd + kChunk - 1) / kChunk;
   const int slots = std::min(kMaxSlots, resident_per_cu<KS, kReduced>(lds) * cu_count_markov());
   const int nvs = std::min(max_slices, markov_slices(chunks, nbt, slots));
