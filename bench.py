@@ -46,6 +46,10 @@ def parse():
     p.add_argument("--graph", action="store_true", help="replay each step as one captured HIP graph")
     p.add_argument("--verify", default="rejection", choices=("rejection", "coupled"),
                    help="stage 3 rule: rejection sampling on p_t, p_d (default) or Gumbel-coupled verification")
+    p.add_argument("--draft-rows", default="deferred", choices=("deferred", "stored"),
+                   help="deferred (default where it applies: no target map, rejection verification): stage 2 "
+                        "keeps the base logits and stage 3 rebuilds only the draft rows it reads; stored: stage 2 "
+                        "writes every processed draft row")
     p.add_argument("--round", default="path", choices=("path", "full"),
                    help="path: stages 1-4 with the workload's synthetic confidences and fixed K (default); "
                         "full: also the confidence head (its output feeds admission) and the throughput-optimal "
@@ -70,10 +74,12 @@ def src_hash(path: str) -> str:
 class Path:
     """Device buffers and the four C-ABI calls of one round."""
 
-    def __init__(self, w, torch, dsl, synth, verify_mode="rejection", full_round=False):
+    def __init__(self, w, torch, dsl, synth, verify_mode="rejection", full_round=False, draft_rows="deferred"):
         self.w, self.torch, self.dsl = w, torch, dsl
         self.coupled = verify_mode == "coupled"
         self.full = full_round
+        # deferred draft rows need the identity vocabulary map and rejection verification
+        self.deferred = draft_rows == "deferred" and not self.coupled and w.Vd == w.V
         dev = torch.device("cuda:0")
         rp = synth.request_params(w)
 
@@ -110,7 +116,9 @@ class Path:
         self.ws_markov = torch.empty(max(16, dsl.markov_workspace_size(w.B, w.N, w.Vd, w.r)),
                                      dtype=torch.uint8, device=dev)
         vws = dsl.verify_coupled_workspace_size(w.B, w.N, w.V) if self.coupled else \
+            dsl.verify_deferred_workspace_size(w.B, w.N, w.V) if self.deferred else \
             dsl.verify_workspace_size(w.B, w.N, w.V)
+        self.win = torch.empty((w.B, w.N), dtype=torch.float32, device=dev)
         self.ws_verify = torch.empty(max(16, vws), dtype=torch.uint8, device=dev)
         # target logits [B, N+1, V]: this batch's base logits (row N repeats row N-1),
         # scattered to target ids, plus N(0, sigma_b) noise -- made once, untimed
@@ -177,17 +185,27 @@ class Path:
             # the confidence head rides along: w_h as one more LM-head row, the rest in stage 2
             stage("draft_logits", lambda: dsl.draft_logits(self.hidden, self.lm_head, out=self.logits.view(w.M, w.Vd),
                                                            w_h=self.w_h, h_dot=self.h_dot))
-            stage("markov_sample", lambda: dsl.markov_sample(
-                self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, seed,
-                draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov,
-                conf=(self.h_dot, self.w_e, self.cbias, self.tau, self.c_model)))
+            cargs = (self.h_dot, self.w_e, self.cbias, self.tau, self.c_model)
+            if self.deferred:
+                stage("markov_sample", lambda: dsl.markov_sample_deferred(
+                    self.logits, self.w1, self.w2, self.anchor, self.temp, self.rid, seed, draft_tokens=self.tokens,
+                    log_z=self.logz, win_logit=self.win, workspace=self.ws_markov, conf=cargs))
+            else:
+                stage("markov_sample", lambda: dsl.markov_sample(
+                    self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, seed,
+                    draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov, conf=cargs))
             conf = self.c_model
         else:
             stage("draft_logits", lambda: dsl.draft_logits(self.hidden, self.lm_head,
                                                            out=self.logits.view(w.M, w.Vd)))
-            stage("markov_sample", lambda: dsl.markov_sample(
-                self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, seed,
-                draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov))
+            if self.deferred:
+                stage("markov_sample", lambda: dsl.markov_sample_deferred(
+                    self.logits, self.w1, self.w2, self.anchor, self.temp, self.rid, seed, draft_tokens=self.tokens,
+                    log_z=self.logz, win_logit=self.win, workspace=self.ws_markov))
+            else:
+                stage("markov_sample", lambda: dsl.markov_sample(
+                    self.logits, self.w1, self.w2, self.d2t, self.anchor, self.temp, self.rid, seed,
+                    draft_tokens=self.tokens, log_z=self.logz, workspace=self.ws_markov))
             conf = self.conf
         K = self.budget()
         if self.full:
@@ -197,6 +215,12 @@ class Path:
             stage("verify", lambda: dsl.verify_coupled(
                 self.target, self.tokens, self.inv, self.admit_len, self.temp, self.rid, seed, Vd=w.Vd,
                 accepted=self.accepted, out_tokens=self.out_tokens, workspace=self.ws_verify))
+        elif self.deferred:
+            # (stage 2's anchor: advance runs after this stage)
+            stage("verify", lambda: dsl.verify_deferred(
+                self.target, self.logits, self.logz, self.win, self.tokens, self.anchor, self.w1, self.w2,
+                self.admit_len, self.temp, self.rid, seed, accepted=self.accepted, out_tokens=self.out_tokens,
+                workspace=self.ws_verify))
         else:
             stage("verify", lambda: dsl.verify(
                 dsl.INPUT_LOGITS, self.target, self.logits, self.logz, self.tokens, self.inv, self.admit_len,
@@ -244,15 +268,19 @@ class StageTimer:
         return {k: float(np.mean([b.elapsed_time(e) for b, e in v])) for k, v in self.pairs.items()}
 
 
-def stage_bytes(w, admit_len, coupled):
+def stage_bytes(w, admit_len, coupled, deferred=False):
     """Compulsory HBM bytes of stage 2 and stage 3 per step.
     Stage 2: base logits read and processed logits written (8 B per entry), W2
-    once, one W1 row per position.  Stage 3: target rows k <= L_b (4 V each);
-    rejection sampling also reads one target and one draft row to sample from."""
-    k2 = 8 * w.B * w.N * w.Vd + 2 * w.r * w.Vd + 2 * w.r * w.B * w.N
+    once, one W1 row per position; with deferred draft rows only the read (4 B).
+    Stage 3: target rows k <= L_b (4 V each); rejection sampling also reads one
+    target and one draft row to sample from (deferred: the base row and W2 once)."""
+    per_entry = 4 if deferred else 8
+    k2 = per_entry * w.B * w.N * w.Vd + 2 * w.r * w.Vd + 2 * w.r * w.B * w.N
     k3 = 4 * w.V * int((np.asarray(admit_len) + 1).sum())
     if not coupled:
         k3 += w.B * (4 * w.V + 4 * w.Vd)
+    if deferred:
+        k3 += 2 * w.r * w.Vd
     return k2, k3
 
 
@@ -388,7 +416,7 @@ def main():
                                    "replayed as one captured graph"}))
         sys.exit(2)
     w = synth.get(args.workload)
-    path = Path(w, torch, dsl, synth, args.verify, args.round == "full")
+    path = Path(w, torch, dsl, synth, args.verify, args.round == "full", args.draft_rows)
     result = run(args, w, path, torch)
     # release the graph and every device buffer, synchronised, before the interpreter
     # (and any profiler attached to it) tears the HIP runtime down
@@ -497,7 +525,7 @@ def run(args, w, path, torch):
 
     positions = w.B * w.N
     value = positions / (ms_per_step * 1e-3)
-    k2_bytes, k3_bytes = stage_bytes(w, path.admit_len.cpu().numpy(), path.coupled)
+    k2_bytes, k3_bytes = stage_bytes(w, path.admit_len.cpu().numpy(), path.coupled, path.deferred)
     roof = k1_roofline(w, stage_ms.get("draft_logits_live", stage_ms["draft_logits"]))
     if cold_ms:
         _, flops = k1_work(w)
@@ -522,7 +550,8 @@ def run(args, w, path, torch):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "V": w.V, "Vd": w.Vd, "r": w.r,
-                   "K": w.budget, "graph": graph is not None},
+                   "K": w.budget, "graph": graph is not None,
+                   "draft_rows": "deferred" if path.deferred else "stored"},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": roof,
     }

@@ -27,6 +27,7 @@ __all__ = [
     "LIB_PATH", "load", "abi_version", "INPUT_LOGITS", "INPUT_PROBS", "DSparkError",
     "philox_blocks", "race_exponentials", "draft_logits", "markov_sample",
     "markov_workspace_size", "build_inverse_map", "verify", "verify_workspace_size", "verify_noalloc", "admit",
+    "markov_sample_deferred", "verify_deferred", "verify_deferred_workspace_size",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.so")
@@ -61,6 +62,11 @@ _SIGS = {
     "dspark_markov_sample_conf": (_c_int, [_c_void_p] * 7 + [_c_u64] + [_c_void_p] * 4 + [ctypes.c_float]
                                   + [_c_void_p] * 2 + [_c_int] * 5 + [_c_void_p, _c_size, _c_void_p]),
     "dspark_advance": (_c_int, [_c_void_p] * 4 + [_c_int] * 2 + [_c_void_p]),
+    "dspark_markov_sample_deferred": (_c_int, [_c_void_p] * 6 + [_c_u64] + [_c_void_p] * 5 + [ctypes.c_float]
+                                      + [_c_void_p] * 2 + [_c_int] * 5 + [_c_void_p, _c_size, _c_void_p]),
+    "dspark_verify_deferred_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
+    "dspark_verify_deferred": (_c_int, [_c_void_p] * 8 + [_c_int] + [_c_void_p] * 3 + [_c_u64, _c_void_p, _c_void_p]
+                               + [_c_int] * 3 + [_c_void_p, _c_size, _c_void_p]),
     "dspark_choose_k": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "dspark_admit": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p]),
 }
@@ -227,6 +233,44 @@ def markov_sample(logits: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, d2t:
     return draft_tokens, log_z
 
 
+def markov_sample_deferred(logits: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, anchor: torch.Tensor,
+                           temperature: torch.Tensor, request_id: torch.Tensor, seed: int,
+                           draft_tokens: Optional[torch.Tensor] = None, log_z: Optional[torch.Tensor] = None,
+                           win_logit: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           conf=None):
+    """Stage 2 keeping the base logits (dspark_markov_sample_deferred): logits [B, N, V] are
+    only read.  Returns (tokens, log_z, win_logit), plus c when conf = (h_dot, w_e, bias,
+    tau, c_out or None) is given."""
+    B, N, Vd = logits.shape
+    V, r = w1.shape
+    dev = logits.device
+    if draft_tokens is None:
+        draft_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if log_z is None:
+        log_z = torch.empty((B, N), dtype=torch.float32, device=dev)
+    if win_logit is None:
+        win_logit = torch.empty((B, N), dtype=torch.float32, device=dev)
+    ws = _workspace(workspace, markov_workspace_size(B, N, Vd, r), dev)
+    h_dot = w_e = tau = c_out = None
+    cbias = 0.0
+    if conf is not None:
+        h_dot, w_e, cbias, tau, c_out = conf
+        if c_out is None:
+            c_out = torch.empty((B, N), dtype=torch.float32, device=dev)
+    _check("dspark_markov_sample_deferred", load().dspark_markov_sample_deferred(
+        _ptr(logits, "logits", _F32, dev), _ptr(w1, "w1", _BF16, dev), _ptr(w2, "w2", _BF16, dev, (Vd, r)),
+        _ptr(anchor, "anchor", _I32, dev, (B,)), _ptr(temperature, "temperature", _F32, dev, (B,)),
+        _ptr(request_id, "request_id", _U32, dev, (B,)), seed,
+        _ptr(draft_tokens, "draft_tokens", _I32, dev, (B, N)), _ptr(log_z, "log_z", _F32, dev, (B, N)),
+        _ptr(win_logit, "win_logit", _F32, dev, (B, N)),
+        _ptr(h_dot, "h_dot", _F32, dev, (B * N,)), _ptr(w_e, "w_e", _BF16, dev, (r,)), float(cbias),
+        _ptr(tau, "tau", _F32, dev, (N,)), _ptr(c_out, "c_out", _F32, dev, (B, N)),
+        B, N, V, Vd, r, ws.data_ptr(), ws.numel(), _stream(logits)))
+    if conf is not None:
+        return draft_tokens, log_z, win_logit, c_out
+    return draft_tokens, log_z, win_logit
+
+
 def markov_check() -> None:
     """Synchronise the current stream and raise DSparkError if a few-request Markov
     launch since the last check gave up on a grid barrier (its outputs are -1 / NaN)."""
@@ -283,6 +327,37 @@ def verify(input_kind: int, target: torch.Tensor, draft: torch.Tensor, draft_log
         B, N, V, Vd, ws.data_ptr(), ws.numel(), _stream(target)))
     if accept_prob is not None:
         return accepted, out_tokens, accept_prob
+    return accepted, out_tokens
+
+
+def verify_deferred_workspace_size(B: int, N: int, V: int) -> int:
+    return int(load().dspark_verify_deferred_workspace_size(B, N, V))
+
+
+def verify_deferred(target: torch.Tensor, draft_base: torch.Tensor, draft_log_z: torch.Tensor,
+                    win_logit: torch.Tensor, draft_tokens: torch.Tensor, anchor: torch.Tensor, w1: torch.Tensor,
+                    w2: torch.Tensor, verify_len: Optional[torch.Tensor], temperature: torch.Tensor,
+                    request_id: torch.Tensor, seed: int, accepted: Optional[torch.Tensor] = None,
+                    out_tokens: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Stage 3 on kept base logits (dspark_verify_deferred).  draft_base [B, N, V]: each
+    request's first-rejection row is recomputed in place.  Returns (accepted, out_tokens)."""
+    B, N, V = draft_base.shape
+    r = w1.shape[1]
+    dev = target.device
+    if accepted is None:
+        accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace, verify_deferred_workspace_size(B, N, V), dev)
+    _check("dspark_verify_deferred", load().dspark_verify_deferred(
+        _ptr(target, "target", _F32, dev, (B, N + 1, V)), _ptr(draft_base, "draft_base", _F32, dev, (B, N, V)),
+        _ptr(draft_log_z, "draft_log_z", _F32, dev, (B, N)), _ptr(win_logit, "win_logit", _F32, dev, (B, N)),
+        _ptr(draft_tokens, "draft_tokens", _I32, dev, (B, N)), _ptr(anchor, "anchor", _I32, dev, (B,)),
+        _ptr(w1, "w1", _BF16, dev), _ptr(w2, "w2", _BF16, dev, (V, r)), r,
+        _ptr(verify_len, "verify_len", _I32, dev, (B,)), _ptr(temperature, "temperature", _F32, dev, (B,)),
+        _ptr(request_id, "request_id", _U32, dev, (B,)), seed,
+        _ptr(accepted, "accepted", _I32, dev, (B,)), _ptr(out_tokens, "out_tokens", _I32, dev, (B, N + 1)),
+        B, N, V, ws.data_ptr(), ws.numel(), _stream(target)))
     return accepted, out_tokens
 
 

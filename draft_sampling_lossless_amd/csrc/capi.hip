@@ -118,7 +118,8 @@ namespace {
 dspark_status markov_checked(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
                              const int32_t* anchor, const float* temperature, const uint32_t* request_id,
                              uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd, int r,
-                             void* workspace, size_t workspace_bytes, const dspark::ConfArgs& conf, void* stream) {
+                             void* workspace, size_t workspace_bytes, const dspark::ConfArgs& conf, float* win,
+                             void* stream) {
   REQUIRE(B >= 1, DSPARK_ERR_INVALID, "B must be >= 1 (got %d)", B);
   REQUIRE(B <= DSPARK_MAX_B, DSPARK_ERR_UNSUPPORTED, "B must be <= %d (got %d)", DSPARK_MAX_B, B);
   REQUIRE(N >= 1, DSPARK_ERR_INVALID, "N must be >= 1 (got %d)", N);
@@ -145,9 +146,9 @@ dspark_status markov_checked(float* logits, const uint16_t* w1, const uint16_t* 
   REQUIRE(workspace_bytes >= need, DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
           need);
   return hip_status(dspark::launch_markov_sample(logits, w1, w2, d2t, anchor, temperature, request_id, seed,
-                                                 draft_tokens, log_z, B, N, V, Vd, r, workspace, conf,
+                                                 draft_tokens, log_z, B, N, V, Vd, r, workspace, conf, win,
                                                  (hipStream_t)stream),
-                    conf.out ? "markov_sample_conf" : "markov_sample");
+                    win ? "markov_sample_deferred" : conf.out ? "markov_sample_conf" : "markov_sample");
 }
 }  // namespace
 
@@ -158,7 +159,7 @@ dspark_status dspark_markov_sample(float* logits, const uint16_t* w1, const uint
                                    uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,
                                    int r, void* workspace, size_t workspace_bytes, void* stream) {
   return markov_checked(logits, w1, w2, d2t, anchor, temperature, request_id, seed, draft_tokens, log_z, B, N, V, Vd,
-                        r, workspace, workspace_bytes, dspark::ConfArgs{}, stream);
+                        r, workspace, workspace_bytes, dspark::ConfArgs{}, nullptr, stream);
 }
 
 dspark_status dspark_markov_sample_conf(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
@@ -179,7 +180,34 @@ dspark_status dspark_markov_sample_conf(float* logits, const uint16_t* w1, const
   conf.tau = tau;
   conf.out = c_out;
   return markov_checked(logits, w1, w2, d2t, anchor, temperature, request_id, seed, draft_tokens, log_z, B, N, V, Vd,
-                        r, workspace, workspace_bytes, conf, stream);
+                        r, workspace, workspace_bytes, conf, nullptr, stream);
+}
+
+dspark_status dspark_markov_sample_deferred(float* logits, const uint16_t* w1, const uint16_t* w2,
+                                            const int32_t* anchor, const float* temperature,
+                                            const uint32_t* request_id, uint64_t seed, int32_t* draft_tokens,
+                                            float* log_z, float* win_logit, const float* h_dot, const uint16_t* w_e,
+                                            float conf_bias, const float* tau, float* c_out, int B, int N, int V,
+                                            int Vd, int r, void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(Vd == V, DSPARK_ERR_UNSUPPORTED, "markov_sample_deferred: no target map (Vd must equal V; got Vd=%d, V=%d)",
+          Vd, V);
+  REQUIRE_PTR(win_logit, "win_logit");
+  dspark::ConfArgs conf;
+  const bool with_conf = h_dot || w_e || tau || c_out;
+  if (with_conf) {
+    REQUIRE_PTR(h_dot, "h_dot (the confidence arguments are all given or all NULL)");
+    REQUIRE_PTR16(w_e, "w_e (the confidence arguments are all given or all NULL)");
+    REQUIRE_PTR(tau, "tau (the confidence arguments are all given or all NULL)");
+    REQUIRE_PTR(c_out, "c_out (the confidence arguments are all given or all NULL)");
+    REQUIRE(std::isfinite(conf_bias), DSPARK_ERR_INVALID, "conf_bias must be finite");
+    conf.hdot = h_dot;
+    conf.we = w_e;
+    conf.bias = conf_bias;
+    conf.tau = tau;
+    conf.out = c_out;
+  }
+  return markov_checked(logits, w1, w2, nullptr, anchor, temperature, request_id, seed, draft_tokens, log_z, B, N, V,
+                        Vd, r, workspace, workspace_bytes, conf, win_logit, stream);
 }
 
 dspark_status dspark_markov_check(void* stream) {
@@ -265,6 +293,43 @@ dspark_status dspark_verify(int input_kind, const float* target, const float* dr
                                           temperature, request_id, seed, accepted, out_tokens, accept_prob, B, N,
                                           V, Vd, workspace, (hipStream_t)stream),
                     "verify");
+}
+
+size_t dspark_verify_deferred_workspace_size(int B, int N, int V) {
+  if (B <= 0 || N <= 0 || V <= 0) return 0;
+  return dspark::plan_verify(B, N, V).total_bytes + dspark::verify_deferred_extra_bytes(B, V);
+}
+
+dspark_status dspark_verify_deferred(const float* target, float* draft_base, const float* draft_log_z,
+                                     const float* win_logit, const int32_t* draft_tokens, const int32_t* anchor,
+                                     const uint16_t* w1, const uint16_t* w2, int r, const int32_t* verify_len,
+                                     const float* temperature, const uint32_t* request_id, uint64_t seed,
+                                     int32_t* accepted, int32_t* out_tokens, int B, int N, int V, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  const dspark_status st = verify_args(DSPARK_INPUT_LOGITS, target, draft_base, draft_log_z, draft_tokens, nullptr,
+                                       temperature, request_id, accepted, out_tokens, B, N, V, V);
+  if (st != DSPARK_OK) return st;
+  REQUIRE_PTR(win_logit, "win_logit");
+  REQUIRE_PTR(anchor, "anchor");
+  REQUIRE_PTR16(w1, "w1");
+  REQUIRE_PTR16(w2, "w2");
+  REQUIRE(r >= 8 && r % 8 == 0, DSPARK_ERR_INVALID, "r must be a positive multiple of 8 (got %d)", r);
+  REQUIRE(r <= DSPARK_MAX_RANK, DSPARK_ERR_UNSUPPORTED, "r must be <= %d (got %d)", DSPARK_MAX_RANK, r);
+  const size_t need = dspark_verify_deferred_workspace_size(B, N, V);
+  REQUIRE(workspace != nullptr, DSPARK_ERR_WORKSPACE, "workspace must not be NULL (%zu bytes needed)", need);
+  REQUIRE(aligned16(workspace), DSPARK_ERR_INVALID, "workspace must be 16-byte aligned");
+  REQUIRE(workspace_bytes >= need, DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
+          need);
+  dspark::DeferredArgs d;
+  d.win = win_logit;
+  d.anchor = anchor;
+  d.w1 = w1;
+  d.w2 = w2;
+  d.r = r;
+  return hip_status(dspark::launch_verify_deferred(target, draft_base, draft_log_z, draft_tokens, verify_len,
+                                                   temperature, request_id, seed, accepted, out_tokens, B, N, V, d,
+                                                   workspace, (hipStream_t)stream),
+                    "verify_deferred");
 }
 
 size_t dspark_verify_noalloc_max_bytes(void) { return dspark::kVerifyScratchBytes; }

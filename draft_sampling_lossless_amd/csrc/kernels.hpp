@@ -52,6 +52,7 @@ struct MarkovPlan {
   int btiles;          // 64-request tiles
   size_t tgt_offset;   // workspace offset of the int32 target-id table (reduced vocabulary)
   size_t spill_offset; // workspace offset of the spill row (stores of entries that do not exist)
+  size_t lw_offset;    // workspace offset of the partials' winner logits (kept base logits)
   size_t partial_bytes;  // workspace bytes (the larger need of the two paths)
   FewPlan few;
 };
@@ -60,7 +61,14 @@ MarkovPlan plan_markov(int B, int N, int Vd, int r, int cus);
 hipError_t launch_markov_sample(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
                                 const int32_t* anchor, const float* temperature, const uint32_t* request_id,
                                 uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,
-                                int r, void* workspace, const ConfArgs& conf, hipStream_t stream);
+                                int r, void* workspace, const ConfArgs& conf, float* win, hipStream_t stream);
+// processed logits of one row per request (rows[b], -1: none), recomputed in place from
+// the base logits there with the previous token prev[b], exactly as the sampling pass
+// forms them; spill: markov_replay_spill_bytes(Vd) bytes of scratch
+size_t markov_replay_spill_bytes(int Vd);
+hipError_t launch_markov_replay(float* logits, const uint16_t* w1, const uint16_t* w2, const int32_t* rows,
+                                const int32_t* prev, const float* temperature, const uint32_t* request_id, int B,
+                                int N, int V, int Vd, int r, float* spill, hipStream_t stream);
 // few-request kernel: test hooks (0 normal, 1 single workgroup, 2 forced barrier give-up)
 // and the host-side check of the device's sticky give-up word (synchronises `stream`;
 // on a give-up also resets the counter sets)
@@ -82,6 +90,23 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
                          const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
                          int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
                          hipStream_t stream);
+// Logits mode on kept base logits (stage 2 run with win != nullptr): p_d of each drafted
+// token comes from win, and the processed row of each request's first rejection is
+// recomputed in place in draft_base before the sampling pass reads it.  No inverse map
+// (Vd == V), no acceptance probabilities.  workspace: plan_verify(B, N, V).total_bytes
+// + verify_deferred_extra_bytes(B, V).
+struct DeferredArgs {
+  const float* win = nullptr;       // [B, N] processed logit of each drafted token
+  const int32_t* anchor = nullptr;  // [B] token before position 0
+  const uint16_t* w1 = nullptr;     // [V, r] bf16
+  const uint16_t* w2 = nullptr;     // [Vd, r] bf16
+  int r = 0;
+};
+size_t verify_deferred_extra_bytes(int B, int V);
+hipError_t launch_verify_deferred(const float* target, float* draft_base, const float* draft_log_z,
+                                  const int32_t* draft_tokens, const int32_t* verify_len, const float* temperature,
+                                  const uint32_t* request_id, uint64_t seed, int32_t* accepted, int32_t* out_tokens,
+                                  int B, int N, int V, const DeferredArgs& d, void* workspace, hipStream_t stream);
 // launch_verify with the library's static per-device scratch array as workspace
 constexpr size_t kVerifyScratchBytes = (size_t)4 << 20;
 hipError_t launch_verify_noalloc(int input_kind, const float* target, const float* draft, const float* draft_log_z,

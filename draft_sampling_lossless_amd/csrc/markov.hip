@@ -122,7 +122,19 @@ __device__ __forceinline__ void dma16(const uint16_t* src, char* lds_base) {
 }
 
 constexpr int kTurnRow = 272, kTurnBytes = 16 * kTurnRow;  // per wave: 16 requests x 64 entries
-template <int KS, bool kReduced>
+
+// Modes of the per-step kernel.  kStore: sample and store the processed logits in
+// place.  kKeep: sample, leave the base logits untouched and record, per (request,
+// workgroup), the processed logit of the workgroup's winner (io.lw).  kReplay: store
+// the processed logits of one row per request (io.rows[b], -1: none) in place, with the
+// same chunk, fragment and MFMA sequence as the sampling modes, so they equal what
+// kStore would have stored bit for bit.
+enum StepMode { kStore = 0, kKeep = 1, kReplay = 2 };
+struct StepIO {
+  float* lw;             // kKeep: [B x nvs]
+  const int32_t* rows;   // kReplay: [B]
+};
+template <int KS, bool kReduced, int kMode>
 __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, const uint16_t* __restrict__ w1,
                                                    const uint16_t* __restrict__ w2, const int32_t* __restrict__ tgt_of,
                                                    float* __restrict__ spill_row, const int32_t* __restrict__ prev_tok,
@@ -130,7 +142,7 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
                                                    const uint32_t* __restrict__ request_id, uint32_t key0,
                                                    uint32_t key1, MarkovPartial* __restrict__ partial, int step,
                                                    int B, int N, int V, int Vd, int r, int nvs, int nbt,
-                                                   ConfArgs conf) {
+                                                   ConfArgs conf, StepIO io) {
   constexpr int P = 4 * KS;
   using Lay = ChunkLds<P>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -233,13 +245,17 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   // two blocks (or a lane with no finite key) sends the lane to an exact rescan.
   int bblk = vs * kChunk;
   bool tie = false;
+  float bl[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // kKeep: logits of the best block
 
   // This lane's logits row as float4 (Vd is a multiple of 4).  Loads clamp to the
   // row; stores of entries that do not exist (past Vd, or a lane without a request)
   // go to a spill row in the workspace, so every lane issues the same loads and
   // stores and the vector-memory counter stays exact.
   const int vd4 = Vd / 4;
-  float4* const row4 = reinterpret_cast<float4*>(logits + ((size_t)b * N + step) * Vd);
+  // the row this step reads (kReplay: the request's own row; a request without one
+  // reads row 0 and stores nothing)
+  const int rowb = (kMode == kReplay) ? max(io.rows[b], 0) : step;
+  float4* const row4 = reinterpret_cast<float4*>(logits + ((size_t)b * N + rowb) * Vd);
   float4* const spill4 = reinterpret_cast<float4*>(spill_row);
   // stores go out by rows: store instruction k of a chunk writes requests 4 k .. 4 k + 3
   // of the wave, lane L entries 4 (L % 16) .. +3 of request 4 k + L / 16 (256 contiguous
@@ -250,7 +266,8 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int bq = rq0 + 4 * k + (lane >> 4);
-    srow[k] = bq < B ? reinterpret_cast<float4*>(logits + ((size_t)bq * N + step) * Vd) : nullptr;
+    const int rq = (kMode == kReplay && bq < B) ? io.rows[bq] : step;
+    srow[k] = (bq < B && rq >= 0) ? reinterpret_cast<float4*>(logits + ((size_t)bq * N + rq) * Vd) : nullptr;
   }
   auto load_base = [&](int c, float4 (&bv)[4]) {
     const int j4 = c * (kChunk / 4) + g;
@@ -314,15 +331,20 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
       l[f][1] = cb[f].y + acc[f][1];
       l[f][2] = cb[f].z + acc[f][2];
       l[f][3] = cb[f].w + acc[f][3];
-      *reinterpret_cast<float4*>(turn + n * kTurnRow + (16 * f + 4 * g) * 4) = make_float4(l[f][0], l[f][1], l[f][2], l[f][3]);
+      if (kMode != kKeep)
+        *reinterpret_cast<float4*>(turn + n * kTurnRow + (16 * f + 4 * g) * 4) =
+            make_float4(l[f][0], l[f][1], l[f][2], l[f][3]);
     }
+    if (kMode != kKeep) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = lane & 15, jj4 = jc / 4 + e;
-      const float4 v = *reinterpret_cast<const float4*>(turn + (4 * k + (lane >> 4)) * kTurnRow + e * 16);
-      float4* dst = (srow[k] != nullptr && jj4 < vd4) ? srow[k] + jj4 : spill4 + jj4;
-      *dst = v;
+      for (int k = 0; k < 4; ++k) {
+        const int e = lane & 15, jj4 = jc / 4 + e;
+        const float4 v = *reinterpret_cast<const float4*>(turn + (4 * k + (lane >> 4)) * kTurnRow + e * 16);
+        float4* dst = (srow[k] != nullptr && jj4 < vd4) ? srow[k] + jj4 : spill4 + jj4;
+        *dst = v;
+      }
     }
+    if (kMode == kReplay) return;
     if (jc + kChunk > Vd) {  // the last, partial chunk: entries past Vd never win nor count
 #pragma unroll
       for (int f = 0; f < 4; ++f)
@@ -348,6 +370,10 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
       if (km > bkey) {
         bkey = km;
         bblk = jc + 16 * f;
+        if (kMode == kKeep) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bl[i] = l[f][i];
+        }
       }
       // one block at a time: interleaving the four blocks' Philox chains buys nothing
       // here (other waves fill the pipeline) and would hold four times the registers
@@ -364,13 +390,21 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
     chunk(c + nvs, bb, ba);
   }
 
+  if (kMode == kReplay) return;
   // the entry of the winning block: its keys again from the logits this lane stored
+  // (kKeep: from the copy in registers)
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   int btok;
+  float lwin = -INFINITY;  // kKeep: processed logit of this lane's winner
   {
     const int jb = bblk + 4 * g;
     float lv[4];
-    load_stored4(reinterpret_cast<const float*>(row4) + min(jb, Vd - 4), lv);
+    if (kMode == kKeep) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lv[i] = bl[i];
+    } else {
+      load_stored4(reinterpret_cast<const float*>(row4) + min(jb, Vd - 4), lv);
+    }
     float lg[4], y[4], key[4];
     noise(jb, lg);
     keys_of(lg, lv, y, key);
@@ -381,6 +415,10 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
       for (int i = 3; i >= 0; --i)
         if (key[i] == bkey) hit = i;
       btok = jb + hit;
+      lwin = lv[0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i)
+        if (hit == i) lwin = lv[i];
     } else {
       const int4 tv = *reinterpret_cast<const int4*>(tgt_of + min(jb, Vd - 4));
       const int t[4] = {tv.x, tv.y, tv.z, tv.w};
@@ -422,6 +460,7 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   }
 
   // merge the four lanes (g) of request n: partners n ^ 16, then n ^ 32
+  const int btok_own = btok;
   {
     uint32_t k0, k1, t0, t1, m0, m1, s0, s1;
     rows_pair(__float_as_uint(bkey), k0, k1);
@@ -444,6 +483,8 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
     state_merge(bkey, btok, bm, bs, __uint_as_float(k1), (int)t1, __uint_as_float(m1), __uint_as_float(s1));
   }
   if (g == 0 && lane_ok) partial[(size_t)b * nvs + vs] = MarkovPartial{bkey, btok, bm, bs};
+  // (the lanes of a request hold disjoint entries: exactly one of them owns the winner)
+  if (kMode == kKeep && lane_ok && btok_own == btok) io.lw[(size_t)b * nvs + vs] = lwin;
 }
 
 namespace {
@@ -451,7 +492,8 @@ namespace {
 __global__ __launch_bounds__(256) void markov_merge(const MarkovPartial* __restrict__ partial,
                                                     const float* __restrict__ temperature,
                                                     int32_t* __restrict__ draft_tokens, float* __restrict__ log_z,
-                                                    int step, int B, int N, int nvs) {
+                                                    int step, int B, int N, int nvs, const float* __restrict__ lw,
+                                                    float* __restrict__ win) {
   const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (b >= B) return;
@@ -462,6 +504,20 @@ __global__ __launch_bounds__(256) void markov_merge(const MarkovPartial* __restr
     state_merge(key, tok, m, s, q.key, q.tok, q.m, q.s);
   }
   wave_state_merge(key, tok, m, s);
+  if (win != nullptr) {
+    // the winner's processed logit, from the one partial that holds its id (the
+    // workgroups of a request cover disjoint entries)
+    float v = -INFINITY;
+    bool found = false;
+    for (int p = lane; p < nvs; p += 64)
+      if (!found && partial[(size_t)b * nvs + p].tok == tok) {
+        v = lw[(size_t)b * nvs + p];
+        found = true;
+      }
+    const uint64_t hit = __ballot(found);
+    v = __shfl(v, hit ? (int)__builtin_ctzll(hit) : 0);
+    if (lane == 0) win[(size_t)b * N + step] = v;
+  }
   if (lane == 0) {
     draft_tokens[(size_t)b * N + step] = tok;
     // T == 0: the key is the logit itself, and log Z is defined as the largest one
@@ -498,7 +554,7 @@ int markov_slices(int chunks, int nbt, int slots) {
   return std::min(chunks, per);
 }
 
-template <int KS, bool kReduced>
+template <int KS, bool kReduced, int kMode>
 int resident_per_cu(size_t lds) {
   static int cached[64] = {0};
   int dev = 0;
@@ -506,44 +562,73 @@ int resident_per_cu(size_t lds) {
   if (!cached[dev]) {
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ, reinterpret_cast<const void*>(&markov_step<KS, kReduced>), 256, lds) != hipSuccess || occ <= 0)
+            &occ, reinterpret_cast<const void*>(&markov_step<KS, kReduced, kMode>), 256, lds) != hipSuccess || occ <= 0)
       occ = 1;
     cached[dev] = occ;
   }
   return cached[dev];
 }
 
-template <int KS, bool kReduced>
+template <int KS, bool kReduced, int kMode>
+int step_slices(int chunks, int nbt, int max_slices, size_t lds) {
+  const int slots = std::min(kMaxSlots, resident_per_cu<KS, kReduced, kMode>(lds) * cu_count_markov());
+  return std::min(max_slices, markov_slices(chunks, nbt, slots));
+}
+
+template <int KS, bool kReduced, int kMode>
 hipError_t launch_steps(float* logits, const uint16_t* w1, const uint16_t* w2, const int32_t* tgt,
                         float* spill, const int32_t* anchor, const float* temperature, const uint32_t* request_id, uint32_t k0,
                         uint32_t k1, MarkovPartial* partial, int32_t* draft_tokens, float* log_z, int B, int N, int V,
-                        int Vd, int r, int nbt, int max_slices, const ConfArgs& conf, hipStream_t stream) {
+                        int Vd, int r, int nbt, int max_slices, const ConfArgs& conf, float* lw, float* win,
+                        hipStream_t stream) {
   const size_t lds = ChunkLds<4 * KS>::kBytes + 4 * kTurnBytes;
   const int chunks = (Vd + kChunk - 1) / kChunk;
-  const int slots = std::min(kMaxSlots, resident_per_cu<KS, kReduced>(lds) * cu_count_markov());
-  const int nvs = std::min(max_slices, markov_slices(chunks, nbt, slots));
+  const int nvs = step_slices<KS, kReduced, kMode>(chunks, nbt, max_slices, lds);
   const dim3 grid((nvs + 7) / 8 * 8 * nbt);
+  const StepIO io{lw, nullptr};
   for (int i = 0; i < N; ++i) {
     const int32_t* prev = (i == 0) ? anchor : draft_tokens + (i - 1);
     const int stride = (i == 0) ? 1 : N;
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(markov_step<KS, kReduced>), grid, dim3(256), lds, stream, logits, w1, w2, tgt,
-                       spill, prev, stride, temperature, request_id, k0, k1, partial, i, B, N, V, Vd, r, nvs, nbt,
-                       conf);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(markov_step<KS, kReduced, kMode>), grid, dim3(256), lds, stream, logits, w1,
+                       w2, tgt, spill, prev, stride, temperature, request_id, k0, k1, partial, i, B, N, V, Vd, r, nvs,
+                       nbt, conf, io);
     hipLaunchKernelGGL(markov_merge, dim3((B + 3) / 4), dim3(256), 0, stream, partial, temperature, draft_tokens,
-                       log_z, i, B, N, nvs);
+                       log_z, i, B, N, nvs, lw, win);
   }
   return hipGetLastError();
 }
 
 template <int KS>
-hipError_t launch_ks(bool reduced, float* logits, const uint16_t* w1, const uint16_t* w2, const int32_t* tgt,
-                     float* spill, const int32_t* anchor, const float* temperature, const uint32_t* request_id, uint32_t k0,
-                     uint32_t k1, MarkovPartial* partial, int32_t* draft_tokens, float* log_z, int B, int N, int V,
-                     int Vd, int r, int nbt, int max_slices, const ConfArgs& conf, hipStream_t stream) {
-  return reduced ? launch_steps<KS, true>(logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                                          draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, conf, stream)
-                 : launch_steps<KS, false>(logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                                           draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, conf, stream);
+hipError_t launch_ks(bool reduced, bool keep, float* logits, const uint16_t* w1, const uint16_t* w2,
+                     const int32_t* tgt, float* spill, const int32_t* anchor, const float* temperature,
+                     const uint32_t* request_id, uint32_t k0, uint32_t k1, MarkovPartial* partial,
+                     int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd, int r, int nbt, int max_slices,
+                     const ConfArgs& conf, float* lw, float* win, hipStream_t stream) {
+  if (keep)  // (no target map: checked by the caller)
+    return launch_steps<KS, false, kKeep>(logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1,
+                                          partial, draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, conf, lw,
+                                          win, stream);
+  return reduced ? launch_steps<KS, true, kStore>(logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1,
+                                                  partial, draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, conf,
+                                                  nullptr, nullptr, stream)
+                 : launch_steps<KS, false, kStore>(logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0,
+                                                   k1, partial, draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices,
+                                                   conf, nullptr, nullptr, stream);
+}
+
+template <int KS>
+hipError_t launch_replay_ks(float* logits, const uint16_t* w1, const uint16_t* w2, float* spill, const int32_t* rows,
+                            const int32_t* prev, const float* temperature, const uint32_t* request_id, int B, int N,
+                            int V, int Vd, int r, int nbt, int max_slices, hipStream_t stream) {
+  const size_t lds = ChunkLds<4 * KS>::kBytes + 4 * kTurnBytes;
+  const int chunks = (Vd + kChunk - 1) / kChunk;
+  const int nvs = step_slices<KS, false, kReplay>(chunks, nbt, max_slices, lds);
+  const dim3 grid((nvs + 7) / 8 * 8 * nbt);
+  const StepIO io{nullptr, rows};
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(markov_step<KS, false, kReplay>), grid, dim3(256), lds, stream, logits, w1, w2,
+                     nullptr, spill, prev, 1, temperature, request_id, 0u, 0u, nullptr, 0, B, N, V, Vd, r, nvs, nbt,
+                     ConfArgs{}, io);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -563,6 +648,8 @@ MarkovPlan plan_markov(int B, int N, int Vd, int r, int cus) {
   p.partial_bytes += ((size_t)Vd * sizeof(int32_t) + 255) / 256 * 256;
   p.spill_offset = p.partial_bytes;  // a logits row for stores of entries that do not exist
   p.partial_bytes += (size_t)chunks * kChunk * sizeof(float);
+  p.lw_offset = p.partial_bytes;     // winner logits of the partials (kept base logits)
+  p.partial_bytes += ((size_t)B * p.vslices * sizeof(float) + 255) / 256 * 256;
   // the query (cus == 0) must cover whichever path a launch picks
   if (p.few.bytes > p.partial_bytes) p.partial_bytes = p.few.bytes;
   return p;
@@ -571,30 +658,61 @@ MarkovPlan plan_markov(int B, int N, int Vd, int r, int cus) {
 hipError_t launch_markov_sample(float* logits, const uint16_t* w1, const uint16_t* w2, const int64_t* d2t,
                                 const int32_t* anchor, const float* temperature, const uint32_t* request_id,
                                 uint64_t seed, int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd,
-                                int r, void* workspace, const ConfArgs& conf, hipStream_t stream) {
+                                int r, void* workspace, const ConfArgs& conf, float* win, hipStream_t stream) {
   const MarkovPlan p = plan_markov(B, N, Vd, r, cu_count_markov());
-  if (p.few.use)
+  const bool keep = win != nullptr;
+  if (keep && d2t != nullptr) return hipErrorInvalidValue;  // kept base logits: no target map
+  // (the few-request kernel stores the processed logits: kept base logits take the per-step path)
+  if (p.few.use && !keep)
     return launch_markov_few(p.few, logits, w1, w2, d2t, anchor, temperature, request_id, seed, draft_tokens, log_z,
                              B, N, V, Vd, r, workspace, conf, stream);
   MarkovPartial* partial = static_cast<MarkovPartial*>(workspace);
   int32_t* tgt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.tgt_offset);
   float* spill = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.spill_offset);
+  float* lw = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.lw_offset);
   const bool reduced = d2t != nullptr;
   if (reduced) hipLaunchKernelGGL(target_table, dim3((Vd + 255) / 256), dim3(256), 0, stream, d2t, Vd, tgt);
   const uint32_t k0 = (uint32_t)(seed & 0xFFFFFFFFu), k1 = (uint32_t)(seed >> 32);
   switch (ksteps_of(r)) {
     case 1:
-      return launch_ks<1>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, stream);
+      return launch_ks<1>(reduced, keep, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, lw, win, stream);
     case 2:
-      return launch_ks<2>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, stream);
+      return launch_ks<2>(reduced, keep, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, lw, win, stream);
     case 4:
-      return launch_ks<4>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, stream);
+      return launch_ks<4>(reduced, keep, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, lw, win, stream);
     default:
-      return launch_ks<8>(reduced, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
-                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, stream);
+      return launch_ks<8>(reduced, keep, logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1, partial,
+                          draft_tokens, log_z, B, N, V, Vd, r, p.btiles, p.vslices, conf, lw, win, stream);
+  }
+}
+
+size_t markov_replay_spill_bytes(int Vd) {
+  const int chunks = (Vd + kChunk - 1) / kChunk;
+  return (size_t)chunks * kChunk * sizeof(float);
+}
+
+hipError_t launch_markov_replay(float* logits, const uint16_t* w1, const uint16_t* w2, const int32_t* rows,
+                                const int32_t* prev, const float* temperature, const uint32_t* request_id, int B,
+                                int N, int V, int Vd, int r, float* spill, hipStream_t stream) {
+  const int nbt = (B + kReqPerWG - 1) / kReqPerWG;
+  const int chunks = (Vd + kChunk - 1) / kChunk;
+  const int max_slices = markov_slices(chunks, nbt, kMaxSlots);
+  switch (ksteps_of(r)) {
+    case 1:
+      return launch_replay_ks<1>(logits, w1, w2, spill, rows, prev, temperature, request_id, B, N, V, Vd, r, nbt,
+                                 max_slices, stream);
+    case 2:
+      return launch_replay_ks<2>(logits, w1, w2, spill, rows, prev, temperature, request_id, B, N, V, Vd, r, nbt,
+                                 max_slices, stream);
+    case 4:
+      return launch_replay_ks<4>(logits, w1, w2, spill, rows, prev, temperature, request_id, B, N, V, Vd, r, nbt,
+                                 max_slices, stream);
+    default:
+      return launch_replay_ks<8>(logits, w1, w2, spill, rows, prev, temperature, request_id, B, N, V, Vd, r, nbt,
+                                 max_slices, stream);
   }
 }
 

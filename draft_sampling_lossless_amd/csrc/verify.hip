@@ -227,6 +227,17 @@ __global__ __launch_bounds__(256) void verify_rowstats(const float* __restrict__
 // The acceptance of request b by one 256-thread workgroup.  kCoherent: the
 // partial statistics were written by other workgroups of the same launch (loads
 // at device scope).
+// Kept base logits (deferred draft rows): p_d of the drafted token at position k is
+// win[b, k], and the acceptance pass names the row the sampling pass will read
+// (rows[b]: the first rejection, -1 when no draft row is read) and the token before it
+// (prev[b]) for the replay that recomputes that row.
+struct AcceptDef {
+  const float* win = nullptr;
+  const int32_t* anchor = nullptr;
+  int32_t* rows = nullptr;
+  int32_t* prev = nullptr;
+};
+
 template <bool kCoherent>
 __device__ __forceinline__ void accept_body(int b, int input_kind, const float* __restrict__ target,
                                             const float* __restrict__ draft, const float* __restrict__ draft_log_z,
@@ -239,7 +250,7 @@ __device__ __forceinline__ void accept_body(int b, int input_kind, const float* 
                                             Job* __restrict__ jobs, unsigned* __restrict__ tickets,
                                             int32_t* __restrict__ accepted, int32_t* __restrict__ out_tokens,
                                             float* __restrict__ accept_prob, int N, int V, int Vd, int nchunks,
-                                            int sample_chunks) {
+                                            int sample_chunks, AcceptDef def) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = verify_len ? min(max(verify_len[b], 0), N) : N;
   const uint32_t req = request_id[b];
@@ -259,7 +270,7 @@ __device__ __forceinline__ void accept_body(int b, int input_kind, const float* 
     const int xs = (x >= 0 && x < V) ? x : 0;
     xj = inv_map ? inv_map[xs] : xs;
     lt = target[((size_t)b * (N + 1) + k) * V + xs];
-    ld = draft[((size_t)b * N + k) * Vd + max(xj, 0)];
+    ld = def.win ? def.win[(size_t)b * N + k] : draft[((size_t)b * N + k) * Vd + max(xj, 0)];
     if (!probs) ldz = draft_log_z[(size_t)b * N + k];
   }
 
@@ -361,6 +372,10 @@ __device__ __forceinline__ void accept_body(int b, int input_kind, const float* 
     if (accept_prob && hot) rows = L + ((a == L) ? 1 : 0);
     jb.parts = rows * sample_chunks;
     jobs[b] = jb;
+    if (def.rows) {
+      def.rows[b] = (jb.mode == kJobResid) ? a : -1;
+      def.prev[b] = (a == 0) ? def.anchor[b] : draft_tokens[(size_t)b * N + a - 1];
+    }
     tickets[b] = 0u;
     if (probs) rstat[(size_t)b * (N + 1)] = make_float2(0.0f, 1.0f);
   }
@@ -378,10 +393,11 @@ __global__ __launch_bounds__(256) void verify_accept(int input_kind, const float
                                                      float2* __restrict__ rstat, Job* __restrict__ jobs,
                                                      unsigned* __restrict__ tickets, int32_t* __restrict__ accepted,
                                                      int32_t* __restrict__ out_tokens, float* __restrict__ accept_prob,
-                                                     int N, int V, int Vd, int nchunks, int sample_chunks) {
+                                                     int N, int V, int Vd, int nchunks, int sample_chunks,
+                                                     AcceptDef def) {
   accept_body<false>(blockIdx.x, input_kind, target, draft, draft_log_z, draft_tokens, inv_map, verify_len,
                      temperature, request_id, key0, key1, stats, rstat, jobs, tickets, accepted, out_tokens,
-                     accept_prob, N, V, Vd, nchunks, sample_chunks);
+                     accept_prob, N, V, Vd, nchunks, sample_chunks, def);
 }
 
 // Statistics and acceptance in one launch (logits input, B <= kFusedMaxB): the
@@ -406,7 +422,8 @@ __global__ __launch_bounds__(256) void verify_stats_accept(
     const uint32_t* __restrict__ request_id, uint32_t key0, uint32_t key1, RowStat* __restrict__ stats,
     float2* __restrict__ rstat, Job* __restrict__ jobs, unsigned* __restrict__ tickets,
     int32_t* __restrict__ accepted, int32_t* __restrict__ out_tokens, float* __restrict__ accept_prob,
-    unsigned* __restrict__ stat_tickets, int N, int V, int Vd, int nchunks, int chunk, int sample_chunks) {
+    unsigned* __restrict__ stat_tickets, int N, int V, int Vd, int nchunks, int chunk, int sample_chunks,
+    AcceptDef def) {
   const int row = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
   const int b = row / (N + 1), k = row % (N + 1);
   const int L = verify_len ? min(max(verify_len[b], 0), N) : N;
@@ -440,7 +457,7 @@ __global__ __launch_bounds__(256) void verify_stats_accept(
     __hip_atomic_store(rt + threadIdx.x * kTStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   accept_body<true>(b, DSPARK_INPUT_LOGITS, target, draft, draft_log_z, draft_tokens, inv_map, verify_len,
                     temperature, request_id, key0, key1, stats, rstat, jobs, tickets, accepted, out_tokens,
-                    accept_prob, N, V, Vd, nchunks, sample_chunks);
+                    accept_prob, N, V, Vd, nchunks, sample_chunks, def);
 }
 
 // ------------------------------------------------------------------ sampling rows
@@ -705,11 +722,12 @@ VerifyPlan plan_verify(int B, int N, int V) {
   return p;
 }
 
-hipError_t launch_verify(int input_kind, const float* target, const float* draft, const float* draft_log_z,
-                         const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
-                         const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
-                         int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
-                         hipStream_t stream) {
+namespace {
+hipError_t verify_impl(int input_kind, const float* target, const float* draft, const float* draft_log_z,
+                       const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
+                       const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
+                       int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
+                       const DeferredArgs* dfr, hipStream_t stream) {
   const VerifyPlan p = plan_verify(B, N, V);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t rows = (size_t)B * (N + 1);
@@ -725,6 +743,18 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
   RacePartial* race = reinterpret_cast<RacePartial*>(w);
   w += al(rows * p.sample_chunks * sizeof(RacePartial));
   float* apart = reinterpret_cast<float*>(w);
+  AcceptDef def;
+  float* spill = nullptr;
+  if (dfr) {  // after the plan's bytes: rows [B], prev [B], the replay's spill row
+    char* x = ws + p.total_bytes;
+    def.win = dfr->win;
+    def.anchor = dfr->anchor;
+    def.rows = reinterpret_cast<int32_t*>(x);
+    x += al((size_t)B * sizeof(int32_t));
+    def.prev = reinterpret_cast<int32_t*>(x);
+    x += al((size_t)B * sizeof(int32_t));
+    spill = reinterpret_cast<float*>(x);
+  }
   const uint32_t k0 = (uint32_t)(seed & 0xFFFFFFFFu), k1 = (uint32_t)(seed >> 32);
   const bool probs = input_kind == DSPARK_INPUT_PROBS;
   const unsigned stat_grid = (unsigned)((long)B * (N + 1) * p.stat_chunks);
@@ -747,14 +777,21 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
     hipLaunchKernelGGL(verify_stats_accept, dim3(stat_grid), dim3(256), 0, stream, target, draft, draft_log_z,
                        draft_tokens, inv_map, verify_len, temperature, request_id, k0, k1, stats, rstat, jobs,
                        tickets, accepted, out_tokens, accept_prob, st, N, V, Vd, p.stat_chunks, p.stat_chunk,
-                       p.sample_chunks);
+                       p.sample_chunks, def);
   } else {
     if (!probs)
       hipLaunchKernelGGL(verify_rowstats, dim3(stat_grid), dim3(256), 0, stream, target, verify_len, temperature,
                          stats, B, N, V, p.stat_chunks, p.stat_chunk);
     hipLaunchKernelGGL(verify_accept, dim3(B), dim3(256), 0, stream, input_kind, target, draft, draft_log_z,
                        draft_tokens, inv_map, verify_len, temperature, request_id, k0, k1, stats, rstat, jobs,
-                       tickets, accepted, out_tokens, accept_prob, N, V, Vd, p.stat_chunks, p.sample_chunks);
+                       tickets, accepted, out_tokens, accept_prob, N, V, Vd, p.stat_chunks, p.sample_chunks, def);
+  }
+  if (dfr) {
+    // the rows the sampling pass reads, from the base logits (the caller's buffer)
+    const hipError_t e =
+        launch_markov_replay(const_cast<float*>(draft), dfr->w1, dfr->w2, def.rows, def.prev, temperature,
+                             request_id, B, N, V, Vd, dfr->r, spill, stream);
+    if (e != hipSuccess) return e;
   }
   const int R = accept_prob ? N + 1 : 1;
   hipLaunchKernelGGL(verify_sample, dim3((unsigned)((long)B * R * p.sample_chunks)), dim3(256), 0, stream,
@@ -762,6 +799,29 @@ hipError_t launch_verify(int input_kind, const float* target, const float* draft
                      race, apart, tickets, accepted, out_tokens, accept_prob, B, N, V, Vd, R, p.sample_chunks,
                      p.sample_chunk);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_verify(int input_kind, const float* target, const float* draft, const float* draft_log_z,
+                         const int32_t* draft_tokens, const int32_t* inv_map, const int32_t* verify_len,
+                         const float* temperature, const uint32_t* request_id, uint64_t seed, int32_t* accepted,
+                         int32_t* out_tokens, float* accept_prob, int B, int N, int V, int Vd, void* workspace,
+                         hipStream_t stream) {
+  return verify_impl(input_kind, target, draft, draft_log_z, draft_tokens, inv_map, verify_len, temperature,
+                     request_id, seed, accepted, out_tokens, accept_prob, B, N, V, Vd, workspace, nullptr, stream);
+}
+
+size_t verify_deferred_extra_bytes(int B, int V) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  return 2 * al((size_t)B * sizeof(int32_t)) + al(markov_replay_spill_bytes(V));
+}
+
+hipError_t launch_verify_deferred(const float* target, float* draft_base, const float* draft_log_z,
+                                  const int32_t* draft_tokens, const int32_t* verify_len, const float* temperature,
+                                  const uint32_t* request_id, uint64_t seed, int32_t* accepted, int32_t* out_tokens,
+                                  int B, int N, int V, const DeferredArgs& d, void* workspace, hipStream_t stream) {
+  return verify_impl(DSPARK_INPUT_LOGITS, target, draft_base, draft_log_z, draft_tokens, nullptr, verify_len,
+                     temperature, request_id, seed, accepted, out_tokens, nullptr, B, N, V, V, workspace, &d, stream);
 }
 
 // ---------------------------------------------------------------- no-allocation variant

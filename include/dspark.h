@@ -11,6 +11,8 @@
  *   dspark_markov_sample  stage 2: N-step low-rank Markov Gumbel-max loop [P1 §2.2, §3, §5; P2 §4]
  *   dspark_admit          stage 4: survival by chain rule, pooled top-K    [P2 §6, §7]
  *   dspark_verify         stage 3: lossless rejection-sampling verify      [P2 §2; P3 §2]
+ *   dspark_markov_sample_deferred / dspark_verify_deferred
+ *                         stages 2 and 3 without storing every processed draft row
  *
  * Conventions shared by every call
  *   Memory     Every pointer argument is device memory (HBM) unless stated otherwise.
@@ -58,7 +60,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 4
+#define DSPARK_ABI_VERSION 5
 
 typedef enum dspark_status {
   DSPARK_OK = 0,
@@ -315,6 +317,50 @@ dspark_status dspark_markov_sample_conf(float* logits, const uint16_t* w1, const
                                         const float* tau, float* c_out,
                                         int B, int N, int V, int Vd, int r,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- deferred draft rows
+ * Stages 2 and 3 without storing the processed draft logits of every position.  The
+ * verification rule above [P2 §2] reads, per request, p_d of the drafted token at each
+ * verified position and one whole processed draft row: the residual at the first
+ * rejection (none when every position is accepted, or at T == 0).  The other N - 1
+ * rows stage 2 would store are never read.
+ *   dspark_markov_sample_deferred  stage 2 as dspark_markov_sample_conf (the five
+ *              confidence arguments h_dot, w_e, tau, c_out all given or all NULL:
+ *              no confidence, conf_bias ignored), except that logits keeps the base
+ *              logits (nothing is written to it) and win_logit [B, N] float32 (device,
+ *              out) receives l at each drafted token: win_logit[b, i] is the value
+ *              dspark_markov_sample would have stored at logits[b, i, draft_tokens[b, i]].
+ *              No target map: Vd == V (else DSPARK_ERR_UNSUPPORTED).  Always the
+ *              per-step kernels (never the few-request kernel); the workspace is
+ *              dspark_markov_workspace_size(B, N, Vd, r).
+ *   dspark_verify_deferred  dspark_verify in logits mode on those outputs: draft_base
+ *              [B, N, V] float32 = the base logits stage 2 kept (device, 16-byte
+ *              aligned), draft_log_z, win_logit and draft_tokens from stage 2, anchor
+ *              [B] and w1, w2, r as given to stage 2.  p_d of the drafted token at k is
+ *              taken from win_logit; the processed row of each request's first
+ *              rejection is recomputed in place in draft_base, with the same chunks,
+ *              fragments and MFMA sequence as stage 2, so it equals what stage 2 would
+ *              have stored bit for bit; every other row of draft_base is left as it
+ *              is.  accepted and out_tokens then equal dspark_verify's on the processed
+ *              logits bit for bit.  No inverse map, no acceptance probabilities.
+ *              workspace >= dspark_verify_deferred_workspace_size(B, N, V) bytes.
+ * Other arguments, limits and errors as dspark_markov_sample_conf / dspark_verify. */
+dspark_status dspark_markov_sample_deferred(float* logits, const uint16_t* w1, const uint16_t* w2,
+                                            const int32_t* anchor, const float* temperature,
+                                            const uint32_t* request_id, uint64_t seed,
+                                            int32_t* draft_tokens, float* log_z, float* win_logit,
+                                            const float* h_dot, const uint16_t* w_e, float conf_bias,
+                                            const float* tau, float* c_out,
+                                            int B, int N, int V, int Vd, int r,
+                                            void* workspace, size_t workspace_bytes, void* stream);
+size_t dspark_verify_deferred_workspace_size(int B, int N, int V);
+dspark_status dspark_verify_deferred(const float* target, float* draft_base, const float* draft_log_z,
+                                     const float* win_logit, const int32_t* draft_tokens,
+                                     const int32_t* anchor, const uint16_t* w1, const uint16_t* w2, int r,
+                                     const int32_t* verify_len, const float* temperature,
+                                     const uint32_t* request_id, uint64_t seed,
+                                     int32_t* accepted, int32_t* out_tokens, int B, int N, int V,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- end of a round
  * The next round's anchors ["DSpark 的实现和测评" §2.1: the anchor of a request is the

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(dspark_lib):
 
 
 def test_abi_version(dspark_lib):
-    assert dsl.abi_version() == 4
+    assert dsl.abi_version() == 5
 
 
 def _err():
@@ -92,6 +92,37 @@ def test_verify_validation(dspark_lib):
     need = dsl.verify_workspace_size(2, 8, 1024)
     assert need > 0
     assert _verify(workspace_bytes=need - 1) == WORKSPACE
+
+
+def _markov_deferred(**kw):
+    a = dict(logits=FAKE, w1=FAKE, w2=FAKE, anchor=FAKE, temperature=FAKE, request_id=FAKE, seed=0,
+             draft_tokens=FAKE, log_z=FAKE, win_logit=FAKE, h_dot=None, w_e=None, conf_bias=0.0, tau=None,
+             c_out=None, B=4, N=8, V=1024, Vd=1024, r=16, workspace=FAKE, workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return dsl.load().dspark_markov_sample_deferred(*a.values())
+
+
+def _verify_deferred(**kw):
+    a = dict(target=FAKE, draft_base=FAKE, draft_log_z=FAKE, win_logit=FAKE, draft_tokens=FAKE, anchor=FAKE,
+             w1=FAKE, w2=FAKE, r=16, verify_len=None, temperature=FAKE, request_id=FAKE, seed=0, accepted=FAKE,
+             out_tokens=FAKE, B=2, N=8, V=1024, workspace=FAKE, workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return dsl.load().dspark_verify_deferred(*a.values())
+
+
+def test_deferred_validation(dspark_lib):
+    assert _markov_deferred(Vd=512) == UNSUPPORTED and "target map" in _err()
+    assert _markov_deferred(win_logit=None) == INVALID and "win_logit" in _err()
+    assert _markov_deferred(h_dot=FAKE) == INVALID and "all given or all NULL" in _err()
+    assert _markov_deferred(B=0) == INVALID
+    assert _markov_deferred(workspace=None) == WORKSPACE
+    assert _verify_deferred(win_logit=None) == INVALID and "win_logit" in _err()
+    assert _verify_deferred(anchor=None) == INVALID and "anchor" in _err()
+    assert _verify_deferred(r=12) == INVALID
+    assert _verify_deferred(draft_log_z=None) == INVALID and "draft_log_z" in _err()
+    need = dsl.verify_deferred_workspace_size(2, 8, 1024)
+    assert need > dsl.verify_workspace_size(2, 8, 1024)
+    assert _verify_deferred(workspace_bytes=need - 1) == WORKSPACE
 
 
 def test_draft_logits_and_rng_validation(dspark_lib):

@@ -648,26 +648,30 @@ def test_multi_round_graph(name, over):
 
 # ------------------------------------------------------------------ whole round in a HIP graph
 def _round_outputs(path):
-    return [t.detach().clone() for t in (path.tokens, path.logz, path.logits, path.survival, path.admit_len,
-                                          path.accepted, path.out_tokens)]
+    outs = [path.tokens, path.logz, path.logits, path.survival, path.admit_len, path.accepted, path.out_tokens]
+    if path.deferred:
+        outs.append(path.win)
+    return [t.detach().clone() for t in outs]
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("name,over,coupled", [
-    ("tiny", {}, False),                                                          # few-request Markov kernel
-    ("batched", dict(B=8, H=256, V=8192, Vd=8192, r=64), False),                  # few-request, several requests
-    ("reduced_vocab", dict(B=40, H=256, V=8192, Vd=2048, r=64, K=200), False),    # per-step Markov, target map
-    ("batched", dict(B=24, H=512, V=4096, Vd=4096, r=32), True),                  # coupled verification
+@pytest.mark.parametrize("name,over,coupled,rows", [
+    ("tiny", {}, False, "stored"),                                                # few-request Markov kernel
+    ("tiny", {}, False, "deferred"),                                              # deferred rows, per-step kernel
+    ("batched", dict(B=8, H=256, V=8192, Vd=8192, r=64), False, "stored"),        # few-request, several requests
+    ("batched", dict(B=40, H=256, V=8192, Vd=8192, r=64), False, "deferred"),     # deferred rows, replay in the graph
+    ("reduced_vocab", dict(B=40, H=256, V=8192, Vd=2048, r=64, K=200), False, "deferred"),  # target map: stored
+    ("batched", dict(B=24, H=512, V=4096, Vd=4096, r=32), True, "deferred"),      # coupled verification
 ])
-def test_graph_replay_round(name, over, coupled):
+def test_graph_replay_round(name, over, coupled, rows):
     """A whole round (stages 1-4) captured once in a HIP graph and replayed: every replay,
     with eager work and synchronisations between replays, gives the eager round's outputs
     bit for bit (the library allocates nothing and clears its counters with kernels)."""
     import bench
     import draft_sampling_lossless_amd as dsl
     w = synth.get(name, **over)
-    say(f"graph replay {name} {over} coupled={coupled}")
-    path = bench.Path(w, torch, dsl, synth, "coupled" if coupled else "rejection", False)
+    say(f"graph replay {name} {over} coupled={coupled} draft rows {rows}")
+    path = bench.Path(w, torch, dsl, synth, "coupled" if coupled else "rejection", False, rows)
     path.step()
     torch.cuda.synchronize()
     ref = _round_outputs(path)
@@ -676,7 +680,7 @@ def test_graph_replay_round(name, over, coupled):
         path.step()
     torch.cuda.synchronize()
     for rep in range(3):
-        for t in (path.tokens, path.logz, path.logits, path.out_tokens):
+        for t in (path.tokens, path.logz, path.logits, path.out_tokens, path.win):
             t.fill_(-7)
         torch.cuda.synchronize()
         graph.replay()
