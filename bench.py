@@ -47,9 +47,9 @@ def parse():
     p.add_argument("--verify", default="rejection", choices=("rejection", "coupled"),
                    help="stage 3 rule: rejection sampling on p_t, p_d (default) or Gumbel-coupled verification")
     p.add_argument("--draft-rows", default="deferred", choices=("deferred", "stored"),
-                   help="deferred (default where it applies: no target map, rejection verification): stage 2 "
-                        "keeps the base logits and stage 3 rebuilds only the draft rows it reads; stored: stage 2 "
-                        "writes every processed draft row")
+                   help="deferred (default where it applies: no target map, rejection verification, more "
+                        "than 16 requests): stage 2 keeps the base logits and stage 3 rebuilds only the draft rows "
+                        "it reads; stored: stage 2 writes every processed draft row")
     p.add_argument("--round", default="path", choices=("path", "full"),
                    help="path: stages 1-4 with the workload's synthetic confidences and fixed K (default); "
                         "full: also the confidence head (its output feeds admission) and the throughput-optimal "
@@ -78,8 +78,10 @@ class Path:
         self.w, self.torch, self.dsl = w, torch, dsl
         self.coupled = verify_mode == "coupled"
         self.full = full_round
-        # deferred draft rows need the identity vocabulary map and rejection verification
-        self.deferred = draft_rows == "deferred" and not self.coupled and w.Vd == w.V
+        # deferred draft rows need the identity vocabulary map and rejection verification, and
+        # take the per-step Markov kernels: at 16 requests or fewer the few-request kernel,
+        # which stores the rows, is faster (one request: 0.28 against 0.37 ms per round)
+        self.deferred = draft_rows == "deferred" and not self.coupled and w.Vd == w.V and w.B > 16
         dev = torch.device("cuda:0")
         rp = synth.request_params(w)
 
@@ -315,15 +317,17 @@ def k1_roofline(w, k1_ms):
 def measured_traffic(stage, w):
     """HBM bytes (FETCH + WRITE, calibrated) per call of a stage from the committed
     rocprofv3 counter summary profiles/<stage>_<workload>_traffic.json, if it was
-    taken on the current source of the kernel file it names; else null."""
+    taken on the current sources of the kernel files it names; else null."""
     path = os.path.join(PROFILES, f"{stage}_{w.name}_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         d = json.load(open(path))
-        src = os.path.join(ROOT, d["source_file"])
-        if d.get("source_sha256_16") != src_hash(src):
-            return None
+        # every kernel source the stage's launches come from (older files name one)
+        files = d.get("source_files") or {d["source_file"]: d["source_sha256_16"]}
+        for f, h in files.items():
+            if h != src_hash(os.path.join(ROOT, f)):
+                return None
         return d.get("bytes_per_call")
     except Exception:
         return None

@@ -657,7 +657,7 @@ def _round_outputs(path):
 @pytest.mark.gpu
 @pytest.mark.parametrize("name,over,coupled,rows", [
     ("tiny", {}, False, "stored"),                                                # few-request Markov kernel
-    ("tiny", {}, False, "deferred"),                                              # deferred rows, per-step kernel
+    ("batched", dict(B=20, H=256, V=4096, Vd=4096, r=32), False, "deferred"),     # deferred rows, 20 requests
     ("batched", dict(B=8, H=256, V=8192, Vd=8192, r=64), False, "stored"),        # few-request, several requests
     ("batched", dict(B=40, H=256, V=8192, Vd=8192, r=64), False, "deferred"),     # deferred rows, replay in the graph
     ("reduced_vocab", dict(B=40, H=256, V=8192, Vd=2048, r=64, K=200), False, "deferred"),  # target map: stored
