@@ -155,6 +155,11 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   const int n = lane & 15, g = lane >> 4;
   const int nchunks = (Vd + kChunk - 1) / kChunk;
   const int kc = r / 8;  // W2 pieces per row that hold data
+  if (kMode == kReplay) {
+    // a request tile without a row to rebuild has nothing to do (uniform over the workgroup)
+    const int q = bt * kReqPerWG + tid;
+    if (!__syncthreads_or(tid < kReqPerWG && q < B && io.rows[q] >= 0)) return;
+  }
   const int rq0 = bt * kReqPerWG + wave * kReqPerWave;
   const bool wave_active = rq0 < B;
   const bool lane_ok = rq0 + n < B;
@@ -253,10 +258,10 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   // stores and the vector-memory counter stays exact.
   const int vd4 = Vd / 4;
   // the row this step reads (kReplay: the request's own row; a request without one
-  // reads row 0 and stores nothing)
-  const int rowb = (kMode == kReplay) ? max(io.rows[b], 0) : step;
-  float4* const row4 = reinterpret_cast<float4*>(logits + ((size_t)b * N + rowb) * Vd);
+  // reads the spill row, which stays in L2, and stores nothing)
+  const int rowb = (kMode == kReplay) ? io.rows[b] : step;
   float4* const spill4 = reinterpret_cast<float4*>(spill_row);
+  float4* const row4 = rowb >= 0 ? reinterpret_cast<float4*>(logits + ((size_t)b * N + rowb) * Vd) : spill4;
   // stores go out by rows: store instruction k of a chunk writes requests 4 k .. 4 k + 3
   // of the wave, lane L entries 4 (L % 16) .. +3 of request 4 k + L / 16 (256 contiguous
   // bytes per request); the chunk's logits are turned around in this wave's LDS block
