@@ -28,6 +28,7 @@ __all__ = [
     "philox_blocks", "race_exponentials", "draft_logits", "markov_sample",
     "markov_workspace_size", "build_inverse_map", "verify", "verify_workspace_size", "verify_noalloc", "admit",
     "markov_sample_deferred", "verify_deferred", "verify_deferred_workspace_size",
+    "context_kv", "context_kv_workspace_size",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.so")
@@ -65,6 +66,9 @@ _SIGS = {
     "dspark_markov_sample_deferred": (_c_int, [_c_void_p] * 6 + [_c_u64] + [_c_void_p] * 5 + [ctypes.c_float]
                                       + [_c_void_p] * 2 + [_c_int] * 5 + [_c_void_p, _c_size, _c_void_p]),
     "dspark_verify_deferred_workspace_size": (_c_size, [_c_int, _c_int, _c_int]),
+    "dspark_context_kv_workspace_size": (_c_size, [_c_int] * 5),
+    "dspark_context_kv": (_c_int, [_c_void_p] * 11 + [_c_int] * 6 + [_c_i64, ctypes.c_float, ctypes.c_float]
+                          + [_c_void_p, _c_size, _c_void_p]),
     "dspark_verify_deferred": (_c_int, [_c_void_p] * 8 + [_c_int] + [_c_void_p] * 3 + [_c_u64, _c_void_p, _c_void_p]
                                + [_c_int] * 3 + [_c_void_p, _c_size, _c_void_p]),
     "dspark_choose_k": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p]),
@@ -359,6 +363,35 @@ def verify_deferred(target: torch.Tensor, draft_base: torch.Tensor, draft_log_z:
         _ptr(accepted, "accepted", _I32, dev, (B,)), _ptr(out_tokens, "out_tokens", _I32, dev, (B, N + 1)),
         B, N, V, ws.data_ptr(), ws.numel(), _stream(target)))
     return accepted, out_tokens
+
+
+# ---------------------------------------------------------------- context-KV precompute
+
+def context_kv_workspace_size(num_ctx: int, H_d: int, L: int, nkv: int, hd: int) -> int:
+    return int(load().dspark_context_kv_workspace_size(num_ctx, H_d, L, nkv, hd))
+
+
+def context_kv(aux: torch.Tensor, fc_w: torch.Tensor, fc_b: Optional[torch.Tensor], hnorm_w: torch.Tensor,
+               kv_w: torch.Tensor, kv_b: torch.Tensor, knorm_w: torch.Tensor, positions: torch.Tensor,
+               slots: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, eps: float = 1e-6,
+               rope_theta: float = 1e6, workspace: Optional[torch.Tensor] = None) -> None:
+    """dspark_context_kv: writes the K/V of the M context tokens into k_cache / v_cache
+    [L, num_slots, nkv, hd] (bf16) at their slots.  Weights are bf16 (or int16 bit
+    patterns); positions int32 [M], slots int64 [M]."""
+    M, H_in = aux.shape
+    H_d = fc_w.shape[0]
+    L, num_slots, nkv, hd = k_cache.shape
+    dev = aux.device
+    ws = _workspace(workspace, context_kv_workspace_size(M, H_d, L, nkv, hd), dev)
+    kvr = L * 2 * nkv * hd
+    _check("dspark_context_kv", load().dspark_context_kv(
+        _ptr(aux, "aux", _BF16, dev, (M, H_in)), _ptr(fc_w, "fc_w", _BF16, dev, (H_d, H_in)),
+        _ptr(fc_b, "fc_b", _BF16, dev, (H_d,)), _ptr(hnorm_w, "hnorm_w", _BF16, dev, (H_d,)),
+        _ptr(kv_w, "kv_w", _BF16, dev, (kvr, H_d)), _ptr(kv_b, "kv_b", _BF16, dev, (kvr,)),
+        _ptr(knorm_w, "knorm_w", _BF16, dev, (L, hd)), _ptr(positions, "positions", _I32, dev, (M,)),
+        _ptr(slots, "slots", _I64, dev, (M,)), _ptr(k_cache, "k_cache", _BF16, dev),
+        _ptr(v_cache, "v_cache", _BF16, dev, tuple(k_cache.shape)), M, H_in, H_d, L, nkv, hd, num_slots,
+        float(eps), float(rope_theta), ws.data_ptr(), ws.numel(), _stream(aux)))
 
 
 def verify_noalloc(input_kind: int, target: torch.Tensor, draft: torch.Tensor, draft_log_z: Optional[torch.Tensor],

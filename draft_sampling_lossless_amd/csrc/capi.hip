@@ -332,6 +332,50 @@ dspark_status dspark_verify_deferred(const float* target, float* draft_base, con
                     "verify_deferred");
 }
 
+size_t dspark_context_kv_workspace_size(int num_ctx, int H_d, int L, int nkv, int hd) {
+  if (num_ctx <= 0 || H_d <= 0 || L <= 0 || nkv <= 0 || hd <= 0) return 0;
+  return dspark::context_kv_workspace_bytes(num_ctx, H_d, L, nkv, hd);
+}
+
+dspark_status dspark_context_kv(const uint16_t* aux, const uint16_t* fc_w, const uint16_t* fc_b,
+                                const uint16_t* hnorm_w, const uint16_t* kv_w, const uint16_t* kv_b,
+                                const uint16_t* knorm_w, const int32_t* positions, const int64_t* slots,
+                                uint16_t* k_cache, uint16_t* v_cache, int num_ctx, int H_in, int H_d, int L,
+                                int nkv, int hd, int64_t num_slots, float eps, float rope_theta, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  REQUIRE(num_ctx >= 0, DSPARK_ERR_INVALID, "num_ctx must be >= 0 (got %d)", num_ctx);
+  REQUIRE(H_in > 0 && H_in % 8 == 0, DSPARK_ERR_INVALID, "H_in must be a positive multiple of 8 (got %d)", H_in);
+  REQUIRE(H_d > 0 && H_d % 8 == 0, DSPARK_ERR_INVALID, "H_d must be a positive multiple of 8 (got %d)", H_d);
+  REQUIRE(L >= 1 && nkv >= 1, DSPARK_ERR_INVALID, "L and nkv must be >= 1 (got %d, %d)", L, nkv);
+  REQUIRE(hd >= 2 && hd % 2 == 0, DSPARK_ERR_INVALID, "hd must be even and >= 2 (got %d)", hd);
+  REQUIRE(hd <= 256, DSPARK_ERR_UNSUPPORTED, "hd must be <= 256 (got %d)", hd);
+  REQUIRE((L * 2 * nkv * hd) % 8 == 0, DSPARK_ERR_INVALID, "L * 2 * nkv * hd must be a multiple of 8");
+  REQUIRE(num_slots >= 1, DSPARK_ERR_INVALID, "num_slots must be >= 1");
+  REQUIRE(eps >= 0.0f && std::isfinite(eps), DSPARK_ERR_INVALID, "eps must be finite and >= 0");
+  REQUIRE(rope_theta > 0.0f && std::isfinite(rope_theta), DSPARK_ERR_INVALID, "rope_theta must be finite and > 0");
+  if (num_ctx == 0) return ok();
+  REQUIRE((int64_t)num_ctx * L * 2 * nkv * hd < ((int64_t)1 << 40), DSPARK_ERR_UNSUPPORTED, "num_ctx too large");
+  REQUIRE_PTR16(aux, "aux");
+  REQUIRE_PTR16(fc_w, "fc_w");
+  REQUIRE_PTR(hnorm_w, "hnorm_w");
+  REQUIRE_PTR16(kv_w, "kv_w");
+  REQUIRE_PTR(kv_b, "kv_b");
+  REQUIRE_PTR(knorm_w, "knorm_w");
+  REQUIRE_PTR(positions, "positions");
+  REQUIRE_PTR(slots, "slots");
+  REQUIRE_PTR(k_cache, "k_cache");
+  REQUIRE_PTR(v_cache, "v_cache");
+  const size_t need = dspark_context_kv_workspace_size(num_ctx, H_d, L, nkv, hd);
+  REQUIRE(workspace != nullptr, DSPARK_ERR_WORKSPACE, "workspace must not be NULL (%zu bytes needed)", need);
+  REQUIRE(aligned16(workspace), DSPARK_ERR_INVALID, "workspace must be 16-byte aligned");
+  REQUIRE(workspace_bytes >= need, DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes,
+          need);
+  return hip_status(dspark::launch_context_kv(aux, fc_w, fc_b, hnorm_w, kv_w, kv_b, knorm_w, positions, slots,
+                                              k_cache, v_cache, num_ctx, H_in, H_d, L, nkv, hd, num_slots, eps,
+                                              rope_theta, workspace, (hipStream_t)stream),
+                    "context_kv");
+}
+
 size_t dspark_verify_noalloc_max_bytes(void) { return dspark::kVerifyScratchBytes; }
 
 dspark_status dspark_verify_noalloc(int input_kind, const float* target, const float* draft,

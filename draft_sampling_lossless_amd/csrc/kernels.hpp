@@ -107,6 +107,13 @@ hipError_t launch_verify_deferred(const float* target, float* draft_base, const 
                                   const int32_t* draft_tokens, const int32_t* verify_len, const float* temperature,
                                   const uint32_t* request_id, uint64_t seed, int32_t* accepted, int32_t* out_tokens,
                                   int B, int N, int V, const DeferredArgs& d, void* workspace, hipStream_t stream);
+// ---- context-KV precompute (the step before the path)
+size_t context_kv_workspace_bytes(int M, int Hd, int L, int nkv, int hd);
+hipError_t launch_context_kv(const uint16_t* aux, const uint16_t* fc_w, const uint16_t* fc_b, const uint16_t* hnorm_w,
+                             const uint16_t* kv_w, const uint16_t* kv_b, const uint16_t* knorm_w,
+                             const int32_t* positions, const int64_t* slots, uint16_t* k_cache, uint16_t* v_cache,
+                             int M, int H_in, int Hd, int L, int nkv, int hd, int64_t num_slots, float eps,
+                             float theta, void* workspace, hipStream_t stream);
 // launch_verify with the library's static per-device scratch array as workspace
 constexpr size_t kVerifyScratchBytes = (size_t)4 << 20;
 hipError_t launch_verify_noalloc(int input_kind, const float* target, const float* draft, const float* draft_log_z,

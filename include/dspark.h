@@ -13,6 +13,8 @@
  *   dspark_verify         stage 3: lossless rejection-sampling verify      [P2 §2; P3 §2]
  *   dspark_markov_sample_deferred / dspark_verify_deferred
  *                         stages 2 and 3 without storing every processed draft row
+ *   dspark_context_kv     the step before the path: draft KV cache of new context
+ *                         tokens from the target's hidden states [P1 §4]
  *
  * Conventions shared by every call
  *   Memory     Every pointer argument is device memory (HBM) unless stated otherwise.
@@ -60,7 +62,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 5
+#define DSPARK_ABI_VERSION 6
 
 typedef enum dspark_status {
   DSPARK_OK = 0,
@@ -361,6 +363,37 @@ dspark_status dspark_verify_deferred(const float* target, float* draft_base, con
                                      const uint32_t* request_id, uint64_t seed,
                                      int32_t* accepted, int32_t* out_tokens, int B, int N, int V,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- context-KV precompute
+ * The draft KV cache of M = num_ctx new context tokens, filled from the target's
+ * intermediate hidden states in one pass instead of a layer-by-layer target forward
+ * [P1 §4 (Context KV 预计算); P2 §3 (KV injection)]:
+ *   ctx    = aux . fc_w^T + fc_b                       [M, H_d]   (fc_b may be NULL)
+ *   normed = bf16(ctx / sqrt(mean_j ctx_j^2 + eps) * hnorm_w)      the fused GEMM's operand
+ *   all_kv = normed . kv_w^T + kv_b                    [M, L*2*nkv*hd], rows of kv_w
+ *            ordered (layer, K/V, head, dim), one GEMM for every layer
+ *   for every layer l and head h, token m at slot s = slots[m]:
+ *     k = all_kv[m, l, 0, h, :] / sqrt(mean k^2 + eps) * knorm_w[l, :]    (grouped RMSNorm)
+ *     k = rotate-half RoPE: for i < hd/2 the pair (k_i, k_{i+hd/2}) rotated by
+ *         angle positions[m] * rope_theta^(-2i/hd)                          (fused RoPE)
+ *     k_cache[l, s, h, :] = bf16(k);   v_cache[l, s, h, :] = bf16(all_kv[m, l, 1, h, :])
+ *   aux [M, H_in], fc_w [H_d, H_in], fc_b [H_d] or NULL, hnorm_w [H_d], kv_w
+ *   [L*2*nkv*hd, H_d], kv_b [L*2*nkv*hd], knorm_w [L, hd]: bf16 bits, device (aux, fc_w,
+ *   kv_w 16-byte aligned).  positions [M] int32, slots [M] int64, device; a slot outside
+ *   [0, num_slots) is skipped (nothing written for that token).  k_cache, v_cache
+ *   [L, num_slots, nkv, hd] bf16 bits, device, written in place (other slots untouched).
+ *   Products accumulate in float32 on MFMA (the draft-logit kernels), norms and RoPE in
+ *   float32 with the angles formed in double.  H_in % 8 == 0, H_d % 8 == 0, hd even,
+ *   2 <= hd <= 256, eps >= 0, rope_theta > 0; num_ctx == 0 enqueues nothing.
+ *   workspace >= dspark_context_kv_workspace_size(num_ctx, H_d, L, nkv, hd) bytes,
+ *   device, 16-byte aligned. */
+size_t dspark_context_kv_workspace_size(int num_ctx, int H_d, int L, int nkv, int hd);
+dspark_status dspark_context_kv(const uint16_t* aux, const uint16_t* fc_w, const uint16_t* fc_b,
+                                const uint16_t* hnorm_w, const uint16_t* kv_w, const uint16_t* kv_b,
+                                const uint16_t* knorm_w, const int32_t* positions, const int64_t* slots,
+                                uint16_t* k_cache, uint16_t* v_cache, int num_ctx, int H_in, int H_d,
+                                int L, int nkv, int hd, int64_t num_slots, float eps, float rope_theta,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- end of a round
  * The next round's anchors ["DSpark 的实现和测评" §2.1: the anchor of a request is the

@@ -82,23 +82,27 @@ def rope_rotate_half(x, pos, theta: float) -> np.ndarray:
 
 def context_kv(aux_bits, fc_w_bits, fc_b_bits, hnorm_w_bits, kv_w_bits, kv_b_bits, knorm_w_bits, positions,
                slots, L: int, nkv: int, hd: int, num_slots: int, eps: float, theta: float,
-               k_cache=None, v_cache=None):
+               k_cache=None, v_cache=None, normed_bits=None):
     """Steps 1-5 above.
 
     aux_bits [num_ctx, H_in], fc_w_bits [H_d, H_in], fc_b_bits [H_d] or None,
     hnorm_w_bits [H_d], kv_w_bits [L*2*nkv*hd, H_d], kv_b_bits [L*2*nkv*hd],
     knorm_w_bits [L, hd]: bf16 bit patterns.  positions [num_ctx] int, slots
     [num_ctx] int in [0, num_slots).  k_cache / v_cache: [L, num_slots, nkv, hd]
-    uint16 arrays to write into (fresh zero arrays if None).
+    uint16 arrays to write into (fresh zero arrays if None).  normed_bits: optional
+    [num_ctx, H_d] bf16 operand of the fused GEMM to start from (steps 3-5 from
+    another implementation's rounding of step 2); computed here if None.
 
-    Returns dict(k_cache, v_cache, context, normed_bits, all_kv, k_final): the caches
+    Returns dict(k_cache, v_cache, context, normed, normed_bits, all_kv, k_final): the caches
     (bf16 bits) and the float64 intermediates of each step."""
     aux = bf16_decode(aux_bits)
     fc_w = bf16_decode(fc_w_bits)
     ctx = aux @ fc_w.T                                                    # step 1
     if fc_b_bits is not None:
         ctx = ctx + bf16_decode(fc_b_bits)
-    normed_bits = bf16_round(rms_norm(ctx, bf16_decode(hnorm_w_bits), eps))  # step 2: bf16 operand
+    normed = rms_norm(ctx, bf16_decode(hnorm_w_bits), eps)               # step 2: bf16 operand
+    if normed_bits is None:
+        normed_bits = bf16_round(normed)
     all_kv = bf16_decode(normed_bits) @ bf16_decode(kv_w_bits).T + bf16_decode(kv_b_bits)
     n = aux.shape[0]
     kv = all_kv.reshape(n, L, 2, nkv, hd)
@@ -117,4 +121,5 @@ def context_kv(aux_bits, fc_w_bits, fc_b_bits, hnorm_w_bits, kv_w_bits, kv_b_bit
         for layer in range(L):
             k_cache[layer, s] = kb[m, layer]
             v_cache[layer, s] = vb[m, layer]
-    return dict(k_cache=k_cache, v_cache=v_cache, context=ctx, normed_bits=normed_bits, all_kv=all_kv, k_final=k)
+    return dict(k_cache=k_cache, v_cache=v_cache, context=ctx, normed=normed, normed_bits=normed_bits, all_kv=all_kv,
+                k_final=k)

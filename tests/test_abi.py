@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(dspark_lib):
 
 
 def test_abi_version(dspark_lib):
-    assert dsl.abi_version() == 5
+    assert dsl.abi_version() == 6
 
 
 def _err():
@@ -123,6 +123,28 @@ def test_deferred_validation(dspark_lib):
     need = dsl.verify_deferred_workspace_size(2, 8, 1024)
     assert need > dsl.verify_workspace_size(2, 8, 1024)
     assert _verify_deferred(workspace_bytes=need - 1) == WORKSPACE
+
+
+def _context_kv(**kw):
+    a = dict(aux=FAKE, fc_w=FAKE, fc_b=None, hnorm_w=FAKE, kv_w=FAKE, kv_b=FAKE, knorm_w=FAKE, positions=FAKE,
+             slots=FAKE, k_cache=FAKE, v_cache=FAKE, num_ctx=16, H_in=256, H_d=128, L=2, nkv=2, hd=64,
+             num_slots=64, eps=1e-6, theta=1e6, workspace=FAKE, workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return dsl.load().dspark_context_kv(*a.values())
+
+
+def test_context_kv_validation(dspark_lib):
+    assert _context_kv(H_in=12) == INVALID
+    assert _context_kv(hd=63) == INVALID
+    assert _context_kv(hd=512) == UNSUPPORTED
+    assert _context_kv(eps=-1.0) == INVALID
+    assert _context_kv(theta=0.0) == INVALID
+    assert _context_kv(num_ctx=0) == OK                     # empty: nothing enqueued
+    assert _context_kv(slots=None) == INVALID and "slots" in _err()
+    assert _context_kv(aux=FAKE_ODD) == INVALID and "aligned" in _err()
+    assert _context_kv(workspace=None) == WORKSPACE
+    need = dsl.context_kv_workspace_size(16, 128, 2, 2, 64)
+    assert need > 0 and _context_kv(workspace_bytes=need - 1) == WORKSPACE
 
 
 def test_draft_logits_and_rng_validation(dspark_lib):
