@@ -54,6 +54,10 @@ def parse():
                    help="path: stages 1-4 with the workload's synthetic confidences and fixed K (default); "
                         "full: also the confidence head (its output feeds admission) and the throughput-optimal "
                         "K, computed from this round's survival and used two rounds later")
+    p.add_argument("--context-kv", type=int, default=8192, metavar="NCTX",
+                   help="also time the context-KV precompute (the step before the path) on one prefill chunk of "
+                        "NCTX tokens at H_in = H_d = 4096, 5 layers of 8 KV heads x 128 (0: skip); reported beside "
+                        "the headline, not in it")
     p.add_argument("--rounds", type=int, default=8,
                    help="multi-round driver: R consecutive rounds (each drafting from the previous round's last "
                         "emitted token, with its own seed) captured in one HIP graph and replayed; reports tau and "
@@ -345,6 +349,53 @@ def hbm_roofline(name, bytes_, ms, w, cold_ms=None):
     return out
 
 
+def context_kv_bench(torch, dsl, n_ctx, H=4096, L=5, nkv=8, hd=128, reps=10):
+    """dspark_context_kv on one prefill chunk: seeded synthetic bf16 weights and hidden
+    states made on the device, positions 0 .. n_ctx-1 at slots 0 .. n_ctx-1.  Time per
+    call from HIP events on the launch stream, warm; flops of the two products."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+
+    def bf(shape, std, mean=0.0):
+        return (torch.randn(shape, generator=g, device=dev) * std + mean).to(torch.bfloat16)
+
+    kvr = L * 2 * nkv * hd
+    args = dict(aux=bf((n_ctx, H), 1.0), fc_w=bf((H, H), H ** -0.5), fc_b=bf((H,), 0.1), hnorm_w=bf((H,), 0.1, 1.0),
+                kv_w=bf((kvr, H), H ** -0.5), kv_b=bf((kvr,), 0.1), knorm_w=bf((L, hd), 0.1, 1.0),
+                positions=torch.arange(n_ctx, dtype=torch.int32, device=dev),
+                slots=torch.arange(n_ctx, dtype=torch.int64, device=dev),
+                k_cache=torch.empty((L, n_ctx, nkv, hd), dtype=torch.bfloat16, device=dev),
+                v_cache=torch.empty((L, n_ctx, nkv, hd), dtype=torch.bfloat16, device=dev))
+    ws = torch.empty(dsl.context_kv_workspace_size(n_ctx, H, L, nkv, hd), dtype=torch.uint8, device=dev)
+
+    def call():
+        dsl.context_kv(args["aux"], args["fc_w"], args["fc_b"], args["hnorm_w"], args["kv_w"], args["kv_b"],
+                       args["knorm_w"], args["positions"], args["slots"], args["k_cache"], args["v_cache"],
+                       workspace=ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * n_ctx * H * (H + kvr)
+    tfs = flops / (ms * 1e-3) / 1e12
+    out = {"num_ctx": n_ctx, "H_in": H, "H_d": H, "L": L, "nkv": nkv, "hd": hd, "ms": round(ms, 4),
+           "tokens_per_s": round(n_ctx / (ms * 1e-3), 1), "achieved_tflops": round(tfs, 1),
+           "peak_tflops": MFMA_BF16_PEAK_TFS, "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+           "note": "fc and fused K/V products (MFMA) plus the norm, RoPE and cache-write passes; flops of the "
+                   "products; synthetic seeded weights"}
+    del args, ws
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(w, budget_s):
     """The oracle, as it stands, on a bounded sample of the workload: whole rounds
     of the first request (all N positions, full vocabulary), repeated while the
@@ -571,6 +622,8 @@ def run(args, w, path, torch):
         del graph
     if args.rounds > 0 and not path.full:
         result["multi_round"] = multi_round(w, path, torch, args.rounds)
+    if args.context_kv > 0:
+        result["context_kv"] = context_kv_bench(torch, path.dsl, args.context_kv)
     return result
 
 
