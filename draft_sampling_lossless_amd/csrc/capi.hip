@@ -357,14 +357,15 @@ dspark_status dspark_context_kv(const uint16_t* aux, const uint16_t* fc_w, const
   REQUIRE((int64_t)num_ctx * L * 2 * nkv * hd < ((int64_t)1 << 40), DSPARK_ERR_UNSUPPORTED, "num_ctx too large");
   REQUIRE_PTR16(aux, "aux");
   REQUIRE_PTR16(fc_w, "fc_w");
-  REQUIRE_PTR(hnorm_w, "hnorm_w");
+  if (fc_b) REQUIRE(aligned16(fc_b), DSPARK_ERR_INVALID, "fc_b must be 16-byte aligned");
+  REQUIRE_PTR16(hnorm_w, "hnorm_w");
   REQUIRE_PTR16(kv_w, "kv_w");
-  REQUIRE_PTR(kv_b, "kv_b");
-  REQUIRE_PTR(knorm_w, "knorm_w");
+  REQUIRE_PTR16(kv_b, "kv_b");
+  REQUIRE_PTR16(knorm_w, "knorm_w");
   REQUIRE_PTR(positions, "positions");
   REQUIRE_PTR(slots, "slots");
-  REQUIRE_PTR(k_cache, "k_cache");
-  REQUIRE_PTR(v_cache, "v_cache");
+  REQUIRE_PTR16(k_cache, "k_cache");
+  REQUIRE_PTR16(v_cache, "v_cache");
   const size_t need = dspark_context_kv_workspace_size(num_ctx, H_d, L, nkv, hd);
   REQUIRE(workspace != nullptr, DSPARK_ERR_WORKSPACE, "workspace must not be NULL (%zu bytes needed)", need);
   REQUIRE(aligned16(workspace), DSPARK_ERR_INVALID, "workspace must be 16-byte aligned");

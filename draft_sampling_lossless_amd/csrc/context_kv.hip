@@ -58,6 +58,48 @@ __global__ __launch_bounds__(256) void ctx_rmsnorm(const float* __restrict__ x, 
   }
 }
 
+// one workgroup per row, H_d <= 1024 x kRowVec: the row in registers as float4, one pass
+constexpr int kRowVec = 16;
+__global__ __launch_bounds__(256) void ctx_rmsnorm_vec(const float* __restrict__ x, const uint16_t* __restrict__ bias,
+                                                       const uint16_t* __restrict__ w, uint16_t* __restrict__ out,
+                                                       int Hd, float eps) {
+  __shared__ float red[4];
+  const float4* row = reinterpret_cast<const float4*>(x + (size_t)blockIdx.x * Hd);
+  const int n4 = Hd / 4;
+  float4 v[kRowVec];
+  float ss = 0.0f;
+#pragma unroll
+  for (int t = 0; t < kRowVec; ++t) {
+    const int j = threadIdx.x + 256 * t;
+    v[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (j < n4) {
+      v[t] = row[j];
+      if (bias) {
+        const uint2 bb = reinterpret_cast<const uint2*>(bias)[j];
+        v[t].x += bf16_to_f32(bb.x & 0xFFFF);
+        v[t].y += bf16_to_f32(bb.x >> 16);
+        v[t].z += bf16_to_f32(bb.y & 0xFFFF);
+        v[t].w += bf16_to_f32(bb.y >> 16);
+      }
+      ss = fmaf(v[t].x, v[t].x, fmaf(v[t].y, v[t].y, fmaf(v[t].z, v[t].z, fmaf(v[t].w, v[t].w, ss))));
+    }
+  }
+  const float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)Hd + eps);
+  uint2* orow = reinterpret_cast<uint2*>(out + (size_t)blockIdx.x * Hd);
+#pragma unroll
+  for (int t = 0; t < kRowVec; ++t) {
+    const int j = threadIdx.x + 256 * t;
+    if (j < n4) {
+      const uint2 ww = reinterpret_cast<const uint2*>(w)[j];
+      const uint32_t a = f32_to_bf16(v[t].x * inv * bf16_to_f32(ww.x & 0xFFFF));
+      const uint32_t b = f32_to_bf16(v[t].y * inv * bf16_to_f32(ww.x >> 16));
+      const uint32_t c = f32_to_bf16(v[t].z * inv * bf16_to_f32(ww.y & 0xFFFF));
+      const uint32_t d = f32_to_bf16(v[t].w * inv * bf16_to_f32(ww.y >> 16));
+      orow[j] = make_uint2(a | (b << 16), c | (d << 16));
+    }
+  }
+}
+
 constexpr int kMaxHd = 256;
 
 // one workgroup per token; wave w takes the (layer, head) pairs w, w + 4, ...; lane i
@@ -121,6 +163,69 @@ __global__ __launch_bounds__(256) void ctx_kv_finish(const float* __restrict__ a
   }
 }
 
+// hd = 128: one workgroup per token, one (layer, head) per wave and iteration; lanes
+// 0-31 do the head's K (lane q: entries 2q, 2q+1 and their rotary partners 2q+64,
+// 2q+65), lanes 32-63 its V (four consecutive entries each); paired loads and stores
+__global__ __launch_bounds__(256) void ctx_kv_finish128(const float* __restrict__ allkv,
+                                                        const uint16_t* __restrict__ kv_b,
+                                                        const uint16_t* __restrict__ knorm_w,
+                                                        const int32_t* __restrict__ positions,
+                                                        const int64_t* __restrict__ slots,
+                                                        uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int L,
+                                                        int nkv, int64_t num_slots, float eps, double theta) {
+  constexpr int hd = 128, half = 64;
+  __shared__ float cs[half], sn[half];
+  const int m = blockIdx.x;
+  const int64_t slot = slots[m];
+  if (slot < 0 || slot >= num_slots) return;  // (uniform) a slot outside the cache is skipped
+  if (threadIdx.x < half) {
+    const double ang = (double)positions[m] * pow(theta, -2.0 * (double)threadIdx.x / (double)hd);
+    double s_, c_;
+    sincos(ang, &s_, &c_);
+    cs[threadIdx.x] = (float)c_;
+    sn[threadIdx.x] = (float)s_;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kv = nkv * hd;
+  const float* row = allkv + (size_t)m * L * 2 * kv;
+  for (int p = wave; p < L * nkv; p += 4) {
+    const int l = p / nkv, h = p % nkv;
+    const size_t cbase = (((size_t)l * num_slots + slot) * nkv + h) * hd;
+    if (lane < 32) {
+      const int i = 2 * lane, ko = (2 * l) * kv + h * hd;
+      const float2 x = *reinterpret_cast<const float2*>(row + ko + i);
+      const float2 y = *reinterpret_cast<const float2*>(row + ko + i + half);
+      const uint32_t bx = *reinterpret_cast<const uint32_t*>(kv_b + ko + i);
+      const uint32_t by = *reinterpret_cast<const uint32_t*>(kv_b + ko + i + half);
+      const float a0 = x.x + bf16_to_f32(bx & 0xFFFF), a1 = x.y + bf16_to_f32(bx >> 16);
+      const float b0 = y.x + bf16_to_f32(by & 0xFFFF), b1 = y.y + bf16_to_f32(by >> 16);
+      float ss = fmaf(a0, a0, fmaf(a1, a1, fmaf(b0, b0, b1 * b1)));
+      for (int o = 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o);   // (within lanes 0-31)
+      const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
+      const uint16_t* kw = knorm_w + (size_t)l * hd;
+      const uint32_t wx = *reinterpret_cast<const uint32_t*>(kw + i);
+      const uint32_t wy = *reinterpret_cast<const uint32_t*>(kw + i + half);
+      const float x0 = a0 * inv * bf16_to_f32(wx & 0xFFFF), x1 = a1 * inv * bf16_to_f32(wx >> 16);
+      const float y0 = b0 * inv * bf16_to_f32(wy & 0xFFFF), y1 = b1 * inv * bf16_to_f32(wy >> 16);
+      const float c0 = cs[i], s0 = sn[i], c1 = cs[i + 1], s1 = sn[i + 1];
+      const uint32_t lo = (uint32_t)f32_to_bf16(x0 * c0 - y0 * s0) | ((uint32_t)f32_to_bf16(x1 * c1 - y1 * s1) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(y0 * c0 + x0 * s0) | ((uint32_t)f32_to_bf16(y1 * c1 + x1 * s1) << 16);
+      *reinterpret_cast<uint32_t*>(kc + cbase + i) = lo;
+      *reinterpret_cast<uint32_t*>(kc + cbase + i + half) = hi;
+    } else {
+      const int i = 4 * (lane - 32), vo = (2 * l + 1) * kv + h * hd;
+      const float4 x = *reinterpret_cast<const float4*>(row + vo + i);
+      const uint2 bb = *reinterpret_cast<const uint2*>(kv_b + vo + i);
+      const uint32_t a = f32_to_bf16(x.x + bf16_to_f32(bb.x & 0xFFFF));
+      const uint32_t b = f32_to_bf16(x.y + bf16_to_f32(bb.x >> 16));
+      const uint32_t c = f32_to_bf16(x.z + bf16_to_f32(bb.y & 0xFFFF));
+      const uint32_t d = f32_to_bf16(x.w + bf16_to_f32(bb.y >> 16));
+      *reinterpret_cast<uint2*>(vc + cbase + i) = make_uint2(a | (b << 16), c | (d << 16));
+    }
+  }
+}
+
 }  // namespace
 
 size_t context_kv_workspace_bytes(int M, int Hd, int L, int nkv, int hd) {
@@ -144,11 +249,18 @@ hipError_t launch_context_kv(const uint16_t* aux, const uint16_t* fc_w, const ui
   float* allkv = reinterpret_cast<float*>(w);
   hipError_t e = launch_draft_logits(aux, fc_w, ctx, M, H_in, Hd, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ctx_rmsnorm, dim3(M), dim3(256), 0, stream, ctx, fc_b, hnorm_w, normed, Hd, eps);
+  if (Hd <= 1024 * kRowVec)
+    hipLaunchKernelGGL(ctx_rmsnorm_vec, dim3(M), dim3(256), 0, stream, ctx, fc_b, hnorm_w, normed, Hd, eps);
+  else
+    hipLaunchKernelGGL(ctx_rmsnorm, dim3(M), dim3(256), 0, stream, ctx, fc_b, hnorm_w, normed, Hd, eps);
   e = launch_draft_logits(normed, kv_w, allkv, M, Hd, L * 2 * nkv * hd, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ctx_kv_finish, dim3(M), dim3(256), 0, stream, allkv, kv_b, knorm_w, positions, slots, k_cache,
-                     v_cache, L, nkv, hd, num_slots, eps, (double)theta);
+  if (hd == 128)
+    hipLaunchKernelGGL(ctx_kv_finish128, dim3(M), dim3(256), 0, stream, allkv, kv_b, knorm_w, positions, slots,
+                       k_cache, v_cache, L, nkv, num_slots, eps, (double)theta);
+  else
+    hipLaunchKernelGGL(ctx_kv_finish, dim3(M), dim3(256), 0, stream, allkv, kv_b, knorm_w, positions, slots,
+                       k_cache, v_cache, L, nkv, hd, num_slots, eps, (double)theta);
   return hipGetLastError();
 }
 

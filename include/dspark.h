@@ -378,10 +378,11 @@ dspark_status dspark_verify_deferred(const float* target, float* draft_base, con
  *         angle positions[m] * rope_theta^(-2i/hd)                          (fused RoPE)
  *     k_cache[l, s, h, :] = bf16(k);   v_cache[l, s, h, :] = bf16(all_kv[m, l, 1, h, :])
  *   aux [M, H_in], fc_w [H_d, H_in], fc_b [H_d] or NULL, hnorm_w [H_d], kv_w
- *   [L*2*nkv*hd, H_d], kv_b [L*2*nkv*hd], knorm_w [L, hd]: bf16 bits, device (aux, fc_w,
- *   kv_w 16-byte aligned).  positions [M] int32, slots [M] int64, device; a slot outside
+ *   [L*2*nkv*hd, H_d], kv_b [L*2*nkv*hd], knorm_w [L, hd]: bf16 bits, device, each
+ *   16-byte aligned.  positions [M] int32, slots [M] int64, device; a slot outside
  *   [0, num_slots) is skipped (nothing written for that token).  k_cache, v_cache
- *   [L, num_slots, nkv, hd] bf16 bits, device, written in place (other slots untouched).
+ *   [L, num_slots, nkv, hd] bf16 bits, device, 16-byte aligned, written in place
+ *   (other slots untouched).
  *   Products accumulate in float32 on MFMA (the draft-logit kernels), norms and RoPE in
  *   float32 with the angles formed in double.  H_in % 8 == 0, H_d % 8 == 0, hd even,
  *   2 <= hd <= 256, eps >= 0, rope_theta > 0; num_ctx == 0 enqueues nothing.
