@@ -86,6 +86,9 @@ class Path:
         # take the per-step Markov kernels: at 16 requests or fewer the few-request kernel,
         # which stores the rows, is faster (one request: 0.28 against 0.37 ms per round)
         self.deferred = draft_rows == "deferred" and not self.coupled and w.Vd == w.V and w.B > 16
+        # which kernels a stage launches: counter records apply only to the same variant
+        self.variant = "/".join(("deferred" if self.deferred else "stored", verify_mode,
+                                 "full" if full_round else "path"))
         dev = torch.device("cuda:0")
         rp = synth.request_params(w)
 
@@ -297,7 +300,7 @@ def k1_work(w):
     return bytes_, flops
 
 
-def k1_roofline(w, k1_ms):
+def k1_roofline(w, k1_ms, variant):
     bytes_, flops = k1_work(w)
     # arithmetic intensity vs the ridge of the chip decides the bound
     ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -314,19 +317,22 @@ def k1_roofline(w, k1_ms):
     else:
         roof["kernel"] = ("draft_logits (k1_skinny)" if w.M <= 64 else
                           "draft_logits (k1_big)" if w.H % 64 == 0 else "draft_logits (k1_tiled)")
-    roof["traffic"] = measured_traffic("draft_logits", w)
+    roof["traffic"] = measured_traffic("draft_logits", w, variant)
     return roof
 
 
-def measured_traffic(stage, w):
+def measured_traffic(stage, w, variant):
     """HBM bytes (FETCH + WRITE, calibrated) per call of a stage from the committed
     rocprofv3 counter summary profiles/<stage>_<workload>_traffic.json, if it was
-    taken on the current sources of the kernel files it names; else null."""
+    taken on the same path variant (draft rows / verify rule / round) and on the
+    current sources of the kernel files it names; else null."""
     path = os.path.join(PROFILES, f"{stage}_{w.name}_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         d = json.load(open(path))
+        if d.get("variant") != variant:
+            return None
         # every kernel source the stage's launches come from (older files name one)
         files = d.get("source_files") or {d["source_file"]: d["source_sha256_16"]}
         for f, h in files.items():
@@ -337,11 +343,11 @@ def measured_traffic(stage, w):
         return None
 
 
-def hbm_roofline(name, bytes_, ms, w, cold_ms=None):
+def hbm_roofline(name, bytes_, ms, w, variant, cold_ms=None):
     ach = bytes_ / (ms * 1e-3) / 1e9
     out = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(bytes_),
-           "traffic": measured_traffic(name.split(" ")[0], w)}
+           "traffic": measured_traffic(name.split(" ")[0], w, variant)}
     if cold_ms:
         cold = bytes_ / (cold_ms * 1e-3) / 1e9
         out["achieved_cold"] = round(cold, 1)
@@ -581,15 +587,16 @@ def run(args, w, path, torch):
     positions = w.B * w.N
     value = positions / (ms_per_step * 1e-3)
     k2_bytes, k3_bytes = stage_bytes(w, path.admit_len.cpu().numpy(), path.coupled, path.deferred)
-    roof = k1_roofline(w, stage_ms.get("draft_logits_live", stage_ms["draft_logits"]))
+    roof = k1_roofline(w, stage_ms.get("draft_logits_live", stage_ms["draft_logits"]), path.variant)
     if cold_ms:
         _, flops = k1_work(w)
         roof["frac_cold"] = round(flops / (cold_ms["draft_logits"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4) \
             if roof["bound"] == "mfma" else round(k1_work(w)[0] / (cold_ms["draft_logits"] * 1e-3) / 1e9
                                                   / HBM_PEAK_GBS, 4)
     roof["stages"] = [
-        hbm_roofline("markov_sample", k2_bytes, stage_ms["markov_sample"], w, cold_ms and cold_ms["markov_sample"]),
-        hbm_roofline("verify", k3_bytes, stage_ms["verify"], w, cold_ms and cold_ms["verify"]),
+        hbm_roofline("markov_sample", k2_bytes, stage_ms["markov_sample"], w, path.variant,
+                     cold_ms and cold_ms["markov_sample"]),
+        hbm_roofline("verify", k3_bytes, stage_ms["verify"], w, path.variant, cold_ms and cold_ms["verify"]),
     ]
     result = {
         "metric": "draft+verify positions/sec (B*N) and achieved HBM GB/s at V=151936",

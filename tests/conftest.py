@@ -32,7 +32,8 @@ def dspark_lib():
 
 def pytest_sessionfinish(session, exitstatus):
     """Write the Markov sampler's residual token-mismatch record of this session (the
-    GPU parity tests fill it) to gpurun_out/markov_parity.json."""
+    GPU parity tests fill it) to markov_parity.json in $DSPARK_RESULTS_DIR (default:
+    test_results/ at the repository root)."""
     mod = sys.modules.get("gpu_util")
     rec = getattr(mod, "MARKOV_RECORD", None) if mod else None
     if not rec:
@@ -45,7 +46,7 @@ def pytest_sessionfinish(session, exitstatus):
            "rule": "token differs only where the oracle's top-2 Gumbel key gap <= 1e-2 and the GPU token's "
                    "oracle key is within 1e-2 of the best; teacher-forced on the GPU tokens",
            "cases": [{"case": l, "positions": c, "mismatches": n} for l, c, n in rec]}
-    d = os.path.join(ROOT, "gpurun_out")
+    d = os.environ.get("DSPARK_RESULTS_DIR") or os.path.join(ROOT, "test_results")
     os.makedirs(d, exist_ok=True)
     with open(os.path.join(d, "markov_parity.json"), "w") as f:
         json.dump(out, f, indent=1)
