@@ -10,9 +10,13 @@
 //     V = all_kv[l, 1, h] + b                                    -> v_cache[l, slot, h]
 //                                                                    ctx_kv_finish
 //
-// The two products are MFMA GEMMs (the draft-logit kernels, fp32 out); the two small
-// passes are memory-bound and read what the products wrote.  Angles of the rotary
-// embedding are formed in double per token and shared by every layer and head.
+// The two products are MFMA GEMMs (the draft-logit kernels).  With heads of 128 and
+// more than 64 tokens the K/V product finishes each output tile itself (bias, K norm,
+// RoPE, bf16, slot writes; kv_epilogue_half in gemm.hip), so all_kv never reaches
+// memory; otherwise it writes all_kv in fp32 and ctx_kv_finish reads it.  Angles of the
+// rotary embedding are formed in double per token and shared by every layer and head:
+// in ctx_kv_finish, or for the fused epilogue as a float table [cos x 64, sin x 64] per
+// token (ctx_rope_table).
 #include <math.h>
 
 #include "device.hpp"
@@ -37,6 +41,21 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
   __syncthreads();
   return t;
+}
+
+// the rotary table for heads of 128: rope[m, i] = cos, rope[m, 64 + i] = sin of
+// positions[m] * theta^(-2 i / 128), formed in double; one thread per (token, i)
+__global__ __launch_bounds__(256) void ctx_rope_table(const int32_t* __restrict__ positions, float* __restrict__ rope,
+                                                      int M, double theta) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)M * 64) return;
+  const int64_t m = t >> 6;
+  const int i = (int)(t & 63);
+  const double ang = (double)positions[m] * pow(theta, -2.0 * (double)i / 128.0);
+  double s_, c_;
+  sincos(ang, &s_, &c_);
+  rope[(size_t)m * 128 + i] = (float)c_;
+  rope[(size_t)m * 128 + 64 + i] = (float)s_;
 }
 
 // one workgroup per row: x (+ bias) -> x / sqrt(mean(x^2) + eps) * w -> bf16
@@ -228,10 +247,13 @@ __global__ __launch_bounds__(256) void ctx_kv_finish128(const float* __restrict_
 
 }  // namespace
 
+// workspace: the fc product (fp32), the normalised states (bf16), then either the rotary
+// table (fused epilogue) or all_kv (fp32)
 size_t context_kv_workspace_bytes(int M, int Hd, int L, int nkv, int hd) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  return al((size_t)M * Hd * sizeof(float)) + al((size_t)M * Hd * sizeof(uint16_t)) +
-         al((size_t)M * L * 2 * nkv * hd * sizeof(float));
+  const size_t tail = kv_product_fused(M, Hd, hd) ? al((size_t)M * 128 * sizeof(float))
+                                                  : al((size_t)M * L * 2 * nkv * hd * sizeof(float));
+  return al((size_t)M * Hd * sizeof(float)) + al((size_t)M * Hd * sizeof(uint16_t)) + tail;
 }
 
 hipError_t launch_context_kv(const uint16_t* aux, const uint16_t* fc_w, const uint16_t* fc_b, const uint16_t* hnorm_w,
@@ -246,13 +268,32 @@ hipError_t launch_context_kv(const uint16_t* aux, const uint16_t* fc_w, const ui
   w += al((size_t)M * Hd * sizeof(float));
   uint16_t* normed = reinterpret_cast<uint16_t*>(w);
   w += al((size_t)M * Hd * sizeof(uint16_t));
-  float* allkv = reinterpret_cast<float*>(w);
+  float* tail = reinterpret_cast<float*>(w);
+  const bool fused = kv_product_fused(M, Hd, hd);
+  float* rope = fused ? tail : nullptr;
+  if (fused)
+    hipLaunchKernelGGL(ctx_rope_table, dim3((unsigned)(((int64_t)M * 64 + 255) / 256)), dim3(256), 0, stream,
+                       positions, rope, M, (double)theta);
   hipError_t e = launch_draft_logits(aux, fc_w, ctx, M, H_in, Hd, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
   if (Hd <= 1024 * kRowVec)
     hipLaunchKernelGGL(ctx_rmsnorm_vec, dim3(M), dim3(256), 0, stream, ctx, fc_b, hnorm_w, normed, Hd, eps);
   else
     hipLaunchKernelGGL(ctx_rmsnorm, dim3(M), dim3(256), 0, stream, ctx, fc_b, hnorm_w, normed, Hd, eps);
+  if (fused) {
+    KvEpilogue ep;
+    ep.kv_b = kv_b;
+    ep.knorm_w = knorm_w;
+    ep.rope = rope;
+    ep.slots = slots;
+    ep.kc = k_cache;
+    ep.vc = v_cache;
+    ep.nkv = nkv;
+    ep.num_slots = num_slots;
+    ep.eps = eps;
+    return launch_kv_product(normed, kv_w, M, Hd, L * 2 * nkv * hd, ep, stream);
+  }
+  float* allkv = tail;
   e = launch_draft_logits(normed, kv_w, allkv, M, Hd, L * 2 * nkv * hd, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
   if (hd == 128)

@@ -15,11 +15,14 @@
 //    straight from global memory into MFMA B fragments; the hidden rows (A
 //    fragments) come from L1/L2.  No LDS.
 //  * big (M > 64, H % 64 == 0): MFMA-bound.  256 x 256 output tiles, BK = 64,
-//    two LDS stages filled by global->LDS loads; each wave a 128 x 128 quarter.
+//    two LDS stages filled by global->LDS loads; 8 waves (two per SIMD), each a
+//    128 x 64 block; the output leaves through LDS in whole rows.  A second form
+//    of the same kernel is the context-KV product, whose epilogue writes the
+//    normalised, rotated K and the V heads to the caches in bf16.
 //  * tiled (other M > 64): 128 x 128 output tiles, BK = 64, both operands staged
 //    through double-buffered LDS; 4 waves, each a 64 x 64 block of 16x16 MFMA
-//    fragments.  Both MFMA tilings take a grouped tile order (8 row tiles at a
-//    time), XCD by XCD.
+//    fragments.  Both MFMA tilings take a grouped tile order (a few row tiles at
+//    a time), XCD by XCD.
 //
 // Optional extra row (the confidence head's hidden-state weights): with `wx` set, the
 // LM head is read as Vd + 1 rows, row Vd being wx, and output column Vd goes to
@@ -387,10 +390,116 @@ __device__ __forceinline__ void dma16_g(const uint16_t* src, char* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
 }
 
+// bf16 bits of a float, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
+  return make_uint4(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
+                    bf16_rne(v[4]) | (bf16_rne(v[5]) << 16), bf16_rne(v[6]) | (bf16_rne(v[7]) << 16));
+}
+
+__device__ __forceinline__ void add_bf16x8(float (&v)[8], const uint16_t* b) {
+  const uint4 q = *reinterpret_cast<const uint4*>(b);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] += bf16_to_f32(w[k] & 0xFFFF);
+    v[2 * k + 1] += bf16_to_f32(w[k] >> 16);
+  }
+}
+
+// The K/V product's epilogue over one half of the staged tile (every wave's rows
+// 64 h .. 64 h + 63, all 256 columns: two head blocks of 128).  Value (row r of wave
+// row-half wm, tile column c) sits in wave (wm | (c / 64) << 1)'s 16 KB block, row r,
+// piece (c % 64) / 4 at p ^ (r & 7).  Two threads take one (row, head block): for a K
+// block thread t holds the rotary pairs (i, i + 64), i in [32 t, 32 t + 32), eight at a
+// time; for a V block the dims [64 t, 64 t + 64).
+__device__ __forceinline__ void kv_epilogue_half(const char* smem, int h, int m0, int n0, int M, int ncols,
+                                                 const KvEpilogue& ep) {
+  const int tid = threadIdx.x, t = tid & 1, item = tid >> 1;
+  const int j = item & 1, r = (item >> 1) & 63, wm = item >> 7;
+  const int row = m0 + wm * 128 + 64 * h + r;
+  const int col0 = n0 + j * 128;              // first column of the head block
+  if (row >= M || col0 >= ncols) return;
+  const int64_t slot = ep.slots[row];
+  if (slot < 0 || slot >= ep.num_slots) return;
+  const int hb = col0 / 128, nkv = ep.nkv;
+  const int layer = hb / (2 * nkv), isv = (hb / nkv) & 1, head = hb % nkv;
+  const size_t cbase = (((size_t)layer * ep.num_slots + slot) * nkv + head) * 128;
+  auto lds8 = [&](int c, float (&v)[8]) {     // tile columns c .. c + 7 of this row, c % 8 == 0
+    const int wv = wm | ((c >> 6) << 1), p = (c & 63) >> 2;
+    const char* base = smem + wv * 16384 + r * 256;
+    const floatx4 a = *reinterpret_cast<const floatx4*>(base + ((p ^ (r & 7)) << 4));
+    const floatx4 b = *reinterpret_cast<const floatx4*>(base + (((p + 1) ^ (r & 7)) << 4));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = a[k];
+      v[4 + k] = b[k];
+    }
+  };
+  if (isv) {
+#pragma unroll 2
+    for (int q = 0; q < 8; ++q) {
+      const int d = 64 * t + 8 * q;
+      float v[8];
+      lds8(j * 128 + d, v);
+      add_bf16x8(v, ep.kv_b + col0 + d);
+      *reinterpret_cast<uint4*>(ep.vc + cbase + d) = pack_bf16x8(v);
+    }
+    return;
+  }
+  float ss = 0.0f;
+#pragma unroll 2
+  for (int q = 0; q < 4; ++q) {
+    const int i = 32 * t + 8 * q;
+    float x[8], y[8];
+    lds8(j * 128 + i, x);
+    lds8(j * 128 + 64 + i, y);
+    add_bf16x8(x, ep.kv_b + col0 + i);
+    add_bf16x8(y, ep.kv_b + col0 + 64 + i);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ss = fmaf(x[k], x[k], fmaf(y[k], y[k], ss));
+  }
+  ss += __shfl_xor(ss, 1);
+  const float inv = 1.0f / sqrtf(ss / 128.0f + ep.eps);
+  const uint16_t* kw = ep.knorm_w + (size_t)layer * 128;
+  const float* cs = ep.rope + (size_t)row * 128;
+#pragma unroll 2
+  for (int q = 0; q < 4; ++q) {
+    const int i = 32 * t + 8 * q;
+    float x[8], y[8], wx[8] = {}, wy[8] = {};
+    lds8(j * 128 + i, x);
+    lds8(j * 128 + 64 + i, y);
+    add_bf16x8(x, ep.kv_b + col0 + i);
+    add_bf16x8(y, ep.kv_b + col0 + 64 + i);
+    add_bf16x8(wx, kw + i);
+    add_bf16x8(wy, kw + 64 + i);
+    const float4 c0 = *reinterpret_cast<const float4*>(cs + i), c1 = *reinterpret_cast<const float4*>(cs + i + 4);
+    const float4 s0 = *reinterpret_cast<const float4*>(cs + 64 + i);
+    const float4 s1 = *reinterpret_cast<const float4*>(cs + 64 + i + 4);
+    const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    float lo[8], hi[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float a = x[k] * inv * wx[k], b = y[k] * inv * wy[k];
+      lo[k] = a * c[k] - b * sn[k];
+      hi[k] = b * c[k] + a * sn[k];
+    }
+    *reinterpret_cast<uint4*>(ep.kc + cbase + i) = pack_bf16x8(lo);
+    *reinterpret_cast<uint4*>(ep.kc + cbase + 64 + i) = pack_bf16x8(hi);
+  }
+}
+
+// kKV: the context-KV product (C, wx, xout unused): the epilogue of kv_epilogue_half
+template <bool kKV>
 __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                               float* __restrict__ C, int M, int H, int Vd, int mtiles,
                                               int ntiles, const uint16_t* __restrict__ wx,
-                                              float* __restrict__ xout) {
+                                              float* __restrict__ xout, const KvEpilogue ep) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int kGroupM = 4;
   const int total = mtiles * ntiles;
@@ -474,6 +583,22 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
   // p of row r at p ^ (r & 7)) and writes its block in two halves of 64 rows.
   asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   char* stage = smem + wave * 16384;
+  if constexpr (kKV) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1) __syncthreads();   // every (row, head) item of half 0 is done with the staging
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * i + n, p = 4 * j + g;
+          *reinterpret_cast<floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16)) = acc[4 * h + i][j];
+        }
+      __syncthreads();
+      kv_epilogue_half(smem, h, m0, n0, M, Vd, ep);
+    }
+    return;
+  }
   // whole float4 stores need 16-byte aligned rows
   const bool vec = (Vd % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
 #pragma unroll
@@ -539,15 +664,15 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big),
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<false>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
       if (e != hipSuccess) return e;
       attr_set[dev] = true;
     }
     const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vt + BBN - 1) / BBN;
     const int per_xcd = (mtiles * ntiles + 7) / 8;
-    hipLaunchKernelGGL(k1_big, dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits, M, H, Vd, mtiles,
-                       ntiles, wx, xout);
+    hipLaunchKernelGGL(k1_big<false>, dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits, M, H, Vd,
+                       mtiles, ntiles, wx, xout, KvEpilogue{});
   } else {
     const int mtiles = (M + TBM - 1) / TBM, ntiles = (Vt + TBN - 1) / TBN;
     const int total = mtiles * ntiles;
@@ -556,6 +681,26 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
     hipLaunchKernelGGL(k1_tiled, grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd, mtiles, ntiles, wx,
                        xout);
   }
+  return hipGetLastError();
+}
+
+bool kv_product_fused(int M, int Hd, int hd) { return hd == 128 && M > 64 && Hd % BBK == 0; }
+
+hipError_t launch_kv_product(const uint16_t* normed, const uint16_t* kv_w, int M, int Hd, int ncols,
+                             const KvEpilogue& ep, hipStream_t stream) {
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<true>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
+    if (e != hipSuccess) return e;
+    attr_set[dev] = true;
+  }
+  const int mtiles = (M + BBM - 1) / BBM, ntiles = (ncols + BBN - 1) / BBN;
+  const int per_xcd = (mtiles * ntiles + 7) / 8;
+  hipLaunchKernelGGL(k1_big<true>, dim3(per_xcd * 8), dim3(512), BLDS, stream, normed, kv_w, nullptr, M, Hd, ncols,
+                     mtiles, ntiles, nullptr, nullptr, ep);
   return hipGetLastError();
 }
 

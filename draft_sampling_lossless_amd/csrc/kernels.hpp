@@ -108,6 +108,26 @@ hipError_t launch_verify_deferred(const float* target, float* draft_base, const 
                                   const uint32_t* request_id, uint64_t seed, int32_t* accepted, int32_t* out_tokens,
                                   int B, int N, int V, const DeferredArgs& d, void* workspace, hipStream_t stream);
 // ---- context-KV precompute (the step before the path)
+// The fused K/V product's epilogue: per output row (token) and 128-wide head block, the
+// bias, then for K blocks the RMSNorm over the head and rotate-half RoPE, then bf16 into
+// the caches at the token's slot.  Column n of the product is (layer, K/V, head, dim)
+// with head blocks of 128.
+struct KvEpilogue {
+  const uint16_t* kv_b = nullptr;     // [L*2*nkv*128] bf16
+  const uint16_t* knorm_w = nullptr;  // [L, 128] bf16
+  const float* rope = nullptr;        // [M, 128]: cos of the 64 angles, then their sin
+  const int64_t* slots = nullptr;     // [M]; a slot outside [0, num_slots) is skipped
+  uint16_t* kc = nullptr;             // [L, num_slots, nkv, 128] bf16
+  uint16_t* vc = nullptr;
+  int nkv = 0;
+  int64_t num_slots = 0;
+  float eps = 0.0f;
+};
+// whether the K/V product of M tokens over H_d runs with the fused epilogue (head size 128,
+// the 256 x 256 tiling)
+bool kv_product_fused(int M, int Hd, int hd);
+hipError_t launch_kv_product(const uint16_t* normed, const uint16_t* kv_w, int M, int Hd, int ncols,
+                             const KvEpilogue& ep, hipStream_t stream);
 size_t context_kv_workspace_bytes(int M, int Hd, int L, int nkv, int hd);
 hipError_t launch_context_kv(const uint16_t* aux, const uint16_t* fc_w, const uint16_t* fc_b, const uint16_t* hnorm_w,
                              const uint16_t* kv_w, const uint16_t* kv_b, const uint16_t* knorm_w,

@@ -123,6 +123,8 @@ def _compare(gpu, ref, label):
     (33, 264, 136, 2, 2, 32, 64, True),        # H_in % 64 != 0: the tiled GEMM; small heads
     (20, 256, 256, 1, 2, 256, 32, True),       # hd = 256: two rotary pairs per lane
     (70, 512, 256, 2, 1, 2, 80, True),         # hd = 2: one pair per head
+    (100, 256, 192, 2, 3, 128, 160, True),     # the fused K/V epilogue: ragged rows, tiles mixing K and V heads
+    (65, 512, 128, 1, 1, 128, 65, False),      # fused at its smallest: 65 tokens, one layer, one head
 ])
 def test_context_kv_parity(M, H_in, H_d, L, nkv, hd, S, bias):
     say(f"context_kv M={M} H_in={H_in} H_d={H_d} L={L} nkv={nkv} hd={hd} S={S} fc_bias={bias}")
@@ -139,11 +141,12 @@ def test_context_kv_parity(M, H_in, H_d, L, nkv, hd, S, bias):
         f"K {fk:.3%}, V {fv:.3%}")
 
 
-def test_context_kv_slots_outside_the_cache_are_skipped():
-    c = _case(12, 256, 128, 2, 2, 64, 32, seed=5)
-    c["slots"][[2, 7]] = [-1, 32]
+@pytest.mark.parametrize("M,hd,S", [(12, 64, 32), (90, 128, 96)])   # the finishing pass; the fused epilogue
+def test_context_kv_slots_outside_the_cache_are_skipped(M, hd, S):
+    c = _case(M, 256, 128, 2, 2, hd, S, seed=5)
+    c["slots"][[2, 7]] = [-1, S]
     gk, gv, gn = _run_gpu(c)
-    keep = [m for m in range(12) if m not in (2, 7)]
+    keep = [m for m in range(M) if m not in (2, 7)]
     ref = _run_oracle(c, rows=keep, normed_bits=gn)
     _compare(gk, ref["k_cache"], "K")
     _compare(gv, ref["v_cache"], "V")
