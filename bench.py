@@ -277,15 +277,18 @@ class StageTimer:
         return {k: float(np.mean([b.elapsed_time(e) for b, e in v])) for k, v in self.pairs.items()}
 
 
-def stage_bytes(w, admit_len, coupled, deferred=False):
+def stage_bytes(w, accepted, coupled, deferred=False):
     """Compulsory HBM bytes of stage 2 and stage 3 per step.
     Stage 2: base logits read and processed logits written (8 B per entry), W2
     once, one W1 row per position; with deferred draft rows only the read (4 B).
-    Stage 3: target rows k <= L_b (4 V each); rejection sampling also reads one
-    target and one draft row to sample from (deferred: the base row and W2 once)."""
+    Stage 3: the target rows k <= a_b (4 V each), a_b = the accepted count: the
+    rows of the accepted positions and the decisive one (the first rejection, or
+    the bonus row); verification stops there, so rows past it are not part of the
+    method's work.  Rejection sampling also reads one target and one draft row to
+    sample from (deferred: the base row and W2 once)."""
     per_entry = 4 if deferred else 8
     k2 = per_entry * w.B * w.N * w.Vd + 2 * w.r * w.Vd + 2 * w.r * w.B * w.N
-    k3 = 4 * w.V * int((np.asarray(admit_len) + 1).sum())
+    k3 = 4 * w.V * int((np.asarray(accepted, dtype=np.int64) + 1).sum())
     if not coupled:
         k3 += w.B * (4 * w.V + 4 * w.Vd)
     if deferred:
@@ -586,7 +589,7 @@ def run(args, w, path, torch):
 
     positions = w.B * w.N
     value = positions / (ms_per_step * 1e-3)
-    k2_bytes, k3_bytes = stage_bytes(w, path.admit_len.cpu().numpy(), path.coupled, path.deferred)
+    k2_bytes, k3_bytes = stage_bytes(w, path.accepted.cpu().numpy(), path.coupled, path.deferred)
     roof = k1_roofline(w, stage_ms.get("draft_logits_live", stage_ms["draft_logits"]), path.variant)
     if cold_ms:
         _, flops = k1_work(w)

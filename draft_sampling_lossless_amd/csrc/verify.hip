@@ -209,15 +209,19 @@ __device__ __forceinline__ RowStat rowstats_part(const float* __restrict__ targe
   return a;
 }
 
+// Target rows k0 .. k0 + nk - 1 of every request (rows past the request's verify length
+// exit at once); with cont set, only the requests whose cont flag is set.
 __global__ __launch_bounds__(256) void verify_rowstats(const float* __restrict__ target,
                                                        const int32_t* __restrict__ verify_len,
                                                        const float* __restrict__ temperature,
                                                        RowStat* __restrict__ stats, int B, int N, int V,
-                                                       int nchunks, int chunk) {
-  const int row = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
-  const int b = row / (N + 1), k = row % (N + 1);
+                                                       int nchunks, int chunk, int k0, int nk,
+                                                       const int32_t* __restrict__ cont) {
+  const int rr = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+  const int b = rr / nk, k = k0 + rr % nk;
   const int L = verify_len ? min(max(verify_len[b], 0), N) : N;
-  if (k > L) return;
+  if (k > L || (cont && !cont[b])) return;
+  const int row = b * (N + 1) + k;
   const RowStat a = rowstats_part(target, temperature, row, b, c, V, chunk);
   if (threadIdx.x == 0) stats[(size_t)row * nchunks + c] = a;
 }
@@ -238,6 +242,18 @@ struct AcceptDef {
   int32_t* prev = nullptr;
 };
 
+// Lazy row statistics: the statistics of the first `avail` target rows are computed
+// first, and the acceptance runs on them.  A request whose first rejection (or whose
+// bonus row L) falls among those rows is decided there.  A request whose first
+// min(L, avail) positions are all accepted, with L >= avail, is undecided: cont_out[b] =
+// 1 and nothing else is written.  The rest of its rows are computed next, and a second
+// acceptance pass (avail = N + 1, cont_in) runs only the undecided requests.
+struct AcceptLazy {
+  int avail = DSPARK_MAX_N + 1;
+  int32_t* cont_out = nullptr;
+  const int32_t* cont_in = nullptr;
+};
+
 template <bool kCoherent>
 __device__ __forceinline__ void accept_body(int b, int input_kind, const float* __restrict__ target,
                                             const float* __restrict__ draft, const float* __restrict__ draft_log_z,
@@ -250,9 +266,11 @@ __device__ __forceinline__ void accept_body(int b, int input_kind, const float* 
                                             Job* __restrict__ jobs, unsigned* __restrict__ tickets,
                                             int32_t* __restrict__ accepted, int32_t* __restrict__ out_tokens,
                                             float* __restrict__ accept_prob, int N, int V, int Vd, int nchunks,
-                                            int sample_chunks, AcceptDef def) {
+                                            int sample_chunks, AcceptDef def, AcceptLazy lz) {
+  if (lz.cont_in && !lz.cont_in[b]) return;  // (uniform) decided by the first pass
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = verify_len ? min(max(verify_len[b], 0), N) : N;
+  const int tested = min(L, lz.avail);  // positions whose target row has statistics
   const uint32_t req = request_id[b];
   const bool probs = input_kind == DSPARK_INPUT_PROBS;
   const float T = probs ? 1.0f : temperature[b];
@@ -282,7 +300,7 @@ __device__ __forceinline__ void accept_body(int b, int input_kind, const float* 
   __shared__ int s_a;
   if (!probs && wave < 3) {
     constexpr int kU = 20;  // partials per lane and round
-    const int rows = L + 1, sub = tid & 7;
+    const int rows = min(L + 1, lz.avail), sub = tid & 7;
     for (int k0 = 0; k0 < rows; k0 += 24) {
       const int k = k0 + (tid >> 3);
       float m = -INFINITY, s = 0.0f, av = -INFINITY;
@@ -320,7 +338,7 @@ __device__ __forceinline__ void accept_body(int b, int input_kind, const float* 
   if (wave == 3) {
     bool rej = false;
     float greedy_alpha = 0.0f;
-    if (lane < L) {
+    if (lane < tested) {
       const int k = lane;
       const bool valid = x >= 0 && x < V;  // not a target id: rejected without using anything
       float pt, pd;
@@ -340,7 +358,9 @@ __device__ __forceinline__ void accept_body(int b, int input_kind, const float* 
       rej = !valid || !((double)u * (double)pd < (double)pt);
     }
     const uint64_t mask = __ballot(rej);
-    const int a = mask ? __builtin_ctzll(mask) : L;
+    // no rejection among the tested positions: the bonus row L when its statistics are
+    // there (L < avail), else undecided (-1)
+    const int a = mask ? __builtin_ctzll(mask) : (L < lz.avail ? L : -1);
     if (lane == 0) s_a = a;
     // greedy: alpha is 1 where the draft token is the target argmax (computed here)
     if (accept_prob && !hot && lane < N)
@@ -348,6 +368,8 @@ __device__ __forceinline__ void accept_body(int b, int input_kind, const float* 
   }
   __syncthreads();
   const int a = s_a;
+  if (lz.cont_out && tid == 0) lz.cont_out[b] = (a < 0) ? 1 : 0;
+  if (a < 0) return;
 
   // Outputs: accepted prefix, -1 padding, the sampling job.
   for (int k = tid; k <= N; k += 256) {
@@ -394,10 +416,10 @@ __global__ __launch_bounds__(256) void verify_accept(int input_kind, const float
                                                      unsigned* __restrict__ tickets, int32_t* __restrict__ accepted,
                                                      int32_t* __restrict__ out_tokens, float* __restrict__ accept_prob,
                                                      int N, int V, int Vd, int nchunks, int sample_chunks,
-                                                     AcceptDef def) {
+                                                     AcceptDef def, AcceptLazy lz) {
   accept_body<false>(blockIdx.x, input_kind, target, draft, draft_log_z, draft_tokens, inv_map, verify_len,
                      temperature, request_id, key0, key1, stats, rstat, jobs, tickets, accepted, out_tokens,
-                     accept_prob, N, V, Vd, nchunks, sample_chunks, def);
+                     accept_prob, N, V, Vd, nchunks, sample_chunks, def, lz);
 }
 
 // Statistics and acceptance in one launch (logits input, B <= kFusedMaxB): the
@@ -411,6 +433,9 @@ __global__ __launch_bounds__(256) void verify_accept(int input_kind, const float
 // request puts that request's counters back to zero (every other workgroup of the
 // request has counted by then), so every launch leaves its set as it found it.
 constexpr int kFusedMaxB = 16, kTicketSets = 64, kTGroups = 16;
+// target rows whose statistics the lazy first pass computes (most requests reject
+// within the first two positions)
+constexpr int kLazyRows = 2;
 constexpr int kTStride = 32;                              // words between counters (128 bytes)
 constexpr int kTWordsPerReq = (kTGroups + 1) * kTStride;  // [top, group 0 .. group 15]
 __device__ __attribute__((aligned(256))) unsigned g_stat_tickets[kTicketSets * kFusedMaxB * kTWordsPerReq];
@@ -457,7 +482,7 @@ __global__ __launch_bounds__(256) void verify_stats_accept(
     __hip_atomic_store(rt + threadIdx.x * kTStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   accept_body<true>(b, DSPARK_INPUT_LOGITS, target, draft, draft_log_z, draft_tokens, inv_map, verify_len,
                     temperature, request_id, key0, key1, stats, rstat, jobs, tickets, accepted, out_tokens,
-                    accept_prob, N, V, Vd, nchunks, sample_chunks, def);
+                    accept_prob, N, V, Vd, nchunks, sample_chunks, def, AcceptLazy{});
 }
 
 // ------------------------------------------------------------------ sampling rows
@@ -714,7 +739,7 @@ VerifyPlan plan_verify(int B, int N, int V) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t rows = (size_t)B * (N + 1);
   p.stats_bytes = al(rows * p.stat_chunks * sizeof(RowStat));
-  p.jobs_bytes = al((size_t)B * sizeof(Job)) + al(rows * sizeof(float2)) + al((size_t)B * sizeof(unsigned));
+  p.jobs_bytes = al((size_t)B * sizeof(Job)) + al(rows * sizeof(float2)) + 2 * al((size_t)B * sizeof(unsigned));
   // race and alpha partials for every (request, row, chunk): the rows dimension is
   // used only when alpha is requested, but the size must not depend on the call
   p.race_bytes = al(rows * p.sample_chunks * sizeof(RacePartial)) + al(rows * p.sample_chunks * sizeof(float));
@@ -740,6 +765,8 @@ hipError_t verify_impl(int input_kind, const float* target, const float* draft, 
   w += al(rows * sizeof(float2));
   unsigned* tickets = reinterpret_cast<unsigned*>(w);
   w += al((size_t)B * sizeof(unsigned));
+  int32_t* cont = reinterpret_cast<int32_t*>(w);
+  w += al((size_t)B * sizeof(int32_t));
   RacePartial* race = reinterpret_cast<RacePartial*>(w);
   w += al(rows * p.sample_chunks * sizeof(RacePartial));
   float* apart = reinterpret_cast<float*>(w);
@@ -778,13 +805,36 @@ hipError_t verify_impl(int input_kind, const float* target, const float* draft, 
                        draft_tokens, inv_map, verify_len, temperature, request_id, k0, k1, stats, rstat, jobs,
                        tickets, accepted, out_tokens, accept_prob, st, N, V, Vd, p.stat_chunks, p.stat_chunk,
                        p.sample_chunks, def);
+  } else if (!probs && !accept_prob && N + 1 > kLazyRows) {
+    // lazy row statistics: rows 0 .. kLazyRows - 1 and the acceptance on them, then the
+    // remaining rows of the requests still undecided and their acceptance
+    const unsigned grid_a = (unsigned)((long)B * kLazyRows * p.stat_chunks);
+    const unsigned grid_b = (unsigned)((long)B * (N + 1 - kLazyRows) * p.stat_chunks);
+    AcceptLazy first, second;
+    first.avail = kLazyRows;
+    first.cont_out = cont;
+    second.cont_in = cont;
+    hipLaunchKernelGGL(verify_rowstats, dim3(grid_a), dim3(256), 0, stream, target, verify_len, temperature, stats,
+                       B, N, V, p.stat_chunks, p.stat_chunk, 0, kLazyRows, static_cast<const int32_t*>(nullptr));
+    hipLaunchKernelGGL(verify_accept, dim3(B), dim3(256), 0, stream, input_kind, target, draft, draft_log_z,
+                       draft_tokens, inv_map, verify_len, temperature, request_id, k0, k1, stats, rstat, jobs,
+                       tickets, accepted, out_tokens, accept_prob, N, V, Vd, p.stat_chunks, p.sample_chunks, def,
+                       first);
+    hipLaunchKernelGGL(verify_rowstats, dim3(grid_b), dim3(256), 0, stream, target, verify_len, temperature, stats,
+                       B, N, V, p.stat_chunks, p.stat_chunk, kLazyRows, N + 1 - kLazyRows,
+                       static_cast<const int32_t*>(cont));
+    hipLaunchKernelGGL(verify_accept, dim3(B), dim3(256), 0, stream, input_kind, target, draft, draft_log_z,
+                       draft_tokens, inv_map, verify_len, temperature, request_id, k0, k1, stats, rstat, jobs,
+                       tickets, accepted, out_tokens, accept_prob, N, V, Vd, p.stat_chunks, p.sample_chunks, def,
+                       second);
   } else {
     if (!probs)
       hipLaunchKernelGGL(verify_rowstats, dim3(stat_grid), dim3(256), 0, stream, target, verify_len, temperature,
-                         stats, B, N, V, p.stat_chunks, p.stat_chunk);
+                         stats, B, N, V, p.stat_chunks, p.stat_chunk, 0, N + 1, static_cast<const int32_t*>(nullptr));
     hipLaunchKernelGGL(verify_accept, dim3(B), dim3(256), 0, stream, input_kind, target, draft, draft_log_z,
                        draft_tokens, inv_map, verify_len, temperature, request_id, k0, k1, stats, rstat, jobs,
-                       tickets, accepted, out_tokens, accept_prob, N, V, Vd, p.stat_chunks, p.sample_chunks, def);
+                       tickets, accepted, out_tokens, accept_prob, N, V, Vd, p.stat_chunks, p.sample_chunks, def,
+                       AcceptLazy{});
   }
   if (dfr) {
     // the rows the sampling pass reads, from the base logits (the caller's buffer)
