@@ -557,22 +557,28 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (kt + 1 < KT) issue(kt + 1);
     const char* st = smem + (kt % BNS) * BSTAGE;
+    // the fragments of both half steps are requested at once: the reads of the second
+    // run under the first's MFMAs
+    bf16x8 af[2][8], bf[2][4];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int pc = ((4 * s + g) ^ swz) * 16;
-      bf16x8 af[8], bf[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + brow + j * 16 * 128 + pc));
+        bf[s][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + brow + j * 16 * 128 + pc));
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + arow + i * 16 * 128 + pc));
-      __builtin_amdgcn_sched_barrier(0);
+        af[s][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + arow + i * 16 * 128 + pc));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[s][j], af[s][i], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
     }
