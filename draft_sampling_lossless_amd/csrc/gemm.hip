@@ -494,8 +494,11 @@ __device__ __forceinline__ void kv_epilogue_half(const char* smem, int h, int m0
   }
 }
 
-// kKV: the context-KV product (C, wx, xout unused): the epilogue of kv_epilogue_half
-template <bool kKV>
+// kKV: the context-KV product (C, wx, xout unused): the epilogue of kv_epilogue_half.
+// kWx: with the extra row (wx, xout set); that form reads each half step's fragments
+// just before its MFMAs (the extra row's addressing leaves no registers for reading
+// both at once).
+template <bool kKV, bool kWx>
 __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                               float* __restrict__ C, int M, int H, int Vd, int mtiles,
                                               int ntiles, const uint16_t* __restrict__ wx,
@@ -515,26 +518,59 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // hidden-row half, LM-head-row quarter
   const int n = lane & 15, g = lane >> 4;
-  const int Vt = Vd + (wx ? 1 : 0);         // LM-head rows including the extra one
+  const int Vt = Vd + (kWx ? 1 : 0);        // LM-head rows including the extra one
 
-  // DMA: instruction u (0..3) of this wave fills A rows (and W rows) 32 wave + 8 u .. +7;
+  // DMA: instruction u (0..3) for wave w fills A rows (and W rows) 32 w + 8 u .. +7;
   // lane L takes row 8 u + L / 8 of the wave's 32, physical piece L % 8, which holds
-  // logical piece (L % 8) ^ ((row >> 1) & 7)
-  const uint16_t* asrc[4];
-  const uint16_t* wsrc[4];
+  // logical piece (L % 8) ^ ((row >> 1) & 7).  On an inner tile (every row a real
+  // row, the extra row not among them) waves 0-3 issue the instructions of waves w and
+  // w + 4 (rows + 128, the same swizzle) and waves 4-7 issue none, so the second wave
+  // of each SIMD reaches its MFMAs without waiting on the DMA issue; the addresses are
+  // 32-bit offsets from the tile's row bases.  Edge tiles: every wave its own rows,
+  // clamped (rows past the last: a valid row, never stored), the extra row from wx.
+  const bool inner = (m0 + BBM <= M) && (n0 + BBN <= Vd);
+  const uint16_t* const Ab = A + (size_t)m0 * H;
+  const uint16_t* const Wb = W + (size_t)n0 * H;
+  const uint32_t poff = (uint32_t)(128 * H);
+  // per-lane element offsets of the DMA rows from the tile's row bases: inner tiles
+  // rows of wave w & 3 (the partner's are 128 rows on, the same swizzle); edge tiles
+  // this wave's rows, clamped.  kWx: the extra row is read from wx instead.
+  const int w0 = inner ? (wave & 3) : wave;
+  uint32_t aoff[4], woff[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int r = wave * 32 + 8 * u + (lane >> 3);
+    const int r = w0 * 32 + 8 * u + (lane >> 3);
     const int lg = (lane & 7) ^ ((r >> 1) & 7);
-    asrc[u] = A + (size_t)min(m0 + r, M - 1) * H + lg * 8;               // rows past M: a valid row, never stored
-    wsrc[u] = head_row(W, wx, min(n0 + r, Vt - 1), Vd, H) + lg * 8;      // rows past the last: likewise
+    aoff[u] = (uint32_t)((min(m0 + r, M - 1) - m0) * H + lg * 8);
+    woff[u] = (uint32_t)((min(n0 + r, Vd - 1) - n0) * H + lg * 8);
   }
   auto issue = [&](int kt) {
     char* st = smem + (kt % BNS) * BSTAGE;
+    const uint16_t* ak = Ab + kt * BBK;
+    const uint16_t* wk = Wb + kt * BBK;
+    if (inner) {
+      if (wave < 4) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      dma16_g(asrc[u] + kt * BBK, st + (wave * 32 + 8 * u) * 128);
-      dma16_g(wsrc[u] + kt * BBK, st + BBM * 128 + (wave * 32 + 8 * u) * 128);
+        for (int u = 0; u < 4; ++u) {
+          dma16_g(ak + aoff[u], st + (wave * 32 + 8 * u) * 128);
+          dma16_g(wk + woff[u], st + BBM * 128 + (wave * 32 + 8 * u) * 128);
+          dma16_g(ak + aoff[u] + poff, st + ((wave + 4) * 32 + 8 * u) * 128);
+          dma16_g(wk + woff[u] + poff, st + BBM * 128 + ((wave + 4) * 32 + 8 * u) * 128);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        dma16_g(ak + aoff[u], st + (wave * 32 + 8 * u) * 128);
+        if constexpr (kWx) {
+          const int r = wave * 32 + 8 * u + (lane >> 3);
+          if (n0 + r >= Vd) {   // the extra row (and rows past it, clamped to it)
+            dma16_g(wx + kt * BBK + ((lane & 7) ^ ((r >> 1) & 7)) * 8, st + BBM * 128 + (wave * 32 + 8 * u) * 128);
+            continue;
+          }
+        }
+        dma16_g(wk + woff[u], st + BBM * 128 + (wave * 32 + 8 * u) * 128);
+      }
     }
   };
 
@@ -551,12 +587,35 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
   const int KT = H / BBK;
   issue(0);
   for (int kt = 0; kt < KT; ++kt) {
-    // this wave's 8 DMA instructions of stage kt are done; after the barrier every
+    // this wave's DMA instructions of stage kt are done; after the barrier every
     // wave's are, and every wave has finished reading stage kt - 1, whose buffer
     // stage kt + 1 reuses
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (kt + 1 < KT) issue(kt + 1);
     const char* st = smem + (kt % BNS) * BSTAGE;
+    if constexpr (kWx) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int pc = ((4 * s + g) ^ swz) * 16;
+        bf16x8 af[8], bf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + brow + j * 16 * 128 + pc));
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + arow + i * 16 * 128 + pc));
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      continue;
+    }
     // the fragments of both half steps are requested at once: the reads of the second
     // run under the first's MFMAs
     bf16x8 af[2][8], bf[2][4];
@@ -670,15 +729,22 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<false>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<false, false>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<false, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
       if (e != hipSuccess) return e;
       attr_set[dev] = true;
     }
     const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vt + BBN - 1) / BBN;
     const int per_xcd = (mtiles * ntiles + 7) / 8;
-    hipLaunchKernelGGL(k1_big<false>, dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits, M, H, Vd,
-                       mtiles, ntiles, wx, xout, KvEpilogue{});
+    if (wx)
+      hipLaunchKernelGGL((k1_big<false, true>), dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits, M,
+                         H, Vd, mtiles, ntiles, wx, xout, KvEpilogue{});
+    else
+      hipLaunchKernelGGL((k1_big<false, false>), dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits,
+                         M, H, Vd, mtiles, ntiles, nullptr, nullptr, KvEpilogue{});
   } else {
     const int mtiles = (M + TBM - 1) / TBM, ntiles = (Vt + TBN - 1) / TBN;
     const int total = mtiles * ntiles;
@@ -698,14 +764,14 @@ hipError_t launch_kv_product(const uint16_t* normed, const uint16_t* kv_w, int M
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<true>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<true, false>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
     if (e != hipSuccess) return e;
     attr_set[dev] = true;
   }
   const int mtiles = (M + BBM - 1) / BBM, ntiles = (ncols + BBN - 1) / BBN;
   const int per_xcd = (mtiles * ntiles + 7) / 8;
-  hipLaunchKernelGGL(k1_big<true>, dim3(per_xcd * 8), dim3(512), BLDS, stream, normed, kv_w, nullptr, M, Hd, ncols,
+  hipLaunchKernelGGL((k1_big<true, false>), dim3(per_xcd * 8), dim3(512), BLDS, stream, normed, kv_w, nullptr, M, Hd, ncols,
                      mtiles, ntiles, nullptr, nullptr, ep);
   return hipGetLastError();
 }
