@@ -11,7 +11,10 @@
 //
 // Kernels: coupled_rows streams rows k <= L in (row, chunk) workgroups and writes
 // per-chunk argmax partials; coupled_finalize (one workgroup per request) merges
-// them row by row and applies the prefix rule.
+// them row by row and applies the prefix rule.  With more than 16 requests the rows
+// are taken lazily: rows 0-1 of every request first, and a finalize pass that decides
+// every request whose first mismatch (or row L) lies there; then the remaining rows
+// of the undecided requests and a second finalize pass for them.
 #include <math.h>
 
 #include <algorithm>
@@ -39,11 +42,14 @@ __global__ __launch_bounds__(256) void coupled_rows(const float* __restrict__ ta
                                                    const float* __restrict__ temperature,
                                                    const uint32_t* __restrict__ request_id, uint32_t key0,
                                                    uint32_t key1, ArgPartial* __restrict__ part, int N, int V,
-                                                   int nchunks, int chunk) {
-  const int row = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
-  const int b = row / (N + 1), k = row % (N + 1);
+                                                   int nchunks, int chunk, int k0, int nk,
+                                                   const int32_t* __restrict__ cont) {
+  // rows k0 .. k0 + nk - 1 of every request (with cont: of the requests still undecided)
+  const int rr = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+  const int b = rr / nk, k = k0 + rr % nk;
   const int L = verify_len ? min(max(verify_len[b], 0), N) : N;
-  if (k > L) return;
+  if (k > L || (cont && !cont[b])) return;
+  const int row = b * (N + 1) + k;
   const float T = temperature[b];
   const bool noisy = T > 0.0f;
   const float c2 = noisy ? (1.0f / T) * 1.4426950408889634f : 1.0f;
@@ -104,10 +110,17 @@ __global__ __launch_bounds__(256) void coupled_finalize(const ArgPartial* __rest
                                                         const int32_t* __restrict__ draft_tokens,
                                                         const int32_t* __restrict__ verify_len,
                                                         int32_t* __restrict__ accepted,
-                                                        int32_t* __restrict__ out_tokens, int N, int nchunks) {
+                                                        int32_t* __restrict__ out_tokens, int N, int nchunks,
+                                                        int avail, int32_t* __restrict__ cont_out,
+                                                        const int32_t* __restrict__ cont_in) {
+  // rows 0 .. avail - 1 have partials; with cont_out, a request whose first min(L, avail)
+  // positions all match while L >= avail is undecided (cont_out = 1, nothing written);
+  // with cont_in only the requests so marked run
   const int b = blockIdx.x, tid = threadIdx.x;
+  if (cont_in && !cont_in[b]) return;
   const int L = verify_len ? min(max(verify_len[b], 0), N) : N;
-  const int rows = L + 1, tpr = 256 / rows;
+  const int rows = min(L + 1, avail), tpr = 256 / rows;
+  const int tested = min(L, avail);
   const int k = tid / tpr, sub = tid - k * tpr;
   __shared__ float pk[256];
   __shared__ int pv[256];
@@ -140,12 +153,14 @@ __global__ __launch_bounds__(256) void coupled_finalize(const ArgPartial* __rest
   }
   __syncthreads();
   if (tid < 64) {  // the first mismatch, one lane per position
-    const bool miss = tid < L && draft_tokens[(size_t)b * N + tid] != y[tid];
+    const bool miss = tid < tested && draft_tokens[(size_t)b * N + tid] != y[tid];
     const uint64_t m = __ballot(miss);
-    if (tid == 0) s_a = m ? __builtin_ctzll(m) : L;
+    if (tid == 0) s_a = m ? __builtin_ctzll(m) : (L < avail ? L : -1);
   }
   __syncthreads();
   const int a = s_a;
+  if (cont_out && tid == 0) cont_out[b] = (a < 0) ? 1 : 0;
+  if (a < 0) return;
   for (int kk = tid; kk <= N; kk += 256)
     out_tokens[(size_t)b * (N + 1) + kk] = (kk < a) ? draft_tokens[(size_t)b * N + kk] : (kk == a ? y[a] : -1);
   if (tid == 0) accepted[b] = a;
@@ -157,11 +172,20 @@ int coupled_chunks(long rows, int V) {
   return (int)std::max(1L, std::min(want, maxc));
 }
 
+// rows whose partials the lazy first pass computes; lazy above 16 requests
+constexpr int kLazyRows = 2;
+bool coupled_lazy(int B, int N) { return B > 16 && N + 1 > kLazyRows; }
+// chunks per row: sized for the live rows of the (first) pass
+int coupled_nchunks(int B, int N, int V) {
+  return coupled_chunks(coupled_lazy(B, N) ? (long)B * kLazyRows : (long)B * (N + 1), V);
+}
+
 }  // namespace
 
 size_t coupled_workspace_bytes(int B, int N, int V) {
   const long rows = (long)B * (N + 1);
-  return (size_t)rows * coupled_chunks(rows, V) * sizeof(ArgPartial);
+  const size_t parts = (size_t)rows * coupled_nchunks(B, N, V) * sizeof(ArgPartial);
+  return (parts + 255) / 256 * 256 + (size_t)B * sizeof(int32_t);   // + the continue flags
 }
 
 hipError_t launch_verify_coupled(const float* target, const int32_t* draft_tokens, const int32_t* inv_map,
@@ -169,14 +193,32 @@ hipError_t launch_verify_coupled(const float* target, const int32_t* draft_token
                                  uint64_t seed, int32_t* accepted, int32_t* out_tokens, int B, int N, int V,
                                  void* workspace, hipStream_t stream) {
   const long rows = (long)B * (N + 1);
-  const int nchunks = coupled_chunks(rows, V);
+  const int nchunks = coupled_nchunks(B, N, V);
   const int chunk = ((V + nchunks - 1) / nchunks + 3) / 4 * 4;
   ArgPartial* part = static_cast<ArgPartial*>(workspace);
+  int32_t* cont = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                             ((size_t)rows * nchunks * sizeof(ArgPartial) + 255) / 256 * 256);
   const uint32_t k0 = (uint32_t)(seed & 0xFFFFFFFFu), k1 = (uint32_t)(seed >> 32);
-  hipLaunchKernelGGL(coupled_rows, dim3((unsigned)(rows * nchunks)), dim3(256), 0, stream, target, inv_map,
-                     verify_len, temperature, request_id, k0, k1, part, N, V, nchunks, chunk);
-  hipLaunchKernelGGL(coupled_finalize, dim3(B), dim3(256), 0, stream, part, draft_tokens, verify_len, accepted,
-                     out_tokens, N, nchunks);
+  const int32_t* none = nullptr;
+  if (coupled_lazy(B, N)) {
+    const int nk = N + 1 - kLazyRows;
+    hipLaunchKernelGGL(coupled_rows, dim3((unsigned)((long)B * kLazyRows * nchunks)), dim3(256), 0, stream, target,
+                       inv_map, verify_len, temperature, request_id, k0, k1, part, N, V, nchunks, chunk, 0,
+                       kLazyRows, none);
+    hipLaunchKernelGGL(coupled_finalize, dim3(B), dim3(256), 0, stream, part, draft_tokens, verify_len, accepted,
+                       out_tokens, N, nchunks, kLazyRows, cont, none);
+    hipLaunchKernelGGL(coupled_rows, dim3((unsigned)((long)B * nk * nchunks)), dim3(256), 0, stream, target, inv_map,
+                       verify_len, temperature, request_id, k0, k1, part, N, V, nchunks, chunk, kLazyRows, nk,
+                       static_cast<const int32_t*>(cont));
+    hipLaunchKernelGGL(coupled_finalize, dim3(B), dim3(256), 0, stream, part, draft_tokens, verify_len, accepted,
+                       out_tokens, N, nchunks, N + 1, static_cast<int32_t*>(nullptr),
+                       static_cast<const int32_t*>(cont));
+  } else {
+    hipLaunchKernelGGL(coupled_rows, dim3((unsigned)(rows * nchunks)), dim3(256), 0, stream, target, inv_map,
+                       verify_len, temperature, request_id, k0, k1, part, N, V, nchunks, chunk, 0, N + 1, none);
+    hipLaunchKernelGGL(coupled_finalize, dim3(B), dim3(256), 0, stream, part, draft_tokens, verify_len, accepted,
+                       out_tokens, N, nchunks, N + 1, static_cast<int32_t*>(nullptr), none);
+  }
   return hipGetLastError();
 }
 

@@ -493,6 +493,32 @@ def test_verify_coupled_parity(B, N, V, Vd, temps):
     assert near <= max(1, B // 50)
 
 
+def test_verify_coupled_lazy_rows_full_vocab():
+    """More than 16 requests at V = 151936: rows 0-1 first, the rest for the undecided
+    requests.  Each request's drafts are the target's own coupled draws (from the
+    oracle's noise) for a random prefix, so accepted counts spread over 0 .. L and the
+    second pass has work; results equal the oracle's except at a near-tie."""
+    B, N, V = 20, 6, 151936
+    say(f"verify coupled, lazy rows, B={B} N={N} V={V}")
+    c = _verify_inputs(B, N, V, V, (0.0, 0.7, 1.0), seed=77)
+    seed = 0x5EED
+    g = np.random.default_rng(78)
+    for b in range(B):
+        T = float(c["temp"][b])
+        m = int(g.integers(0, N + 1))
+        for k in range(m):
+            l = c["tgt"][b, k].astype(np.float64)
+            key = (l / T + stages.coupled_noise(seed, k, int(c["rid"][b]), V, None)) if T > 0 else l
+            c["tok"][b, k] = int(np.argmax(key))
+    acc, out = dsl.verify_coupled(dev(c["tgt"]), dev(c["tok"]), None, dev(c["L"]), dev(c["temp"]), dev(c["rid"]),
+                                  seed, Vd=V)
+    ref = stages.verify_coupled(c["tgt"], c["tok"], None, c["L"], c["temp"], c["rid"], seed)
+    near = _compare_coupled(host(acc), host(out), ref)
+    assert near <= 1
+    assert (ref["accepted"] >= 2).sum() >= 3, "the second pass must have requests to decide"
+    say(f"  accepted {host(acc).tolist()}, {near} near-tie")
+
+
 @pytest.mark.parametrize("Vd", [2048, 1000])
 def test_verify_coupled_accepts_stage2_drafts(Vd):
     # drafts from the GPU Markov sampler, target rows equal to its processed logits:
