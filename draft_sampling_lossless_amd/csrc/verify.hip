@@ -11,11 +11,15 @@
 // Kernels:
 //   rowstats   logits mode only.  Row statistics of target rows k <= L: base-2
 //              log-sum-exp of l / T (T > 0) or the argmax (T == 0), per
-//              (row, chunk) partial.
+//              (row, chunk) partial.  Above kFusedMaxB requests without alpha the
+//              rows are lazy: rows 0-1 first, the others only for requests the
+//              acceptance on those rows leaves undecided (two launches each).
 //   accept     one workgroup per request: merges every row's partials at once,
 //              tests all L positions in parallel (one lane each) and takes the
 //              first rejection; writes the accepted prefix, the merged row
 //              statistics and a sampling job.
+//   replay     (kept base logits) the first-rejection row rebuilt in place by the
+//              Markov step kernel, before the sampling pass reads it.
 //   sample     (request, row, chunk) workgroups stream the job row: the target
 //              row and, for a residual, the draft row gathered through the inverse
 //              map; per-chunk race winners for the residual and for its fallback
