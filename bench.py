@@ -321,6 +321,8 @@ def k1_roofline(w, k1_ms, variant):
         roof["kernel"] = ("draft_logits (k1_skinny)" if w.M <= 64 else
                           "draft_logits (k1_big)" if w.H % 64 == 0 else "draft_logits (k1_tiled)")
     roof["traffic"] = measured_traffic("draft_logits", w, variant)
+    if roof["traffic"]:
+        roof["traffic_gbs"] = round(roof["traffic"] / (k1_ms * 1e-3) / 1e9, 1)
     return roof
 
 
@@ -351,6 +353,10 @@ def hbm_roofline(name, bytes_, ms, w, variant, cold_ms=None):
     out = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(bytes_),
            "traffic": measured_traffic(name.split(" ")[0], w, variant)}
+    if out["traffic"]:
+        # the counted HBM bytes over the same time: how hard the stage drives the memory
+        out["traffic_gbs"] = round(out["traffic"] / (ms * 1e-3) / 1e9, 1)
+        out["traffic_frac"] = round(out["traffic_gbs"] / HBM_PEAK_GBS, 4)
     if cold_ms:
         cold = bytes_ / (cold_ms * 1e-3) / 1e9
         out["achieved_cold"] = round(cold, 1)
