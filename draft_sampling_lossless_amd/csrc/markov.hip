@@ -128,8 +128,12 @@ constexpr int kTurnRow = 272, kTurnBytes = 16 * kTurnRow;  // per wave: 16 reque
 // workgroup), the processed logit of the workgroup's winner (io.lw).  kReplay: store
 // the processed logits of one row per request (io.rows[b], -1: none) in place, with the
 // same chunk, fragment and MFMA sequence as the sampling modes, so they equal what
-// kStore would have stored bit for bit.
-enum StepMode { kStore = 0, kKeep = 1, kReplay = 2 };
+// kStore would have stored bit for bit.  kKeep2: kKeep with two chunk buffers: the
+// next chunk's W2 rows and base logits are requested right after the barrier that
+// opens a chunk, so they arrive under its MFMAs and epilogue, and one barrier per
+// chunk suffices (faster with one request tile, where there are few workgroups to
+// hide each other's waits; with more, the halved residency costs more than it saves).
+enum StepMode { kStore = 0, kKeep = 1, kReplay = 2, kKeep2 = 3 };
 struct StepIO {
   float* lw;             // kKeep: [B x nvs]
   const int32_t* rows;   // kReplay: [B]
@@ -144,6 +148,7 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
                                                    int B, int N, int V, int Vd, int r, int nvs, int nbt,
                                                    ConfArgs conf, StepIO io) {
   constexpr int P = 4 * KS;
+  constexpr bool kKeeps = kMode == kKeep || kMode == kKeep2;
   using Lay = ChunkLds<P>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int vs, bt;
@@ -175,17 +180,19 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   const int dma_row = Lay::vocab(0, lane / P);
   const int dma_off = dma_row * r + dma_piece * 8;
   auto issue_w2 = [&](int c) {
+    // kKeep2: chunk c into buffer ((c - vs) / nvs) & 1
+    char* const lbuf = lds + (kMode == kKeep2 ? (((c - vs) / nvs) & 1) * Lay::kBytes : 0);
     const int jc = c * kChunk;
     if (jc + kChunk <= Vd) {
       const uint16_t* src = w2 + (size_t)(jc + wave) * r;
 #pragma unroll
       for (int t = 0; t < KS; ++t)
-        dma16(src + (size_t)Lay::vocab(4 * t, 0) * r + dma_off, lds + (t * 4 + wave) * Lay::kGroup);
+        dma16(src + (size_t)Lay::vocab(4 * t, 0) * r + dma_off, lbuf + (t * 4 + wave) * Lay::kGroup);
     } else {  // the last, partial chunk: rows past Vd load row Vd - 1 (never used)
 #pragma unroll
       for (int t = 0; t < KS; ++t) {
         const int j = min(jc + wave + Lay::vocab(4 * t, 0) + dma_row, Vd - 1);
-        dma16(w2 + (size_t)j * r + dma_piece * 8, lds + (t * 4 + wave) * Lay::kGroup);
+        dma16(w2 + (size_t)j * r + dma_piece * 8, lbuf + (t * 4 + wave) * Lay::kGroup);
       }
     }
   };
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
       if (c == vs) issue_w2(c);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       asm volatile("s_barrier" ::: "memory");
-      asm volatile("s_barrier" ::: "memory");
+      if (kMode != kKeep2) asm volatile("s_barrier" ::: "memory");
       if (c + nvs < nchunks) issue_w2(c + nvs);
     }
     return;
@@ -310,23 +317,30 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   auto chunk = [&](int c, float4 (&cb)[4], float4 (&nb)[4]) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);    // DMA pieces and base logits of chunk c
     asm volatile("s_barrier" ::: "memory");  // every wave's pieces
+    const int cn = c + nvs;
+    if (kMode == kKeep2 && cn < nchunks) {    // the other buffer: last read by chunk c - nvs
+      issue_w2(cn);
+      load_base(cn, nb);
+    }
+    const char* const cbuf = lds + (kMode == kKeep2 ? (((c - vs) / nvs) & 1) * Lay::kBytes : 0);
     floatx4 acc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const char* arow = lds + Lay::offset(f, n) + 16 * g;
+      const char* arow = cbuf + Lay::offset(f, n) + 16 * g;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + 64 * s));
         acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, efrag[s], acc[f], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    asm volatile("s_barrier" ::: "memory");  // the chunk buffer is free again
-    const int cn = c + nvs;
-    if (cn < nchunks) {
-      issue_w2(cn);
-      load_base(cn, nb);
+    if (kMode != kKeep2) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      asm volatile("s_barrier" ::: "memory");  // the chunk buffer is free again
+      if (cn < nchunks) {
+        issue_w2(cn);
+        load_base(cn, nb);
+      }
     }
     const int jc = c * kChunk, j0 = jc + 4 * g, j4 = j0 / 4;  // block f: entries j0 + 16 f .. +3
     float l[4][4];
@@ -336,11 +350,11 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
       l[f][1] = cb[f].y + acc[f][1];
       l[f][2] = cb[f].z + acc[f][2];
       l[f][3] = cb[f].w + acc[f][3];
-      if (kMode != kKeep)
+      if (!kKeeps)
         *reinterpret_cast<float4*>(turn + n * kTurnRow + (16 * f + 4 * g) * 4) =
             make_float4(l[f][0], l[f][1], l[f][2], l[f][3]);
     }
-    if (kMode != kKeep) {
+    if (!kKeeps) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int e = lane & 15, jj4 = jc / 4 + e;
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
       if (km > bkey) {
         bkey = km;
         bblk = jc + 16 * f;
-        if (kMode == kKeep) {
+        if (kKeeps) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) bl[i] = l[f][i];
         }
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   {
     const int jb = bblk + 4 * g;
     float lv[4];
-    if (kMode == kKeep) {
+    if (kKeeps) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) lv[i] = bl[i];
     } else {
@@ -489,7 +503,7 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   }
   if (g == 0 && lane_ok) partial[(size_t)b * nvs + vs] = MarkovPartial{bkey, btok, bm, bs};
   // (the lanes of a request hold disjoint entries: exactly one of them owns the winner)
-  if (kMode == kKeep && lane_ok && btok_own == btok) io.lw[(size_t)b * nvs + vs] = lwin;
+  if (kKeeps && lane_ok && btok_own == btok) io.lw[(size_t)b * nvs + vs] = lwin;
 }
 
 namespace {
@@ -586,7 +600,18 @@ hipError_t launch_steps(float* logits, const uint16_t* w1, const uint16_t* w2, c
                         uint32_t k1, MarkovPartial* partial, int32_t* draft_tokens, float* log_z, int B, int N, int V,
                         int Vd, int r, int nbt, int max_slices, const ConfArgs& conf, float* lw, float* win,
                         hipStream_t stream) {
-  const size_t lds = ChunkLds<4 * KS>::kBytes + 4 * kTurnBytes;
+  const size_t lds = (kMode == kKeep2) ? 2 * ChunkLds<4 * KS>::kBytes : ChunkLds<4 * KS>::kBytes + 4 * kTurnBytes;
+  if (lds > 65536) {  // past the default dynamic LDS limit (once per device)
+    static bool attr_set[64] = {false};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&markov_step<KS, kReduced, kMode>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr_set[dev] = true;
+    }
+  }
   const int chunks = (Vd + kChunk - 1) / kChunk;
   const int nvs = step_slices<KS, kReduced, kMode>(chunks, nbt, max_slices, lds);
   const dim3 grid((nvs + 7) / 8 * 8 * nbt);
@@ -609,7 +634,11 @@ hipError_t launch_ks(bool reduced, bool keep, float* logits, const uint16_t* w1,
                      const uint32_t* request_id, uint32_t k0, uint32_t k1, MarkovPartial* partial,
                      int32_t* draft_tokens, float* log_z, int B, int N, int V, int Vd, int r, int nbt, int max_slices,
                      const ConfArgs& conf, float* lw, float* win, hipStream_t stream) {
-  if (keep)  // (no target map: checked by the caller)
+  if (keep && nbt == 1)  // (no target map: checked by the caller)
+    return launch_steps<KS, false, kKeep2>(logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1,
+                                           partial, draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, conf, lw,
+                                           win, stream);
+  if (keep)
     return launch_steps<KS, false, kKeep>(logits, w1, w2, tgt, spill, anchor, temperature, request_id, k0, k1,
                                           partial, draft_tokens, log_z, B, N, V, Vd, r, nbt, max_slices, conf, lw,
                                           win, stream);
