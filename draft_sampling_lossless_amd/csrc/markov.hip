@@ -22,9 +22,13 @@
 //                 nothing waits on them until the next chunk.  Per lane a running
 //                 best (key, block) and a base-2 log-sum-exp (m, s) are kept; the
 //                 four lanes of a request merge them and write one partial per
-//                 (request, workgroup).
+//                 (request, workgroup).  Modes (StepMode below): store the processed
+//                 logits, keep the base logits and record each partial's winning
+//                 logit instead (with one request tile, two LDS chunk buffers), or
+//                 rebuild one listed row per request.
 //   markov_merge  one wave per request reduces the partials, writes the token
-//                 and log Z.  The next step's kernel reads that token.
+//                 and log Z (keep modes: and the winner's processed logit).  The
+//                 next step's kernel reads that token.
 //
 // Few requests use markov_few.hip instead.
 //

@@ -347,9 +347,11 @@ def test_verify_probs_bit_exact(B, N, V, Vd, reduced):
                                                     # acceptance kernel's statistics merge
                                                     (6, 40, 1024, 1024, (0.7, 1.0), False),
                                                     (4, 64, 512, 512, (0.0, 1.0), False),
-                                                    # more than 256 requests: statistics and acceptance
-                                                    # in separate launches
+                                                    # more than 16 requests: statistics and acceptance in
+                                                    # separate launches, lazy rows from N = 2 on
                                                     (300, 2, 256, 256, (0.0, 1.0), False),
+                                                    (17, 2, 2048, 2048, (0.0, 0.7, 1.0), False),
+                                                    (40, 1, 1024, 1024, (0.7, 1.0), False),   # N = 1: not lazy
                                                     # one full-vocabulary request; a few with mixed temperatures
                                                     (1, 8, 151936, 151936, (1.0,), False),
                                                     (37, 5, 4096, 4096, (0.0, 0.7, 1.0), False)])
@@ -371,6 +373,30 @@ def test_verify_logits_parity(B, N, V, Vd, temps, reduced):
     near = compare_verify(host(acc), host(out), ref, exact=False)
     say(f"  {near} near-tie requests of {B}")
     assert near <= max(1, B // 50)
+
+
+@pytest.mark.parametrize("B,N,temps", [(48, 6, (0.0, 0.7, 1.0)), (20, 3, (1.0,))])
+def test_verify_logits_lazy_rows(B, N, temps):
+    """Target rows close to the draft rows (small noise), so many requests accept two
+    positions or more and the second statistics pass decides them: equal to the oracle
+    except at a near-tie."""
+    V = 2048
+    say(f"verify logits, lazy rows B={B} N={N} V={V} T={temps}")
+    c = _verify_inputs(B, N, V, V, temps, seed=4 * B + N, sigma=0.05)
+    logz = np.empty((B, N), np.float32)
+    for b in range(B):
+        for k in range(N):
+            T = float(c["temp"][b])
+            y = c["proc"][b, k].astype(np.float64)
+            logz[b, k] = (np.log(np.exp(y / T - (y / T).max()).sum()) + (y / T).max()) if T > 0 else y.max()
+    seed = 91
+    acc, out = dsl.verify(dsl.INPUT_LOGITS, dev(c["tgt"]), dev(c["proc"]), dev(logz), dev(c["tok"]), None,
+                          dev(c["L"]), dev(c["temp"]), dev(c["rid"]), seed)
+    ref = stages.verify("logits", c["tgt"], c["proc"], c["tok"], None, c["L"], c["temp"], c["rid"], seed)
+    near = compare_verify(host(acc), host(out), ref, exact=False)
+    assert near <= max(1, B // 50)
+    assert (ref["accepted"] >= 2).sum() >= 3, "the second statistics pass must have requests to decide"
+    say(f"  accepted {host(acc).tolist()}, {near} near-tie")
 
 
 def _alpha_ref(p_t, p_d, inv, L):
