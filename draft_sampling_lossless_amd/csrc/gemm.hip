@@ -682,7 +682,8 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
       const int row = m0 + wm * 128 + 64 * h + r, col = n0 + wn * 64 + 4 * p;
       if (row >= M || col >= Vt) continue;
       if (vec && col + 3 < Vd) {
-        *reinterpret_cast<floatx4*>(C + (size_t)row * Vd + col) = v;
+        // streamed out: the logits are read back only by the next stage
+        __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(C + (size_t)row * Vd + col));
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
