@@ -520,24 +520,31 @@ __global__ __launch_bounds__(256) void markov_merge(const MarkovPartial* __restr
   const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (b >= B) return;
-  float key = -INFINITY, m = -INFINITY, s = 0.0f;
+  float key = -INFINITY, m = -INFINITY, s = 0.0f, v = -INFINITY;
   int tok = 0x7FFFFFFF;
-  for (int p = lane; p < nvs; p += 64) {
-    const MarkovPartial q = partial[(size_t)b * nvs + p];
-    state_merge(key, tok, m, s, q.key, q.tok, q.m, q.s);
+  const bool keep = win != nullptr;
+  // up to 8 partials per lane in flight at once
+  for (int p0 = 0; p0 < nvs; p0 += 512) {
+    MarkovPartial q[8];
+    float qv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + 64 * j + lane;
+      q[j] = p < nvs ? partial[(size_t)b * nvs + p] : MarkovPartial{-INFINITY, 0x7FFFFFFF, -INFINITY, 0.0f};
+      qv[j] = keep && p < nvs ? lw[(size_t)b * nvs + p] : -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (key_beats(q[j].key, q[j].tok, key, tok)) v = qv[j];
+      state_merge(key, tok, m, s, q[j].key, q[j].tok, q[j].m, q[j].s);
+    }
   }
+  const int lane_tok = tok;
   wave_state_merge(key, tok, m, s);
-  if (win != nullptr) {
-    // the winner's processed logit, from the one partial that holds its id (the
-    // workgroups of a request cover disjoint entries)
-    float v = -INFINITY;
-    bool found = false;
-    for (int p = lane; p < nvs; p += 64)
-      if (!found && partial[(size_t)b * nvs + p].tok == tok) {
-        v = lw[(size_t)b * nvs + p];
-        found = true;
-      }
-    const uint64_t hit = __ballot(found);
+  if (keep) {
+    // the winner's processed logit: the lane whose own best is the winner holds it
+    // (the workgroups of a request cover disjoint entries)
+    const uint64_t hit = __ballot(lane_tok == tok);
     v = __shfl(v, hit ? (int)__builtin_ctzll(hit) : 0);
     if (lane == 0) win[(size_t)b * N + step] = v;
   }
