@@ -14,11 +14,13 @@
 //  * skinny (other M <= 64): each wave owns 16*FR vocabulary rows and streams them
 //    straight from global memory into MFMA B fragments; the hidden rows (A
 //    fragments) come from L1/L2.  No LDS.
-//  * big (M > 64, H % 64 == 0): MFMA-bound.  256 x 256 output tiles, BK = 64,
-//    two LDS stages filled by global->LDS loads; 8 waves (two per SIMD), each a
-//    128 x 64 block; the output leaves through LDS in whole rows.  A second form
-//    of the same kernel is the context-KV product, whose epilogue writes the
-//    normalised, rotated K and the V heads to the caches in bf16.
+//  * big (M > 64, H % 64 == 0): MFMA-bound.  256 x 256 output tiles, 8 waves (two
+//    per SIMD), each a 128 x 64 block; the output leaves through LDS in whole rows.
+//    The plain product (k1_pingpong) runs the two waves of a SIMD in alternating
+//    phases over a ring of four BK = 32 stages; the forms with the extra row and
+//    the context-KV product (k1_big) keep BK = 64 in two stages; the latter's
+//    epilogue writes the normalised, rotated K and the V heads to the caches in
+//    bf16.
 //  * tiled (other M > 64): 128 x 128 output tiles, BK = 64, both operands staged
 //    through double-buffered LDS; 4 waves, each a 64 x 64 block of 16x16 MFMA
 //    fragments.  Both MFMA tilings take a grouped tile order (a few row tiles at
@@ -693,6 +695,172 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
   }
 }
 
+// The plain product at many rows: the tiles, waves and epilogue of k1_big, with the
+// two waves of each SIMD in alternating phases.  Group X = waves 0-3, group Y = waves
+// 4-7 (one of each per SIMD); the k dimension runs in BK = 32 stages through a ring of
+// four 32 KB LDS buffers:
+//   phase 2t:   X reads stage t's fragments and issues the A rows of stage t + 3;
+//               Y runs the MFMAs of stage t - 1;
+//   phase 2t+1: X runs the MFMAs of stage t; Y reads stage t and issues the W rows of
+//               stage t + 3.
+// Every phase ends with a workgroup barrier, so on every SIMD one wave's MFMAs run
+// while the other waits on LDS.  Stage t + 3 goes into the buffer of stage t - 1, whose
+// last reader (Y, phase 2t - 1) is done before the barrier that opens phase 2t; each
+// group waits for its half of stage t + 1 before the barrier that closes phase 2t + 1,
+// so a stage's DMA has five or six phases to land.  LDS rows are 64 bytes (32 bf16):
+// logical piece p of row r sits at slot (p + (r >> 2)) & 3, so the 16 rows of one
+// fragment read fall into 16 distinct 16-byte bank groups.  The accumulation order over
+// k is that of k1_big, so both produce the same bits.  Requires H % 32 == 0.
+constexpr int PK = 32, PSTAGE = (BBM + BBN) * PK * 2, PNS = 4, PWOFF = BBM * PK * 2;
+static_assert(PNS * PSTAGE <= BLDS, "the ring and the epilogue share the k1_big LDS size");
+
+__global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                                                   float* __restrict__ C, int M, int H, int Vd, int mtiles,
+                                                   int ntiles) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int kGroupM = 4;
+  const int total = mtiles * ntiles;
+  const int per_xcd = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int group = lin / (kGroupM * ntiles), first_m = group * kGroupM;
+  const int gm = min(mtiles - first_m, kGroupM), within = lin - group * kGroupM * ntiles;
+  const int mt = first_m + within % gm, nt = within / gm;
+  const int m0 = mt * BBM, n0 = nt * BBN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, w4 = wave & 3;
+  const int wm = wave & 1, wn = wave >> 1;  // hidden-row half, LM-head-row quarter
+  const int n = lane & 15, g = lane >> 4;
+
+  // DMA: X fills the A rows, Y the W rows of a stage.  Wave w4 takes rows 64 w4 + 16 u
+  // .. +15 (u = 0..3); lane L row 16 u + L / 4 of them, LDS slot L % 4, which holds
+  // logical piece (L % 4 - L / 16) & 3.  Byte offsets from the tile's first row; rows
+  // past the last are clamped to it (their outputs are never stored).
+  const char* const src = grp == 0 ? reinterpret_cast<const char*>(A + (size_t)m0 * H)
+                                   : reinterpret_cast<const char*>(W + (size_t)n0 * H);
+  const int lim = grp == 0 ? M - 1 - m0 : Vd - 1 - n0;
+  uint32_t off[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 64 * w4 + 16 * u + (lane >> 2);
+    const int p = ((lane & 3) - (lane >> 4)) & 3;
+    off[u] = (uint32_t)(min(r, lim) * H * 2 + p * 16);
+  }
+  const int dst0 = (grp == 0 ? 0 : PWOFF) + 64 * w4 * (PK * 2);
+  auto issue = [&](int t) {
+    char* st = smem + (t % PNS) * PSTAGE + dst0;
+    const char* sk = src + t * PK * 2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      dma16_g(reinterpret_cast<const uint16_t*>(sk + off[u]), st + 16 * u * (PK * 2));
+  };
+
+  floatx4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // fragment reads: row 16 i + n of the wave's rows, logical piece g
+  const int slot = ((g + (n >> 2)) & 3) * 16;
+  const int ard = (wm * 128 + n) * (PK * 2) + slot, brd = PWOFF + (wn * 64 + n) * (PK * 2) + slot;
+  bf16x8 af[8], bf[4];
+  auto read = [&](int t) {
+    const char* st = smem + (t % PNS) * PSTAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + brd + j * 16 * (PK * 2)));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + ard + i * 16 * (PK * 2)));
+  };
+  auto mfma = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // wait until this wave's DMA of stage s has landed, stages up to `last` issued (four
+  // instructions each, completing in order)
+  auto wait_stage = [&](int s, int last) {
+    const int after = last - s;
+    if (after >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (after == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  const int KT = H / PK;
+  const int pro = min(3, KT);
+  for (int t = 0; t < pro; ++t) issue(t);
+  wait_stage(0, pro - 1);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  if (grp == 0) {
+    for (int t = 0; t < KT; ++t) {
+      read(t);                                                   // phase 2t
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 3 < KT) issue(t + 3);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      mfma();                                                    // phase 2t + 1
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < KT) wait_stage(t + 1, min(t + 3, KT - 1));
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    asm volatile("s_barrier" ::: "memory");                      // phase 0
+    __builtin_amdgcn_sched_barrier(0);
+    for (int t = 0; t < KT; ++t) {
+      read(t);                                                   // phase 2t + 1
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 3 < KT) issue(t + 3);
+      if (t + 1 < KT) wait_stage(t + 1, min(t + 3, KT - 1));
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      mfma();                                                    // phase 2t + 2
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < KT) asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Every stage has been read and no DMA is in flight (X passed the last common
+  // barrier after Y's last reads; Y's last MFMAs touch registers only): each wave
+  // stages its 128 x 64 block in its own 16 KB of the ring, in two halves of 64 rows,
+  // and writes whole 256-byte row pieces.
+  char* stage = smem + wave * 16384;
+  const bool vec = (Vd % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * i + n, p = 4 * j + g;
+        *reinterpret_cast<floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16)) = acc[4 * h + i][j];
+      }
+#pragma unroll 4
+    for (int t = 0; t < 16; ++t) {
+      const int r = 4 * t + (lane >> 4), p = lane & 15;
+      const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16));
+      const int row = m0 + wm * 128 + 64 * h + r, col = n0 + wn * 64 + 4 * p;
+      if (row >= M || col >= Vd) continue;
+      if (vec && col + 3 < Vd) {
+        // streamed out: the logits are read back only by the next stage
+        __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(C + (size_t)row * Vd + col));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (col + q < Vd) C[(size_t)row * Vd + col + q] = v[q];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, float* logits, int M, int H,
@@ -730,7 +898,7 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<false, false>),
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_pingpong),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
       if (e == hipSuccess)
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<false, true>),
@@ -744,8 +912,8 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
       hipLaunchKernelGGL((k1_big<false, true>), dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits, M,
                          H, Vd, mtiles, ntiles, wx, xout, KvEpilogue{});
     else
-      hipLaunchKernelGGL((k1_big<false, false>), dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits,
-                         M, H, Vd, mtiles, ntiles, nullptr, nullptr, KvEpilogue{});
+      hipLaunchKernelGGL(k1_pingpong, dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits, M, H, Vd,
+                         mtiles, ntiles);
   } else {
     const int mtiles = (M + TBM - 1) / TBM, ntiles = (Vt + TBN - 1) / TBN;
     const int total = mtiles * ntiles;
