@@ -90,15 +90,19 @@ __device__ __forceinline__ float neg_gumbel2(uint32_t w) {
 // must be emitted for the host-side switch below)
 // LDS layout of one W2 chunk (64 rows of P = 4 KS 16-byte pieces).  Rows sit in P
 // groups of 64 / P rows; a group is 1 KB, written by one global->LDS DMA
-// instruction, and groups are 1040 bytes apart.  A-fragment f, row m lives in
-// group grp(f, m), position pos(f, m) of it.  The 16 rows that one MFMA fragment
-// reads at a k offset land in 16 distinct 16-byte bank groups, and every lane
-// reaches all its fragments and k steps from one base address plus immediates.
+// instruction.  A-fragment f, row m lives in group grp(f, m), position pos(f, m) of
+// it, and every lane reaches all its fragments and k steps from one base address
+// plus immediates.  A 16-byte LDS read is served 32 lanes at a time over 128 banks
+// (512 bytes): lanes 0-31 of a fragment read rows 0-15 at pieces g = 0, 1 (lanes
+// 32-63 at g = 2, 3).  With P >= 16 a fragment's rows are consecutive groups, so
+// groups 1056 bytes apart (32 mod 512) put those 32 pieces in 32 distinct 16-byte
+// bank groups; with P < 16 no group stride does (rows share groups), and 1040 keeps
+// the conflicts two-way.
 template <int P>
 struct ChunkLds {
   static constexpr int kRows = 64 / P;  // rows per group
   static constexpr int kPer = P >= 16 ? 1 : 16 / P;  // (P < 16) positions per fragment
-  static constexpr int kGroup = 1040;   // bytes from one group to the next
+  static constexpr int kGroup = P >= 16 ? 1056 : 1040;  // bytes from one group to the next
   static constexpr int kBytes = P * kGroup;
   __host__ __device__ static constexpr int grp(int f, int m) { return P >= 16 ? (f / kRows) * 16 + m : m % P; }
   __host__ __device__ static constexpr int pos(int f, int m) { return P >= 16 ? f % kRows : f * kPer + m / P; }
