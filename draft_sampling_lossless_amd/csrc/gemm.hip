@@ -708,9 +708,11 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
 // last reader (Y, phase 2t - 1) is done before the barrier that opens phase 2t; each
 // group waits for its half of stage t + 1 before the barrier that closes phase 2t + 1,
 // so a stage's DMA has five or six phases to land.  LDS rows are 64 bytes (32 bf16):
-// logical piece p of row r sits at slot (p + (r >> 2)) & 3, so the 16 rows of one
-// fragment read fall into 16 distinct 16-byte bank groups.  The accumulation order over
-// k is that of k1_big, so both produce the same bits.  Requires H % 32 == 0.
+// logical piece p of row r sits at slot (p + (r >> 1)) & 3.  Rotating the pieces by
+// row pairs keeps a fragment read (16 rows x 4 pieces) free of bank conflicts on
+// gfx950, which a rotation by groups of four rows is not (it read LDS at 58% of the
+// conflict-free rate).  The accumulation order over k is that of k1_big, so both
+// produce the same bits.  Requires H % 32 == 0.
 constexpr int PK = 32, PSTAGE = (BBM + BBN) * PK * 2, PNS = 4, PWOFF = BBM * PK * 2;
 static_assert(PNS * PSTAGE <= BLDS, "the ring and the epilogue share the k1_big LDS size");
 
@@ -736,7 +738,7 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
 
   // DMA: X fills the A rows, Y the W rows of a stage.  Wave w4 takes rows 64 w4 + 16 u
   // .. +15 (u = 0..3); lane L row 16 u + L / 4 of them, LDS slot L % 4, which holds
-  // logical piece (L % 4 - L / 16) & 3.  Byte offsets from the tile's first row; rows
+  // logical piece (L % 4 - L / 8) & 3.  Byte offsets from the tile's first row; rows
   // past the last are clamped to it (their outputs are never stored).
   const char* const src = grp == 0 ? reinterpret_cast<const char*>(A + (size_t)m0 * H)
                                    : reinterpret_cast<const char*>(W + (size_t)n0 * H);
@@ -745,7 +747,7 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = 64 * w4 + 16 * u + (lane >> 2);
-    const int p = ((lane & 3) - (lane >> 4)) & 3;
+    const int p = ((lane & 3) - (lane >> 3)) & 3;
     off[u] = (uint32_t)(min(r, lim) * H * 2 + p * 16);
   }
   const int dst0 = (grp == 0 ? 0 : PWOFF) + 64 * w4 * (PK * 2);
@@ -763,7 +765,7 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   // fragment reads: row 16 i + n of the wave's rows, logical piece g
-  const int slot = ((g + (n >> 2)) & 3) * 16;
+  const int slot = ((g + (n >> 1)) & 3) * 16;
   const int ard = (wm * 128 + n) * (PK * 2) + slot, brd = PWOFF + (wn * 64 + n) * (PK * 2) + slot;
   bf16x8 af[8], bf[4];
   auto read = [&](int t) {
