@@ -695,10 +695,12 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
   }
 }
 
-// The plain product at many rows: the tiles, waves and epilogue of k1_big, with the
-// two waves of each SIMD in alternating phases.  Group X = waves 0-3, group Y = waves
-// 4-7 (one of each per SIMD); the k dimension runs in BK = 32 stages through a ring of
-// four 32 KB LDS buffers:
+// The plain product at many rows: 256 x 64 NB output tiles (NB = 4 or 5 LM-head
+// fragments per wave), eight waves as in k1_big, with the two waves of each SIMD in
+// alternating phases.  Group X = waves 0-3, group Y = waves 4-7 (one of each per SIMD);
+// wave w owns hidden rows 128 (w & 1) .. +127 and LM-head rows 16 NB (w >> 1) .. +16 NB - 1
+// of the tile (8 x NB fragments).  The k dimension runs in BK = 32 stages through a
+// ring of four LDS buffers:
 //   phase 2t:   X reads stage t's fragments and issues the A rows of stage t + 3;
 //               Y runs the MFMAs of stage t - 1;
 //   phase 2t+1: X runs the MFMAs of stage t; Y reads stage t and issues the W rows of
@@ -711,16 +713,23 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
 // logical piece p of row r sits at slot (p + (r >> 1)) & 3.  Rotating the pieces by
 // row pairs keeps a fragment read (16 rows x 4 pieces) free of bank conflicts on
 // gfx950, which a rotation by groups of four rows is not (it read LDS at 58% of the
-// conflict-free rate).  The accumulation order over k is that of k1_big, so both
-// produce the same bits.  Requires H % 32 == 0.
-constexpr int PK = 32, PSTAGE = (BBM + BBN) * PK * 2, PNS = 4, PWOFF = BBM * PK * 2;
-static_assert(PNS * PSTAGE <= BLDS, "the ring and the epilogue share the k1_big LDS size");
+// conflict-free rate).  NB = 5 does 40 MFMAs per phase instead of 32 against the same
+// barrier and moves fewer LDS and L2 bytes per flop.  The accumulation order over k is
+// that of k1_big, so every tiling produces the same bits.  Requires H % 32 == 0.
+constexpr int PK = 32, PNS = 4, PWOFF = BBM * PK * 2;
+__host__ __device__ constexpr int pp_stage(int NB) { return (BBM + 64 * NB) * PK * 2; }
+__host__ __device__ constexpr int pp_lds(int NB) { return PNS * pp_stage(NB); }
+static_assert(pp_lds(4) >= BLDS && pp_lds(5) >= BLDS, "the epilogue stages 8 x 16 KB in the ring");
 
+template <int NB>
 __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                    float* __restrict__ C, int M, int H, int Vd, int mtiles,
                                                    int ntiles) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int kGroupM = 4;
+  constexpr int TN = 64 * NB;           // LM-head rows per tile
+  constexpr int PSTAGE = pp_stage(NB);
+  constexpr int NI = NB;                // DMA instructions per wave and stage of group Y (X: 4)
   const int total = mtiles * ntiles;
   const int per_xcd = (total + 7) / 8;
   const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -728,7 +737,7 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
   const int group = lin / (kGroupM * ntiles), first_m = group * kGroupM;
   const int gm = min(mtiles - first_m, kGroupM), within = lin - group * kGroupM * ntiles;
   const int mt = first_m + within % gm, nt = within / gm;
-  const int m0 = mt * BBM, n0 = nt * BBN;
+  const int m0 = mt * BBM, n0 = nt * TN;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -736,42 +745,45 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
   const int wm = wave & 1, wn = wave >> 1;  // hidden-row half, LM-head-row quarter
   const int n = lane & 15, g = lane >> 4;
 
-  // DMA: X fills the A rows, Y the W rows of a stage.  Wave w4 takes rows 64 w4 + 16 u
-  // .. +15 (u = 0..3); lane L row 16 u + L / 4 of them, LDS slot L % 4, which holds
-  // logical piece (L % 4 - L / 8) & 3.  Byte offsets from the tile's first row; rows
-  // past the last are clamped to it (their outputs are never stored).
+  // DMA: X fills the A rows, Y the W rows of a stage.  X wave w4 takes A rows
+  // 64 w4 + 16 u .. +15 (u = 0..3), Y wave w4 W rows 16 NB w4 + 16 u .. +15
+  // (u = 0..NB-1); lane L row 16 u + L / 4 of them, LDS slot L % 4, which holds
+  // logical piece (L % 4 - L / 8) & 3 (both row bases are multiples of 8).  Byte
+  // offsets from the tile's first row; rows past the last are clamped to it (their
+  // outputs are never stored).
   const char* const src = grp == 0 ? reinterpret_cast<const char*>(A + (size_t)m0 * H)
                                    : reinterpret_cast<const char*>(W + (size_t)n0 * H);
   const int lim = grp == 0 ? M - 1 - m0 : Vd - 1 - n0;
-  uint32_t off[4];
+  const int rbase = grp == 0 ? 64 * w4 : 16 * NB * w4;
+  uint32_t off[NI];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 64 * w4 + 16 * u + (lane >> 2);
+  for (int u = 0; u < NI; ++u) {
+    const int r = rbase + 16 * u + (lane >> 2);
     const int p = ((lane & 3) - (lane >> 3)) & 3;
     off[u] = (uint32_t)(min(r, lim) * H * 2 + p * 16);
   }
-  const int dst0 = (grp == 0 ? 0 : PWOFF) + 64 * w4 * (PK * 2);
+  const int dst0 = (grp == 0 ? 0 : PWOFF) + rbase * (PK * 2);
   auto issue = [&](int t) {
     char* st = smem + (t % PNS) * PSTAGE + dst0;
     const char* sk = src + t * PK * 2;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      dma16_g(reinterpret_cast<const uint16_t*>(sk + off[u]), st + 16 * u * (PK * 2));
+    for (int u = 0; u < NI; ++u)
+      if (grp == 1 || u < 4) dma16_g(reinterpret_cast<const uint16_t*>(sk + off[u]), st + 16 * u * (PK * 2));
   };
 
-  floatx4 acc[8][4];
+  floatx4 acc[8][NB];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   // fragment reads: row 16 i + n of the wave's rows, logical piece g
   const int slot = ((g + (n >> 1)) & 3) * 16;
-  const int ard = (wm * 128 + n) * (PK * 2) + slot, brd = PWOFF + (wn * 64 + n) * (PK * 2) + slot;
-  bf16x8 af[8], bf[4];
+  const int ard = (wm * 128 + n) * (PK * 2) + slot, brd = PWOFF + (wn * 16 * NB + n) * (PK * 2) + slot;
+  bf16x8 af[8], bf[NB];
   auto read = [&](int t) {
     const char* st = smem + (t % PNS) * PSTAGE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
       bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + brd + j * 16 * (PK * 2)));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -782,16 +794,23 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
   };
-  // wait until this wave's DMA of stage s has landed, stages up to `last` issued (four
-  // instructions each, completing in order)
+  // wait until this wave's DMA of stage s has landed, stages up to `last` issued (n
+  // instructions each, completing in order; n = 4 for X, NB for Y)
   auto wait_stage = [&](int s, int last) {
     const int after = last - s;
-    if (after >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (after == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (grp == 0 || NB == 4) {
+      if (after >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (after == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      static_assert(NB == 4 || NB == 5, "the waits below count five instructions per stage");
+      if (after >= 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      else if (after == 1) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
   };
 
   const int KT = H / PK;
@@ -831,11 +850,13 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
   }
 
   // Every stage has been read and no DMA is in flight (X passed the last common
-  // barrier after Y's last reads; Y's last MFMAs touch registers only): each wave
-  // stages its 128 x 64 block in its own 16 KB of the ring, in two halves of 64 rows,
-  // and writes whole 256-byte row pieces.
+  // barrier after Y's last reads; Y's last MFMAs touch registers only).  Fragments
+  // j = 0..3 of each wave (128 x 64) are staged in the wave's own 16 KB of the ring,
+  // in two halves of 64 rows, and leave as whole 256-byte row pieces; fragment j = 4
+  // (NB = 5) is stored straight from the accumulators, 64 bytes per row.
   char* stage = smem + wave * 16384;
   const bool vec = (Vd % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
+  const int cbase = n0 + wn * 16 * NB;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -849,7 +870,7 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
     for (int t = 0; t < 16; ++t) {
       const int r = 4 * t + (lane >> 4), p = lane & 15;
       const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16));
-      const int row = m0 + wm * 128 + 64 * h + r, col = n0 + wn * 64 + 4 * p;
+      const int row = m0 + wm * 128 + 64 * h + r, col = cbase + 4 * p;
       if (row >= M || col >= Vd) continue;
       if (vec && col + 3 < Vd) {
         // streamed out: the logits are read back only by the next stage
@@ -861,6 +882,48 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
       }
     }
   }
+  if constexpr (NB == 5) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = m0 + wm * 128 + 16 * i + n, col = cbase + 64 + 4 * g;
+      if (row >= M || col >= Vd) continue;
+      if (vec && col + 3 < Vd) {
+        *reinterpret_cast<floatx4*>(C + (size_t)row * Vd + col) = acc[i][4];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (col + q < Vd) C[(size_t)row * Vd + col + q] = acc[i][4][q];
+      }
+    }
+  }
+}
+
+// Fragments per wave for the plain product: the one with fewer fragment-waves of tiles
+// over the chip (ties: five, which does more MFMAs per barrier)
+int pingpong_nb(int M, int Vd, int cus) {
+  const long mt = (M + BBM - 1) / BBM;
+  const long w4 = (mt * ((Vd + 255) / 256) + cus - 1) / cus * 4;
+  const long w5 = (mt * ((Vd + 319) / 320) + cus - 1) / cus * 5;
+  return w5 <= w4 ? 5 : 4;
+}
+
+template <int NB>
+hipError_t launch_pingpong(const uint16_t* hidden, const uint16_t* lm_head, float* logits, int M, int H, int Vd,
+                           hipStream_t stream) {
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_pingpong<NB>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, pp_lds(NB));
+    if (e != hipSuccess) return e;
+    attr_set[dev] = true;
+  }
+  const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vd + 64 * NB - 1) / (64 * NB);
+  const int per_xcd = (mtiles * ntiles + 7) / 8;
+  hipLaunchKernelGGL(k1_pingpong<NB>, dim3(per_xcd * 8), dim3(512), pp_lds(NB), stream, hidden, lm_head, logits, M,
+                     H, Vd, mtiles, ntiles);
+  return hipSuccess;
 }
 
 }  // namespace
@@ -896,26 +959,26 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
     else
       hipLaunchKernelGGL((k1_skinny<FR, 4>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd, wx, xout);
   } else if (H % BBK == 0) {
+    if (!wx) {
+      const hipError_t e = pingpong_nb(M, Vd, cu_count()) == 5
+                               ? launch_pingpong<5>(hidden, lm_head, logits, M, H, Vd, stream)
+                               : launch_pingpong<4>(hidden, lm_head, logits, M, H, Vd, stream);
+      if (e != hipSuccess) return e;
+      return hipGetLastError();
+    }
     static bool attr_set[64] = {false};
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_pingpong),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<false, true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<false, true>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
       if (e != hipSuccess) return e;
       attr_set[dev] = true;
     }
     const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vt + BBN - 1) / BBN;
     const int per_xcd = (mtiles * ntiles + 7) / 8;
-    if (wx)
-      hipLaunchKernelGGL((k1_big<false, true>), dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits, M,
-                         H, Vd, mtiles, ntiles, wx, xout, KvEpilogue{});
-    else
-      hipLaunchKernelGGL(k1_pingpong, dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits, M, H, Vd,
-                         mtiles, ntiles);
+    hipLaunchKernelGGL((k1_big<false, true>), dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits, M,
+                       H, Vd, mtiles, ntiles, wx, xout, KvEpilogue{});
   } else {
     const int mtiles = (M + TBM - 1) / TBM, ntiles = (Vt + TBN - 1) / TBN;
     const int total = mtiles * ntiles;

@@ -63,7 +63,11 @@ def test_race_exponentials_bit_exact(n, pos, req, tag):
                                     (16, 512, 393216), (16, 512, 400000),
                                     # big tiles with Vd % 4 = 1, 2, 3: rows of the output not
                                     # 16-byte aligned, the epilogue's scalar stores
-                                    (130, 128, 1001), (260, 256, 1002), (333, 192, 771)])
+                                    (130, 128, 1001), (260, 256, 1002), (333, 192, 771),
+                                    # enough tiles for five LM-head fragments per wave (256 x 320
+                                    # tiles): a partial last row tile and last column tile, with
+                                    # and without 16-byte aligned output rows
+                                    (600, 128, 100001), (600, 128, 100000)])
 def test_draft_logits_small(M, H, Vd):
     say(f"draft_logits M={M} H={H} Vd={Vd}")
     g = np.random.default_rng(M * 7 + H)
@@ -604,7 +608,8 @@ def test_choose_k_scans_past_a_local_maximum_on_gpu():
     (5, 3, 264, 100, 100, 8),            # H not a multiple of 64: the tiled GEMM
     (256, 16, 4096, 4096, 4096, 64),     # Vd a multiple of 256: the extra row opens a new column tile
     (40, 4, 512, 8192, 2048, 32),        # reduced vocabulary, skinny GEMM
-    (12, 2, 4096, 1024, 1024, 16)])      # several requests in the few-request kernel
+    (12, 2, 4096, 1024, 1024, 16),       # several requests in the few-request kernel
+    (64, 8, 256, 151936, 151936, 16)])   # the plain product with 256 x 320 tiles, the extra row with 256 x 256
 def test_confidence_fused_parity(B, N, H, V, Vd, r):
     """The confidence head inside stages 1 and 2: w_h as one more LM-head row (h_dot), the
     embedding part and the sigmoid inside the Markov loop.  Against the oracle's head on the
