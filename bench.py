@@ -303,7 +303,7 @@ def k1_work(w):
     return bytes_, flops
 
 
-def k1_roofline(w, k1_ms, variant, extra_row=False):
+def k1_roofline(w, k1_ms, variant):
     bytes_, flops = k1_work(w)
     # arithmetic intensity vs the ridge of the chip decides the bound
     ridge = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -318,10 +318,8 @@ def k1_roofline(w, k1_ms, variant, extra_row=False):
     if w.M <= 16 and w.H % 512 == 0 and w.H <= 4096:
         roof["kernel"] = "draft_logits (k1_stream)"
     else:
-        # (with the confidence head's extra LM-head row the many-row product is k1_big)
         roof["kernel"] = ("draft_logits (k1_skinny)" if w.M <= 64 else
-                          "draft_logits (k1_tiled)" if w.H % 64 else
-                          "draft_logits (k1_big)" if extra_row else "draft_logits (k1_pingpong)")
+                          "draft_logits (k1_tiled)" if w.H % 64 else "draft_logits (k1_pingpong)")
     roof["traffic"] = measured_traffic("draft_logits", w, variant)
     if roof["traffic"]:
         roof["traffic_gbs"] = round(roof["traffic"] / (k1_ms * 1e-3) / 1e9, 1)
@@ -598,8 +596,7 @@ def run(args, w, path, torch):
     positions = w.B * w.N
     value = positions / (ms_per_step * 1e-3)
     k2_bytes, k3_bytes = stage_bytes(w, path.accepted.cpu().numpy(), path.coupled, path.deferred)
-    roof = k1_roofline(w, stage_ms.get("draft_logits_live", stage_ms["draft_logits"]), path.variant,
-                       extra_row=path.full)
+    roof = k1_roofline(w, stage_ms.get("draft_logits_live", stage_ms["draft_logits"]), path.variant)
     if cold_ms:
         _, flops = k1_work(w)
         roof["frac_cold"] = round(flops / (cold_ms["draft_logits"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4) \

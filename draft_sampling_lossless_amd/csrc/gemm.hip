@@ -14,13 +14,12 @@
 //  * skinny (other M <= 64): each wave owns 16*FR vocabulary rows and streams them
 //    straight from global memory into MFMA B fragments; the hidden rows (A
 //    fragments) come from L1/L2.  No LDS.
-//  * big (M > 64, H % 64 == 0): MFMA-bound.  256 x 256 output tiles, 8 waves (two
-//    per SIMD), each a 128 x 64 block; the output leaves through LDS in whole rows.
-//    The plain product (k1_pingpong) runs the two waves of a SIMD in alternating
-//    phases over a ring of four BK = 32 stages; the forms with the extra row and
-//    the context-KV product (k1_big) keep BK = 64 in two stages; the latter's
-//    epilogue writes the normalised, rotated K and the V heads to the caches in
-//    bf16.
+//  * ping-pong (M > 64, H % 64 == 0): MFMA-bound.  256 x 256 or 256 x 320 output
+//    tiles, 8 waves (two per SIMD), each a 128 x 64 or 128 x 80 block, the two
+//    waves of a SIMD in alternating phases over a ring of four BK = 32 stages; the
+//    output leaves through LDS in whole rows.  The context-KV product (k1_kv) uses
+//    the same eight waves with BK = 64 in two stages, and its epilogue writes the
+//    normalised, rotated K and the V heads to the caches in bf16.
 //  * tiled (other M > 64): 128 x 128 output tiles, BK = 64, both operands staged
 //    through double-buffered LDS; 4 waves, each a 64 x 64 block of 16x16 MFMA
 //    fragments.  Both MFMA tilings take a grouped tile order (a few row tiles at
@@ -371,7 +370,7 @@ __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, 
 
 // ------------------------------------------------------------------ big tiles
 
-// 256 x 256 output tiles, BK = 64, a two-stage LDS ring filled by global->LDS DMA
+// k1_kv: 256 x 256 output tiles, BK = 64, a two-stage LDS ring filled by global->LDS DMA
 // (every load instruction moves 8 rows x 128 B).  Eight waves, two per SIMD, each
 // computing 128 hidden rows x 64 LM-head rows (8 x 4 fragments of 16x16, 128
 // accumulators): while one wave of a SIMD waits on its fragment reads or the barrier,
@@ -380,10 +379,8 @@ __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, 
 // fall into 16 distinct bank groups.  The LM-head fragment is the MFMA's first
 // operand, so a lane's four accumulators are four adjacent output columns of one row,
 // and the MFMAs of a half step run at raised wave priority.  The epilogue stages each
-// wave's 128 x 64 fp32 block through the (then idle) operand ring in two halves and
-// stores whole 256-byte row pieces: storing 16-lane 64-byte pieces straight from the
-// accumulators left the output write exposed for ~12% of a launch at the admission
-// shape.  Requires H % 64 == 0.
+// wave's 128 x 64 fp32 block through the (then idle) operand ring in two halves for
+// the cache-writing pass.  Requires H % 64 == 0.
 constexpr int BBM = 256, BBN = 256, BBK = 64, BNS = 2;
 constexpr int BSTAGE = (BBM + BBN) * BBK * 2;  // 64 KB
 constexpr int BLDS = BNS * BSTAGE;             // 128 KB
@@ -496,15 +493,12 @@ __device__ __forceinline__ void kv_epilogue_half(const char* smem, int h, int m0
   }
 }
 
-// kKV: the context-KV product (C, wx, xout unused): the epilogue of kv_epilogue_half.
-// kWx: with the extra row (wx, xout set); that form reads each half step's fragments
-// just before its MFMAs (the extra row's addressing leaves no registers for reading
-// both at once).
-template <bool kKV, bool kWx>
-__global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-                                              float* __restrict__ C, int M, int H, int Vd, int mtiles,
-                                              int ntiles, const uint16_t* __restrict__ wx,
-                                              float* __restrict__ xout, const KvEpilogue ep) {
+// The context-KV product: the normalised context states (A, M x H) times every layer's
+// fused K/V weights (W, Vd x H, Vd = L * 2 * nkv * 128 columns), whose epilogue
+// (kv_epilogue_half) adds the bias, normalises and rotates the K heads and writes both
+// caches in bf16.
+__global__ __launch_bounds__(512) void k1_kv(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                                             int M, int H, int Vd, int mtiles, int ntiles, const KvEpilogue ep) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int kGroupM = 4;
   const int total = mtiles * ntiles;
@@ -520,23 +514,22 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // hidden-row half, LM-head-row quarter
   const int n = lane & 15, g = lane >> 4;
-  const int Vt = Vd + (kWx ? 1 : 0);        // LM-head rows including the extra one
 
   // DMA: instruction u (0..3) for wave w fills A rows (and W rows) 32 w + 8 u .. +7;
   // lane L takes row 8 u + L / 8 of the wave's 32, physical piece L % 8, which holds
   // logical piece (L % 8) ^ ((row >> 1) & 7).  On an inner tile (every row a real
-  // row, the extra row not among them) waves 0-3 issue the instructions of waves w and
-  // w + 4 (rows + 128, the same swizzle) and waves 4-7 issue none, so the second wave
-  // of each SIMD reaches its MFMAs without waiting on the DMA issue; the addresses are
-  // 32-bit offsets from the tile's row bases.  Edge tiles: every wave its own rows,
-  // clamped (rows past the last: a valid row, never stored), the extra row from wx.
+  // row) waves 0-3 issue the instructions of waves w and w + 4 (rows + 128, the same
+  // swizzle) and waves 4-7 issue none, so the second wave of each SIMD reaches its
+  // MFMAs without waiting on the DMA issue; the addresses are 32-bit offsets from the
+  // tile's row bases.  Edge tiles: every wave its own rows, clamped (rows past the
+  // last: a valid row, never stored).
   const bool inner = (m0 + BBM <= M) && (n0 + BBN <= Vd);
   const uint16_t* const Ab = A + (size_t)m0 * H;
   const uint16_t* const Wb = W + (size_t)n0 * H;
   const uint32_t poff = (uint32_t)(128 * H);
   // per-lane element offsets of the DMA rows from the tile's row bases: inner tiles
   // rows of wave w & 3 (the partner's are 128 rows on, the same swizzle); edge tiles
-  // this wave's rows, clamped.  kWx: the extra row is read from wx instead.
+  // this wave's rows, clamped.
   const int w0 = inner ? (wave & 3) : wave;
   uint32_t aoff[4], woff[4];
 #pragma unroll
@@ -564,13 +557,6 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         dma16_g(ak + aoff[u], st + (wave * 32 + 8 * u) * 128);
-        if constexpr (kWx) {
-          const int r = wave * 32 + 8 * u + (lane >> 3);
-          if (n0 + r >= Vd) {   // the extra row (and rows past it, clamped to it)
-            dma16_g(wx + kt * BBK + ((lane & 7) ^ ((r >> 1) & 7)) * 8, st + BBM * 128 + (wave * 32 + 8 * u) * 128);
-            continue;
-          }
-        }
         dma16_g(wk + woff[u], st + BBM * 128 + (wave * 32 + 8 * u) * 128);
       }
     }
@@ -595,29 +581,6 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (kt + 1 < KT) issue(kt + 1);
     const char* st = smem + (kt % BNS) * BSTAGE;
-    if constexpr (kWx) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int pc = ((4 * s + g) ^ swz) * 16;
-        bf16x8 af[8], bf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + brow + j * 16 * 128 + pc));
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + arow + i * 16 * 128 + pc));
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_s_setprio(0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      continue;
-    }
     // the fragments of both half steps are requested at once: the reads of the second
     // run under the first's MFMAs
     bf16x8 af[2][8], bf[2][4];
@@ -650,26 +613,9 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
   // p of row r at p ^ (r & 7)) and writes its block in two halves of 64 rows.
   asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   char* stage = smem + wave * 16384;
-  if constexpr (kKV) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (h == 1) __syncthreads();   // every (row, head) item of half 0 is done with the staging
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 16 * i + n, p = 4 * j + g;
-          *reinterpret_cast<floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16)) = acc[4 * h + i][j];
-        }
-      __syncthreads();
-      kv_epilogue_half(smem, h, m0, n0, M, Vd, ep);
-    }
-    return;
-  }
-  // whole float4 stores need 16-byte aligned rows
-  const bool vec = (Vd % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
+    if (h == 1) __syncthreads();   // every (row, head) item of half 0 is done with the staging
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -677,26 +623,13 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
         const int r = 16 * i + n, p = 4 * j + g;
         *reinterpret_cast<floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16)) = acc[4 * h + i][j];
       }
-#pragma unroll 4
-    for (int t = 0; t < 16; ++t) {
-      const int r = 4 * t + (lane >> 4), p = lane & 15;
-      const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16));
-      const int row = m0 + wm * 128 + 64 * h + r, col = n0 + wn * 64 + 4 * p;
-      if (row >= M || col >= Vt) continue;
-      if (vec && col + 3 < Vd) {
-        // streamed out: the logits are read back only by the next stage
-        __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(C + (size_t)row * Vd + col));
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (col + q < Vt) put_out(C, xout, row, col + q, Vd, v[q]);
-      }
-    }
+    __syncthreads();
+    kv_epilogue_half(smem, h, m0, n0, M, Vd, ep);
   }
 }
 
 // The plain product at many rows: 256 x 64 NB output tiles (NB = 4 or 5 LM-head
-// fragments per wave), eight waves as in k1_big, with the two waves of each SIMD in
+// fragments per wave), eight waves as in k1_kv, with the two waves of each SIMD in
 // alternating phases.  Group X = waves 0-3, group Y = waves 4-7 (one of each per SIMD);
 // wave w owns hidden rows 128 (w & 1) .. +127 and LM-head rows 16 NB (w >> 1) .. +16 NB - 1
 // of the tile (8 x NB fragments).  The k dimension runs in BK = 32 stages through a
@@ -715,7 +648,8 @@ __global__ __launch_bounds__(512) void k1_big(const uint16_t* __restrict__ A, co
 // gfx950, which a rotation by groups of four rows is not (it read LDS at 58% of the
 // conflict-free rate).  NB = 5 does 40 MFMAs per phase instead of 32 against the same
 // barrier and moves fewer LDS and L2 bytes per flop.  The accumulation order over k is
-// that of k1_big, so every tiling produces the same bits.  Requires H % 32 == 0.
+// that of every other tiling here, so the extra row (wx) and the two tile widths
+// leave the logits' bits unchanged.  Requires H % 32 == 0.
 constexpr int PK = 32, PNS = 4, PWOFF = BBM * PK * 2;
 __host__ __device__ constexpr int pp_stage(int NB) { return (BBM + 64 * NB) * PK * 2; }
 __host__ __device__ constexpr int pp_lds(int NB) { return PNS * pp_stage(NB); }
@@ -724,7 +658,8 @@ static_assert(pp_lds(4) >= BLDS && pp_lds(5) >= BLDS, "the epilogue stages 8 x 1
 template <int NB>
 __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                    float* __restrict__ C, int M, int H, int Vd, int mtiles,
-                                                   int ntiles) {
+                                                   int ntiles, const uint16_t* __restrict__ wx,
+                                                   float* __restrict__ xout) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int kGroupM = 4;
   constexpr int TN = 64 * NB;           // LM-head rows per tile
@@ -748,27 +683,28 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
   // DMA: X fills the A rows, Y the W rows of a stage.  X wave w4 takes A rows
   // 64 w4 + 16 u .. +15 (u = 0..3), Y wave w4 W rows 16 NB w4 + 16 u .. +15
   // (u = 0..NB-1); lane L row 16 u + L / 4 of them, LDS slot L % 4, which holds
-  // logical piece (L % 4 - L / 8) & 3 (both row bases are multiples of 8).  Byte
-  // offsets from the tile's first row; rows past the last are clamped to it (their
-  // outputs are never stored).
-  const char* const src = grp == 0 ? reinterpret_cast<const char*>(A + (size_t)m0 * H)
-                                   : reinterpret_cast<const char*>(W + (size_t)n0 * H);
-  const int lim = grp == 0 ? M - 1 - m0 : Vd - 1 - n0;
+  // logical piece (L % 4 - L / 8) & 3 (both row bases are multiples of 8).  Each lane
+  // keeps a pointer per instruction: hidden rows past the last are clamped to it, and
+  // LM-head rows from Vd on are the extra row wx if there is one, else row Vd - 1
+  // (outputs past the last column are never stored).
   const int rbase = grp == 0 ? 64 * w4 : 16 * NB * w4;
-  uint32_t off[NI];
+  const char* srcp[NI];
 #pragma unroll
   for (int u = 0; u < NI; ++u) {
     const int r = rbase + 16 * u + (lane >> 2);
     const int p = ((lane & 3) - (lane >> 3)) & 3;
-    off[u] = (uint32_t)(min(r, lim) * H * 2 + p * 16);
+    const uint16_t* row;
+    if (grp == 0) row = A + (size_t)min(m0 + r, M - 1) * H;
+    else row = (n0 + r < Vd) ? W + (size_t)(n0 + r) * H : (wx != nullptr ? wx : W + (size_t)(Vd - 1) * H);
+    srcp[u] = reinterpret_cast<const char*>(row) + p * 16;
   }
   const int dst0 = (grp == 0 ? 0 : PWOFF) + rbase * (PK * 2);
   auto issue = [&](int t) {
     char* st = smem + (t % PNS) * PSTAGE + dst0;
-    const char* sk = src + t * PK * 2;
 #pragma unroll
     for (int u = 0; u < NI; ++u)
-      if (grp == 1 || u < 4) dma16_g(reinterpret_cast<const uint16_t*>(sk + off[u]), st + 16 * u * (PK * 2));
+      if (grp == 1 || u < 4)
+        dma16_g(reinterpret_cast<const uint16_t*>(srcp[u] + t * PK * 2), st + 16 * u * (PK * 2));
   };
 
   floatx4 acc[8][NB];
@@ -853,10 +789,12 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
   // barrier after Y's last reads; Y's last MFMAs touch registers only).  Fragments
   // j = 0..3 of each wave (128 x 64) are staged in the wave's own 16 KB of the ring,
   // in two halves of 64 rows, and leave as whole 256-byte row pieces; fragment j = 4
-  // (NB = 5) is stored straight from the accumulators, 64 bytes per row.
+  // (NB = 5) is stored straight from the accumulators, 64 bytes per row.  Column Vd
+  // (the extra row's output) goes to xout.
   char* stage = smem + wave * 16384;
   const bool vec = (Vd % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
   const int cbase = n0 + wn * 16 * NB;
+  const int Vt = Vd + (wx != nullptr ? 1 : 0);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -871,14 +809,14 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
       const int r = 4 * t + (lane >> 4), p = lane & 15;
       const floatx4 v = *reinterpret_cast<const floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16));
       const int row = m0 + wm * 128 + 64 * h + r, col = cbase + 4 * p;
-      if (row >= M || col >= Vd) continue;
+      if (row >= M || col >= Vt) continue;
       if (vec && col + 3 < Vd) {
         // streamed out: the logits are read back only by the next stage
         __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(C + (size_t)row * Vd + col));
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (col + q < Vd) C[(size_t)row * Vd + col + q] = v[q];
+          if (col + q < Vt) put_out(C, xout, row, col + q, Vd, v[q]);
       }
     }
   }
@@ -886,13 +824,13 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = m0 + wm * 128 + 16 * i + n, col = cbase + 64 + 4 * g;
-      if (row >= M || col >= Vd) continue;
+      if (row >= M || col >= Vt) continue;
       if (vec && col + 3 < Vd) {
         *reinterpret_cast<floatx4*>(C + (size_t)row * Vd + col) = acc[i][4];
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (col + q < Vd) C[(size_t)row * Vd + col + q] = acc[i][4][q];
+          if (col + q < Vt) put_out(C, xout, row, col + q, Vd, acc[i][4][q]);
       }
     }
   }
@@ -909,7 +847,7 @@ int pingpong_nb(int M, int Vd, int cus) {
 
 template <int NB>
 hipError_t launch_pingpong(const uint16_t* hidden, const uint16_t* lm_head, float* logits, int M, int H, int Vd,
-                           hipStream_t stream) {
+                           const uint16_t* wx, float* xout, hipStream_t stream) {
   static bool attr_set[64] = {false};
   int dev = 0;
   (void)hipGetDevice(&dev);
@@ -919,10 +857,11 @@ hipError_t launch_pingpong(const uint16_t* hidden, const uint16_t* lm_head, floa
     if (e != hipSuccess) return e;
     attr_set[dev] = true;
   }
-  const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vd + 64 * NB - 1) / (64 * NB);
+  const int Vt = Vd + (wx != nullptr ? 1 : 0);
+  const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vt + 64 * NB - 1) / (64 * NB);
   const int per_xcd = (mtiles * ntiles + 7) / 8;
   hipLaunchKernelGGL(k1_pingpong<NB>, dim3(per_xcd * 8), dim3(512), pp_lds(NB), stream, hidden, lm_head, logits, M,
-                     H, Vd, mtiles, ntiles);
+                     H, Vd, mtiles, ntiles, wx, xout);
   return hipSuccess;
 }
 
@@ -959,26 +898,10 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
     else
       hipLaunchKernelGGL((k1_skinny<FR, 4>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd, wx, xout);
   } else if (H % BBK == 0) {
-    if (!wx) {
-      const hipError_t e = pingpong_nb(M, Vd, cu_count()) == 5
-                               ? launch_pingpong<5>(hidden, lm_head, logits, M, H, Vd, stream)
-                               : launch_pingpong<4>(hidden, lm_head, logits, M, H, Vd, stream);
-      if (e != hipSuccess) return e;
-      return hipGetLastError();
-    }
-    static bool attr_set[64] = {false};
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<false, true>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
-      if (e != hipSuccess) return e;
-      attr_set[dev] = true;
-    }
-    const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vt + BBN - 1) / BBN;
-    const int per_xcd = (mtiles * ntiles + 7) / 8;
-    hipLaunchKernelGGL((k1_big<false, true>), dim3(per_xcd * 8), dim3(512), BLDS, stream, hidden, lm_head, logits, M,
-                       H, Vd, mtiles, ntiles, wx, xout, KvEpilogue{});
+    const hipError_t e = pingpong_nb(M, Vt, cu_count()) == 5
+                             ? launch_pingpong<5>(hidden, lm_head, logits, M, H, Vd, wx, xout, stream)
+                             : launch_pingpong<4>(hidden, lm_head, logits, M, H, Vd, wx, xout, stream);
+    if (e != hipSuccess) return e;
   } else {
     const int mtiles = (M + TBM - 1) / TBM, ntiles = (Vt + TBN - 1) / TBN;
     const int total = mtiles * ntiles;
@@ -998,15 +921,15 @@ hipError_t launch_kv_product(const uint16_t* normed, const uint16_t* kv_w, int M
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_big<true, false>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_kv),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
     if (e != hipSuccess) return e;
     attr_set[dev] = true;
   }
   const int mtiles = (M + BBM - 1) / BBM, ntiles = (ncols + BBN - 1) / BBN;
   const int per_xcd = (mtiles * ntiles + 7) / 8;
-  hipLaunchKernelGGL((k1_big<true, false>), dim3(per_xcd * 8), dim3(512), BLDS, stream, normed, kv_w, nullptr, M, Hd, ncols,
-                     mtiles, ntiles, nullptr, nullptr, ep);
+  hipLaunchKernelGGL(k1_kv, dim3(per_xcd * 8), dim3(512), BLDS, stream, normed, kv_w, M, Hd, ncols, mtiles, ntiles,
+                     ep);
   return hipGetLastError();
 }
 
