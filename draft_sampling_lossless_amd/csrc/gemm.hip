@@ -17,9 +17,9 @@
 //  * ping-pong (M > 64, H % 64 == 0): MFMA-bound.  256 x 256 or 256 x 320 output
 //    tiles, 8 waves (two per SIMD), each a 128 x 64 or 128 x 80 block, the two
 //    waves of a SIMD in alternating phases over a ring of four BK = 32 stages; the
-//    output leaves through LDS in whole rows.  The context-KV product (k1_kv) uses
-//    the same eight waves with BK = 64 in two stages, and its epilogue writes the
-//    normalised, rotated K and the V heads to the caches in bf16.
+//    output leaves through LDS in whole rows.  The context-KV product runs the same
+//    kernel at 256 x 256 with an epilogue that writes the normalised, rotated K and
+//    the V heads to the caches in bf16.
 //  * tiled (other M > 64): 128 x 128 output tiles, BK = 64, both operands staged
 //    through double-buffered LDS; 4 waves, each a 64 x 64 block of 16x16 MFMA
 //    fragments.  Both MFMA tilings take a grouped tile order (a few row tiles at
@@ -370,20 +370,10 @@ __global__ __launch_bounds__(256) void k1_tiled(const uint16_t* __restrict__ A, 
 
 // ------------------------------------------------------------------ big tiles
 
-// k1_kv: 256 x 256 output tiles, BK = 64, a two-stage LDS ring filled by global->LDS DMA
-// (every load instruction moves 8 rows x 128 B).  Eight waves, two per SIMD, each
-// computing 128 hidden rows x 64 LM-head rows (8 x 4 fragments of 16x16, 128
-// accumulators): while one wave of a SIMD waits on its fragment reads or the barrier,
-// the other's MFMAs run.  LDS row = 64 k = eight 16-byte pieces; logical piece q of row
-// r sits at piece q ^ ((r >> 1) & 7), so the 16 rows one fragment reads at a k offset
-// fall into 16 distinct bank groups.  The LM-head fragment is the MFMA's first
-// operand, so a lane's four accumulators are four adjacent output columns of one row,
-// and the MFMAs of a half step run at raised wave priority.  The epilogue stages each
-// wave's 128 x 64 fp32 block through the (then idle) operand ring in two halves for
-// the cache-writing pass.  Requires H % 64 == 0.
-constexpr int BBM = 256, BBN = 256, BBK = 64, BNS = 2;
-constexpr int BSTAGE = (BBM + BBN) * BBK * 2;  // 64 KB
-constexpr int BLDS = BNS * BSTAGE;             // 128 KB
+// Hidden rows per tile of the many-row products; the epilogue stages each wave's
+// 128 x 64 fp32 block in 16 KB of the operand ring (8 waves: 128 KB).
+constexpr int BBM = 256;
+constexpr int BSTAGE_OUT = 8 * 16384;
 
 __device__ __forceinline__ void dma16_g(const uint16_t* src, char* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
@@ -493,143 +483,8 @@ __device__ __forceinline__ void kv_epilogue_half(const char* smem, int h, int m0
   }
 }
 
-// The context-KV product: the normalised context states (A, M x H) times every layer's
-// fused K/V weights (W, Vd x H, Vd = L * 2 * nkv * 128 columns), whose epilogue
-// (kv_epilogue_half) adds the bias, normalises and rotates the K heads and writes both
-// caches in bf16.
-__global__ __launch_bounds__(512) void k1_kv(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-                                             int M, int H, int Vd, int mtiles, int ntiles, const KvEpilogue ep) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int kGroupM = 4;
-  const int total = mtiles * ntiles;
-  const int per_xcd = (total + 7) / 8;
-  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (lin >= total) return;
-  const int group = lin / (kGroupM * ntiles), first_m = group * kGroupM;
-  const int gm = min(mtiles - first_m, kGroupM), within = lin - group * kGroupM * ntiles;
-  const int mt = first_m + within % gm, nt = within / gm;
-  const int m0 = mt * BBM, n0 = nt * BBN;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;  // hidden-row half, LM-head-row quarter
-  const int n = lane & 15, g = lane >> 4;
-
-  // DMA: instruction u (0..3) for wave w fills A rows (and W rows) 32 w + 8 u .. +7;
-  // lane L takes row 8 u + L / 8 of the wave's 32, physical piece L % 8, which holds
-  // logical piece (L % 8) ^ ((row >> 1) & 7).  On an inner tile (every row a real
-  // row) waves 0-3 issue the instructions of waves w and w + 4 (rows + 128, the same
-  // swizzle) and waves 4-7 issue none, so the second wave of each SIMD reaches its
-  // MFMAs without waiting on the DMA issue; the addresses are 32-bit offsets from the
-  // tile's row bases.  Edge tiles: every wave its own rows, clamped (rows past the
-  // last: a valid row, never stored).
-  const bool inner = (m0 + BBM <= M) && (n0 + BBN <= Vd);
-  const uint16_t* const Ab = A + (size_t)m0 * H;
-  const uint16_t* const Wb = W + (size_t)n0 * H;
-  const uint32_t poff = (uint32_t)(128 * H);
-  // per-lane element offsets of the DMA rows from the tile's row bases: inner tiles
-  // rows of wave w & 3 (the partner's are 128 rows on, the same swizzle); edge tiles
-  // this wave's rows, clamped.
-  const int w0 = inner ? (wave & 3) : wave;
-  uint32_t aoff[4], woff[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = w0 * 32 + 8 * u + (lane >> 3);
-    const int lg = (lane & 7) ^ ((r >> 1) & 7);
-    aoff[u] = (uint32_t)((min(m0 + r, M - 1) - m0) * H + lg * 8);
-    woff[u] = (uint32_t)((min(n0 + r, Vd - 1) - n0) * H + lg * 8);
-  }
-  auto issue = [&](int kt) {
-    char* st = smem + (kt % BNS) * BSTAGE;
-    const uint16_t* ak = Ab + kt * BBK;
-    const uint16_t* wk = Wb + kt * BBK;
-    if (inner) {
-      if (wave < 4) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          dma16_g(ak + aoff[u], st + (wave * 32 + 8 * u) * 128);
-          dma16_g(wk + woff[u], st + BBM * 128 + (wave * 32 + 8 * u) * 128);
-          dma16_g(ak + aoff[u] + poff, st + ((wave + 4) * 32 + 8 * u) * 128);
-          dma16_g(wk + woff[u] + poff, st + BBM * 128 + ((wave + 4) * 32 + 8 * u) * 128);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        dma16_g(ak + aoff[u], st + (wave * 32 + 8 * u) * 128);
-        dma16_g(wk + woff[u], st + BBM * 128 + (wave * 32 + 8 * u) * 128);
-      }
-    }
-  };
-
-  floatx4 acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // fragment reads: row (16 i + n) of the wave's rows, logical piece 4 s + g
-  const int swz = (n >> 1) & 7;
-  const int arow = (wm * 128 + n) * 128, brow = BBM * 128 + (wn * 64 + n) * 128;
-
-  const int KT = H / BBK;
-  issue(0);
-  for (int kt = 0; kt < KT; ++kt) {
-    // this wave's DMA instructions of stage kt are done; after the barrier every
-    // wave's are, and every wave has finished reading stage kt - 1, whose buffer
-    // stage kt + 1 reuses
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kt + 1 < KT) issue(kt + 1);
-    const char* st = smem + (kt % BNS) * BSTAGE;
-    // the fragments of both half steps are requested at once: the reads of the second
-    // run under the first's MFMAs
-    bf16x8 af[2][8], bf[2][4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int pc = ((4 * s + g) ^ swz) * 16;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[s][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + brow + j * 16 * 128 + pc));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        af[s][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + arow + i * 16 * 128 + pc));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[s][j], af[s][i], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_s_setprio(0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  // acc[i][j][q] = C[row 16 i + n][column 16 j + 4 g + q] of the wave's block.  Every
-  // wave has finished reading the ring; each takes 16 KB of it (64 rows x 256 B, piece
-  // p of row r at p ^ (r & 7)) and writes its block in two halves of 64 rows.
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  char* stage = smem + wave * 16384;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (h == 1) __syncthreads();   // every (row, head) item of half 0 is done with the staging
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * i + n, p = 4 * j + g;
-        *reinterpret_cast<floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16)) = acc[4 * h + i][j];
-      }
-    __syncthreads();
-    kv_epilogue_half(smem, h, m0, n0, M, Vd, ep);
-  }
-}
-
 // The plain product at many rows: 256 x 64 NB output tiles (NB = 4 or 5 LM-head
-// fragments per wave), eight waves as in k1_kv, with the two waves of each SIMD in
+// fragments per wave), eight waves (two per SIMD), with the two waves of each SIMD in
 // alternating phases.  Group X = waves 0-3, group Y = waves 4-7 (one of each per SIMD);
 // wave w owns hidden rows 128 (w & 1) .. +127 and LM-head rows 16 NB (w >> 1) .. +16 NB - 1
 // of the tile (8 x NB fragments).  The k dimension runs in BK = 32 stages through a
@@ -653,13 +508,19 @@ __global__ __launch_bounds__(512) void k1_kv(const uint16_t* __restrict__ A, con
 constexpr int PK = 32, PNS = 4, PWOFF = BBM * PK * 2;
 __host__ __device__ constexpr int pp_stage(int NB) { return (BBM + 64 * NB) * PK * 2; }
 __host__ __device__ constexpr int pp_lds(int NB) { return PNS * pp_stage(NB); }
-static_assert(pp_lds(4) >= BLDS && pp_lds(5) >= BLDS, "the epilogue stages 8 x 16 KB in the ring");
+static_assert(pp_lds(4) >= BSTAGE_OUT && pp_lds(5) >= BSTAGE_OUT, "the epilogue stages 8 x 16 KB in the ring");
 
-template <int NB>
+//
+// kKV (NB = 4): the context-KV product, the normalised context states (A, M x H) times
+// every layer's fused K/V weights (W, Vd = L * 2 * nkv * 128 rows); a 256-column tile
+// holds two whole heads, and the epilogue (kv_epilogue_half) adds the bias, normalises
+// and rotates the K heads and writes both caches in bf16 (C, wx, xout unused).
+template <int NB, bool kKV>
 __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                    float* __restrict__ C, int M, int H, int Vd, int mtiles,
                                                    int ntiles, const uint16_t* __restrict__ wx,
-                                                   float* __restrict__ xout) {
+                                                   float* __restrict__ xout, const KvEpilogue ep) {
+  static_assert(!kKV || NB == 4, "the cache-writing epilogue takes 256-column tiles");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int kGroupM = 4;
   constexpr int TN = 64 * NB;           // LM-head rows per tile
@@ -792,6 +653,22 @@ __global__ __launch_bounds__(512) void k1_pingpong(const uint16_t* __restrict__ 
   // (NB = 5) is stored straight from the accumulators, 64 bytes per row.  Column Vd
   // (the extra row's output) goes to xout.
   char* stage = smem + wave * 16384;
+  if constexpr (kKV) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1) __syncthreads();   // every (row, head) item of half 0 is done with the staging
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * i + n, p = 4 * j + g;
+          *reinterpret_cast<floatx4*>(stage + r * 256 + ((p ^ (r & 7)) * 16)) = acc[4 * h + i][j];
+        }
+      __syncthreads();
+      kv_epilogue_half(smem, h, m0, n0, M, Vd, ep);
+    }
+    return;
+  }
   const bool vec = (Vd % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
   const int cbase = n0 + wn * 16 * NB;
   const int Vt = Vd + (wx != nullptr ? 1 : 0);
@@ -852,7 +729,7 @@ hipError_t launch_pingpong(const uint16_t* hidden, const uint16_t* lm_head, floa
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_pingpong<NB>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_pingpong<NB, false>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, pp_lds(NB));
     if (e != hipSuccess) return e;
     attr_set[dev] = true;
@@ -860,8 +737,8 @@ hipError_t launch_pingpong(const uint16_t* hidden, const uint16_t* lm_head, floa
   const int Vt = Vd + (wx != nullptr ? 1 : 0);
   const int mtiles = (M + BBM - 1) / BBM, ntiles = (Vt + 64 * NB - 1) / (64 * NB);
   const int per_xcd = (mtiles * ntiles + 7) / 8;
-  hipLaunchKernelGGL(k1_pingpong<NB>, dim3(per_xcd * 8), dim3(512), pp_lds(NB), stream, hidden, lm_head, logits, M,
-                     H, Vd, mtiles, ntiles, wx, xout);
+  hipLaunchKernelGGL((k1_pingpong<NB, false>), dim3(per_xcd * 8), dim3(512), pp_lds(NB), stream, hidden, lm_head,
+                     logits, M, H, Vd, mtiles, ntiles, wx, xout, KvEpilogue{});
   return hipSuccess;
 }
 
@@ -897,7 +774,7 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
       hipLaunchKernelGGL((k1_skinny<FR, 2>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd, wx, xout);
     else
       hipLaunchKernelGGL((k1_skinny<FR, 4>), grid, block, 0, stream, hidden, lm_head, logits, M, H, Vd, wx, xout);
-  } else if (H % BBK == 0) {
+  } else if (H % 64 == 0) {
     const hipError_t e = pingpong_nb(M, Vt, cu_count()) == 5
                              ? launch_pingpong<5>(hidden, lm_head, logits, M, H, Vd, wx, xout, stream)
                              : launch_pingpong<4>(hidden, lm_head, logits, M, H, Vd, wx, xout, stream);
@@ -913,7 +790,7 @@ hipError_t launch_draft_logits(const uint16_t* hidden, const uint16_t* lm_head, 
   return hipGetLastError();
 }
 
-bool kv_product_fused(int M, int Hd, int hd) { return hd == 128 && M > 64 && Hd % BBK == 0; }
+bool kv_product_fused(int M, int Hd, int hd) { return hd == 128 && M > 64 && Hd % 64 == 0; }
 
 hipError_t launch_kv_product(const uint16_t* normed, const uint16_t* kv_w, int M, int Hd, int ncols,
                              const KvEpilogue& ep, hipStream_t stream) {
@@ -921,15 +798,15 @@ hipError_t launch_kv_product(const uint16_t* normed, const uint16_t* kv_w, int M
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_kv),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, BLDS);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1_pingpong<4, true>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, pp_lds(4));
     if (e != hipSuccess) return e;
     attr_set[dev] = true;
   }
-  const int mtiles = (M + BBM - 1) / BBM, ntiles = (ncols + BBN - 1) / BBN;
+  const int mtiles = (M + BBM - 1) / BBM, ntiles = (ncols + 255) / 256;
   const int per_xcd = (mtiles * ntiles + 7) / 8;
-  hipLaunchKernelGGL(k1_kv, dim3(per_xcd * 8), dim3(512), BLDS, stream, normed, kv_w, M, Hd, ncols, mtiles, ntiles,
-                     ep);
+  hipLaunchKernelGGL((k1_pingpong<4, true>), dim3(per_xcd * 8), dim3(512), pp_lds(4), stream, normed, kv_w, nullptr,
+                     M, Hd, ncols, mtiles, ntiles, nullptr, nullptr, ep);
   return hipGetLastError();
 }
 
