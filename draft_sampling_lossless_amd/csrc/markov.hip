@@ -88,33 +88,55 @@ __device__ __forceinline__ float neg_gumbel2(uint32_t w) {
 
 // (templates outside the anonymous namespace: the launch stubs of their instances
 // must be emitted for the host-side switch below)
-// LDS layout of one W2 chunk (64 rows of P = 4 KS 16-byte pieces).  Rows sit in P
-// groups of 64 / P rows; a group is 1 KB, written by one global->LDS DMA
-// instruction.  A-fragment f, row m lives in group grp(f, m), position pos(f, m) of
-// it, and every lane reaches all its fragments and k steps from one base address
-// plus immediates.  A 16-byte LDS read is served 32 lanes at a time over 128 banks
-// (512 bytes): lanes 0-31 of a fragment read rows 0-15 at pieces g = 0, 1 (lanes
-// 32-63 at g = 2, 3).  With P >= 16 a fragment's rows are consecutive groups, so
-// groups 1056 bytes apart (32 mod 512) put those 32 pieces in 32 distinct 16-byte
-// bank groups; with P < 16 no group stride does (rows share groups), and 1040 keeps
-// the conflicts two-way.
+// LDS layout of one W2 chunk (64 rows of P = 4 KS 16-byte pieces) in P groups of
+// 64 / P rows; a group is 1 KB, written by one global->LDS DMA instruction (lane L:
+// position L / P, slot L % P).  A-fragment f, row m lives in group grp(f, m), position
+// pos(f, m), and logical piece q of it (k = 8 q .. 8 q + 7) at slot piece(q, m).  A
+// 16-byte LDS read on gfx950 is free of bank conflicts for these patterns (each lane
+// (n, g) of a fragment read takes row n, piece 4 s + g), as measured with a read probe:
+//  * P >= 16: a fragment's rows are consecutive groups, 1056 bytes apart (1040 left
+//    the reads two-way conflicted); pieces in order;
+//  * P < 16: a fragment's 16 rows are contiguous (one or two groups, no padding), and
+//    the pieces of a row are permuted by row pairs: P = 8 (128-byte rows) q ^ ((m >> 1)
+//    & 7), P = 4 (64-byte rows) (q + (m >> 1)) & 3.  Rows in group order with pieces in
+//    order read at half the rate whatever the group stride.
+// Every lane reaches all its fragments from one base address per k step plus immediates.
 template <int P>
 struct ChunkLds {
   static constexpr int kRows = 64 / P;  // rows per group
-  static constexpr int kPer = P >= 16 ? 1 : 16 / P;  // (P < 16) positions per fragment
-  static constexpr int kGroup = P >= 16 ? 1056 : 1040;  // bytes from one group to the next
+  static constexpr int kPer = P >= 16 ? 1 : 16 / kRows;  // (P < 16) groups per fragment
+  static constexpr int kGroup = P >= 16 ? 1056 : 1024;  // bytes from one group to the next
   static constexpr int kBytes = P * kGroup;
-  __host__ __device__ static constexpr int grp(int f, int m) { return P >= 16 ? (f / kRows) * 16 + m : m % P; }
-  __host__ __device__ static constexpr int pos(int f, int m) { return P >= 16 ? f % kRows : f * kPer + m / P; }
+  __host__ __device__ static constexpr int grp(int f, int m) { return P >= 16 ? (f / kRows) * 16 + m : f * kPer + m / kRows; }
+  __host__ __device__ static constexpr int pos(int f, int m) { return P >= 16 ? f % kRows : m % kRows; }
   __host__ __device__ static constexpr int offset(int f, int m) { return grp(f, m) * kGroup + pos(f, m) * P * 16; }
+  __host__ __device__ static constexpr int piece(int q, int m) {
+    return P >= 16 ? q : P == 8 ? (q ^ ((m >> 1) & 7)) : ((q + (m >> 1)) & 3);
+  }
   // chunk row (vocabulary offset) that group p, position h holds; fragment f row m
   // is vocabulary offset 16 f + m
   __host__ __device__ static constexpr int vocab(int p, int h) {
-    const int f = P >= 16 ? (p / 16) * kRows + h : h / kPer;
-    const int m = P >= 16 ? p % 16 : (h % kPer) * P + p;
-    return 16 * f + m;
+    return P >= 16 ? 16 * ((p / 16) * kRows + h) + p % 16 : p * kRows + h;
+  }
+  // the logical piece that slot s of group p, position h holds
+  __host__ __device__ static constexpr int logical(int s, int p, int h) {
+    const int m = P >= 16 ? 0 : (p % kPer) * kRows + h;  // the row within its fragment
+    return P >= 16 ? s : P == 8 ? (s ^ ((m >> 1) & 7)) : ((s - (m >> 1)) & 3);
   }
 };
+static_assert(ChunkLds<8>::logical(ChunkLds<8>::piece(5, 11), 3, 3) == 5, "slot map inverts (P = 8)");
+static_assert(ChunkLds<4>::logical(ChunkLds<4>::piece(2, 13), 0, 13) == 2, "slot map inverts (P = 4)");
+static_assert(ChunkLds<8>::vocab(3, 3) == 16 * 1 + 11 && ChunkLds<8>::offset(1, 11) == 3 * 1024 + 3 * 128,
+              "group 3 position 3 is fragment 1 row 11 (P = 8)");
+static_assert(ChunkLds<4>::vocab(3, 5) == 16 * 3 + 5 && ChunkLds<4>::offset(3, 5) == 3 * 1024 + 5 * 64 &&
+                  ChunkLds<4>::offset(3, 15) + 64 <= ChunkLds<4>::kBytes,
+              "group 3 position 5 is fragment 3 row 5, inside the chunk (P = 4)");
+static_assert(ChunkLds<8>::offset(3, 15) + 128 <= ChunkLds<8>::kBytes &&
+                  ChunkLds<16>::offset(3, 15) + 256 <= ChunkLds<16>::kBytes &&
+                  ChunkLds<32>::offset(3, 15) + 512 <= ChunkLds<32>::kBytes,
+              "every fragment row lies inside the chunk");
+static_assert(ChunkLds<32>::vocab(17, 1) == 16 * 3 + 1 && ChunkLds<32>::offset(3, 1) == 17 * 1056 + 1 * 512,
+              "group 17 position 1 is fragment 3 row 1 (P = 32)");
 
 // four floats this thread stored earlier in the kernel (device-coherent loads, so a
 // stale vector-L1 line of the values loaded before the store is never returned)
@@ -184,22 +206,25 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
   // With a rank below 32 KS the pieces past the rank repeat the row's last piece:
   // finite values that meet the zero B operand there.  Every wave issues exactly KS
   // DMA instructions per chunk, so the vector-memory counter is known at each wait.
-  const int dma_piece = min(lane % P, kc - 1);
+  // (the row and piece map of group 4 t + wave depends on the wave's parity only, as
+  // 4 t is even: group 4 t + wave holds rows vocab(4 t, 0) + vocab(wave, 0) + vocab(0, h))
+  const int dma_piece = min(Lay::logical(lane % P, wave, lane / P), kc - 1);
   const int dma_row = Lay::vocab(0, lane / P);
   const int dma_off = dma_row * r + dma_piece * 8;
+  const int wrow = Lay::vocab(wave, 0);
   auto issue_w2 = [&](int c) {
     // kKeep2: chunk c into buffer ((c - vs) / nvs) & 1
     char* const lbuf = lds + (kMode == kKeep2 ? (((c - vs) / nvs) & 1) * Lay::kBytes : 0);
     const int jc = c * kChunk;
     if (jc + kChunk <= Vd) {
-      const uint16_t* src = w2 + (size_t)(jc + wave) * r;
+      const uint16_t* src = w2 + (size_t)(jc + wrow) * r;
 #pragma unroll
       for (int t = 0; t < KS; ++t)
         dma16(src + (size_t)Lay::vocab(4 * t, 0) * r + dma_off, lbuf + (t * 4 + wave) * Lay::kGroup);
     } else {  // the last, partial chunk: rows past Vd load row Vd - 1 (never used)
 #pragma unroll
       for (int t = 0; t < KS; ++t) {
-        const int j = min(jc + wave + Lay::vocab(4 * t, 0) + dma_row, Vd - 1);
+        const int j = min(jc + wrow + Lay::vocab(4 * t, 0) + dma_row, Vd - 1);
         dma16(w2 + (size_t)j * r + dma_piece * 8, lbuf + (t * 4 + wave) * Lay::kGroup);
       }
     }
@@ -335,10 +360,11 @@ __global__ __launch_bounds__(256) void markov_step(float* __restrict__ logits, c
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const char* arow = cbuf + Lay::offset(f, n) + 16 * g;
+      const char* arow = cbuf + Lay::offset(f, n);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + 64 * s));
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + 16 * Lay::piece(4 * s + g, n)));
         acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, efrag[s], acc[f], 0, 0, 0);
       }
     }
