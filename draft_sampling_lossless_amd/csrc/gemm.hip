@@ -510,7 +510,6 @@ __host__ __device__ constexpr int pp_stage(int NB) { return (BBM + 64 * NB) * PK
 __host__ __device__ constexpr int pp_lds(int NB) { return PNS * pp_stage(NB); }
 static_assert(pp_lds(4) >= BSTAGE_OUT && pp_lds(5) >= BSTAGE_OUT, "the epilogue stages 8 x 16 KB in the ring");
 
-//
 // kKV (NB = 4): the context-KV product, the normalised context states (A, M x H) times
 // every layer's fused K/V weights (W, Vd = L * 2 * nkv * 128 rows); a 256-column tile
 // holds two whole heads, and the epilogue (kv_epilogue_half) adds the bias, normalises
