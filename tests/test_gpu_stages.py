@@ -609,7 +609,8 @@ def test_choose_k_scans_past_a_local_maximum_on_gpu():
     (256, 16, 4096, 4096, 4096, 64),     # Vd a multiple of 256: the extra row opens a new column tile
     (40, 4, 512, 8192, 2048, 32),        # reduced vocabulary, skinny GEMM
     (12, 2, 4096, 1024, 1024, 16),       # several requests in the few-request kernel
-    (64, 8, 256, 151936, 151936, 16)])   # the plain product with 256 x 320 tiles, the extra row with 256 x 256
+    (64, 8, 256, 151936, 151936, 16),    # 256 x 320 tiles with and without the extra row
+    (256, 16, 256, 38400, 38400, 16)])   # Vd a multiple of 320: the extra row alone in a last 320-wide tile
 def test_confidence_fused_parity(B, N, H, V, Vd, r):
     """The confidence head inside stages 1 and 2: w_h as one more LM-head row (h_dot), the
     embedding part and the sigmoid inside the Markov loop.  Against the oracle's head on the
